@@ -1,0 +1,156 @@
+"""Python access to the CPU oracle (oracle.c) -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
+import this module. It shares no code with the HIP library.
+
+The oracle follows "NeuroPrefetcher: Storage-Aware Sparse LLM Inference via
+Delta Prefetching" (Dhar et al.), section 3.4 (active set from centroid
+masks, delta by set difference, slot map with -1 for non-resident neurons,
+freed slots reused without compaction, cold start) and section 3.5 (sorted
+incoming IDs, neuron-centric [gate|up|down^T] records), with the readings
+listed in oracle.c's header.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from functools import lru_cache
+
+import numpy as np
+
+UNION, INTERSECT, SINGLE = 0, 1, 2
+MODES = {"union": UNION, "intersect": INTERSECT, "single": SINGLE}
+_OK, _EINVAL, _ECAPACITY = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+
+def build_lib(force: bool = False) -> str:
+    """Compile oracle.c (gcc -O2, strict IEEE: no fast-math) into liboracle.so."""
+    src = os.path.join(_HERE, "oracle.c")
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src):
+        tmp = _LIB_PATH + f".tmp{os.getpid()}"
+        cmd = f"gcc -O2 -std=c11 -fPIC -shared -ffp-contract=off -o {tmp} {src}"
+        if os.system(cmd) != 0:
+            raise RuntimeError(f"failed: {cmd}")
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+@lru_cache(maxsize=1)
+def _lib():
+    if not os.path.exists(_LIB_PATH):
+        build_lib()
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.npo_active_set.argtypes = [vp, vp, i32, i32, vp]
+    lib.npo_active_set.restype = i32
+    lib.npo_delta_step.argtypes = [i32, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp]
+    lib.npo_delta_step.restype = i32
+    lib.npo_occupied_slots.argtypes = [i32, vp, vp]
+    lib.npo_occupied_slots.restype = i32
+    lib.npo_copy_bundles.argtypes = [vp, vp, i64, vp, vp, i32]
+    lib.npo_copy_bundles.restype = None
+    lib.npo_sparse_ffn.argtypes = [vp, i32, i32, vp, i32, vp, vp]
+    lib.npo_sparse_ffn.restype = i32
+    return lib
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+class CapacityError(RuntimeError):
+    """|A_t| > K_max: the oracle refuses the step and leaves its state unchanged."""
+
+
+def active_set(mask_g: np.ndarray, mask_u: np.ndarray | None, M: int, mode: int) -> np.ndarray:
+    """Ascending neuron IDs of the active set built from one or two centroid masks."""
+    g = _c(mask_g, np.uint64)
+    u = _c(mask_u if mask_u is not None else mask_g, np.uint64)
+    assert g.size * 64 >= M and u.size * 64 >= M
+    out = np.empty(max(M, 1), dtype=np.int32)
+    n = _lib().npo_active_set(g.ctypes.data, u.ctypes.data, M, mode, out.ctypes.data)
+    if n < 0:
+        raise ValueError(f"unknown mask mode {mode}")
+    return out[:n].copy()
+
+
+@dataclass
+class StepResult:
+    d_in: np.ndarray      # ascending incoming neuron IDs
+    slot_in: np.ndarray   # slot assigned to each incoming neuron
+    d_out: np.ndarray     # ascending outgoing neuron IDs
+
+
+class OracleLayer:
+    """Slot map, owner table and (optionally) the K_max-row buffer of one sparse layer."""
+
+    def __init__(self, M: int, K: int, R: int, d: int, keep_buffer: bool = True):
+        self.M, self.K, self.R, self.d = M, K, R, d
+        self.slot_map = np.full(M, -1, dtype=np.int32)
+        self.owner = np.full(K, -1, dtype=np.int32)
+        self.buf = np.zeros((K, R, d), dtype=np.uint16) if keep_buffer else None
+
+    def reset(self) -> None:
+        self.slot_map.fill(-1)
+        self.owner.fill(-1)
+        if self.buf is not None:
+            self.buf.fill(0)
+
+    def step(self, S: np.ndarray) -> StepResult:
+        S = _c(S, np.int32)
+        d_in = np.empty(self.K, dtype=np.int32)
+        slot_in = np.empty(self.K, dtype=np.int32)
+        d_out = np.empty(self.K, dtype=np.int32)
+        n_in = ctypes.c_int32(0)
+        n_out = ctypes.c_int32(0)
+        rc = _lib().npo_delta_step(self.M, self.K, self.slot_map.ctypes.data, self.owner.ctypes.data,
+                                   S.ctypes.data, S.size, d_in.ctypes.data, slot_in.ctypes.data,
+                                   ctypes.byref(n_in), d_out.ctypes.data, ctypes.byref(n_out))
+        if rc == _ECAPACITY:
+            raise CapacityError(f"|S|={S.size} > K_max={self.K}")
+        if rc != _OK:
+            raise ValueError("invalid active set")
+        return StepResult(d_in[: n_in.value].copy(), slot_in[: n_in.value].copy(),
+                          d_out[: n_out.value].copy())
+
+    def copy_bundles(self, store: np.ndarray, res: StepResult) -> None:
+        """buf[slot_in[k]] = store[d_in[k]] (byte copy); store is uint16 [M][R][d]."""
+        assert self.buf is not None
+        st = store.reshape(-1)
+        assert st.dtype == np.uint16 and st.flags.c_contiguous and st.size >= self.M * self.R * self.d
+        _lib().npo_copy_bundles(self.buf.ctypes.data, st.ctypes.data, self.R * self.d,
+                                res.d_in.ctypes.data, res.slot_in.ctypes.data, res.d_in.size)
+
+    def copy_given_bundles(self, bundles: np.ndarray, res: StepResult) -> None:
+        """Same as copy_bundles, with bundles[k] already holding neuron d_in[k]'s bundle."""
+        assert self.buf is not None
+        b = _c(bundles, np.uint16).reshape(-1)
+        ids = np.arange(res.d_in.size, dtype=np.int32)
+        _lib().npo_copy_bundles(self.buf.ctypes.data, b.ctypes.data, self.R * self.d,
+                                ids.ctypes.data, res.slot_in.ctypes.data, res.d_in.size)
+
+    def occupied_slots(self) -> np.ndarray:
+        out = np.empty(self.K, dtype=np.int32)
+        n = _lib().npo_occupied_slots(self.K, self.owner.ctypes.data, out.ctypes.data)
+        return out[:n].copy()
+
+
+def sparse_ffn(store: np.ndarray, R: int, d: int, ids: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """fp64 y[d] = sum over ids (in the order given) of down_i * h_i; store is uint16 [*][R][d]."""
+    st = store.reshape(-1)
+    assert st.dtype == np.uint16 and st.flags.c_contiguous
+    ids = _c(ids, np.int32)
+    if ids.size:
+        assert ids.min() >= 0 and (int(ids.max()) + 1) * R * d <= st.size
+    x = _c(x, np.float32)
+    assert x.size == d
+    y = np.empty(d, dtype=np.float64)
+    rc = _lib().npo_sparse_ffn(st.ctypes.data, R, d, ids.ctypes.data, ids.size, x.ctypes.data,
+                               y.ctypes.data)
+    if rc != _OK:
+        raise ValueError(f"unsupported bundle rows {R}")
+    return y

@@ -1,0 +1,96 @@
+// Row scatter for gfx950: copies each incoming neuron's bundle from the backing
+// row store into its assigned slot of the resident buffer (NeuroPrefetcher,
+// section 3.5: one record per incoming neuron holds its gate, up and down^T
+// rows; a GPU kernel places it at the slot the delta runtime assigned).
+//
+// The bundle is kept interleaved (one slot = one record), so the copy is a
+// plain 128-bit gather-scatter: workgroup b copies bundles b, b + grid, ...,
+// each lane moving U 16-byte chunks per pass with all U loads issued before
+// the stores. The store may be device memory (an HBM-resident backing store)
+// or pinned host memory (the loads then cross the host link).
+#include "np_internal.hpp"
+
+namespace np {
+namespace {
+
+constexpr int kNT = 256;
+constexpr int kU = 8;
+
+__global__ __launch_bounds__(kNT) void k_scatter_rows(int32_t* counts, const int32_t* __restrict__ d_in,
+                                                      const int32_t* __restrict__ slot_in,
+                                                      const uint4* __restrict__ store,
+                                                      uint4* __restrict__ buf, int32_t M, int32_t K,
+                                                      int32_t cb) {
+    const int n_in = counts[0];
+    for (int i = blockIdx.x; i < n_in; i += gridDim.x) {
+        const int n = d_in[i], s = slot_in[i];
+        if ((unsigned)n >= (unsigned)M || (unsigned)s >= (unsigned)K) {
+            if (threadIdx.x == 0) atomicOr(&counts[3], kErrBadList);
+            continue;
+        }
+        const uint4* src = store + (size_t)n * cb;
+        uint4* dst = buf + (size_t)s * cb;
+        for (int c = threadIdx.x; c < cb; c += kNT * kU) {
+            uint4 v[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                if (c + u * kNT < cb) v[u] = src[c + u * kNT];
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                if (c + u * kNT < cb) dst[c + u * kNT] = v[u];
+        }
+    }
+}
+
+// Streaming read: every lane sums the low words of its 16-byte loads.
+__global__ __launch_bounds__(kNT) void k_probe_read(const uint4* __restrict__ src, int64_t n16, float* sink) {
+    const int64_t stride = (int64_t)gridDim.x * kNT;
+    uint32_t acc = 0;
+    int64_t i = (int64_t)blockIdx.x * kNT + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+        acc += a.x ^ b.y ^ c.z ^ d.w;
+    }
+    for (; i < n16; i += stride) acc += src[i].x;
+    __shared__ uint32_t s;
+    if (threadIdx.x == 0) s = 0;
+    __syncthreads();
+    atomicAdd(&s, acc);
+    __syncthreads();
+    if (threadIdx.x == 0) sink[blockIdx.x] = (float)s;
+}
+
+__global__ __launch_bounds__(kNT) void k_probe_copy(uint4* __restrict__ dst, const uint4* __restrict__ src,
+                                                    int64_t n16) {
+    const int64_t stride = (int64_t)gridDim.x * kNT;
+    for (int64_t i = (int64_t)blockIdx.x * kNT + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+}  // namespace
+
+hipError_t launch_scatter(int32_t* counts, const int32_t* d_in, const int32_t* slot_in,
+                          const uint16_t* store, uint16_t* buf, int32_t M, int32_t K,
+                          int32_t bundle_elems, int grid, hipStream_t s) {
+    hipLaunchKernelGGL(k_scatter_rows, dim3(grid), dim3(kNT), 0, s, counts, d_in, slot_in,
+                       reinterpret_cast<const uint4*>(store), reinterpret_cast<uint4*>(buf), M, K,
+                       bundle_elems / 8);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_read(const void* src, int64_t bytes, float* sink, hipStream_t s) {
+    const int64_t n16 = bytes / 16;
+    int grid = (int)std::min<int64_t>(65536, std::max<int64_t>(1, (n16 + kNT * 4 - 1) / (kNT * 4)));
+    grid = std::min(grid, 256 * 16);
+    hipLaunchKernelGGL(k_probe_read, dim3(grid), dim3(kNT), 0, s, reinterpret_cast<const uint4*>(src), n16, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_copy(void* dst, const void* src, int64_t bytes, hipStream_t s) {
+    const int64_t n16 = bytes / 16;
+    int grid = (int)std::min<int64_t>(256 * 16, std::max<int64_t>(1, (n16 + kNT - 1) / kNT));
+    hipLaunchKernelGGL(k_probe_copy, dim3(grid), dim3(kNT), 0, s, reinterpret_cast<uint4*>(dst),
+                       reinterpret_cast<const uint4*>(src), n16);
+    return hipGetLastError();
+}
+
+}  // namespace np

@@ -1,0 +1,640 @@
+// Host side of the C ABI in include/np.h: layer state, host-side validation,
+// error reporting and the per-token driver (NeuroPrefetcher, sections 3.1, 3.4
+// and 3.5). Every check runs before anything is enqueued, so a failing call
+// leaves all state unchanged.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "np.h"
+#include "np_internal.hpp"
+
+namespace np {
+int ffn_win_max();
+}
+
+using namespace np;
+
+namespace {
+
+thread_local std::string g_err;
+
+np_status fail(np_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+#define NP_HIP(call)                                                                          \
+    do {                                                                                      \
+        hipError_t e_ = (call);                                                               \
+        if (e_ != hipSuccess) return fail(NP_EHIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
+    } while (0)
+
+// Makes `dev` current for the scope and restores the previous device.
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = true;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        if (prev != dev) ok = hipSetDevice(dev) == hipSuccess;
+    }
+    ~DeviceGuard() {
+        int cur = -1;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    }
+};
+
+enum LayerState { kFresh = 0, kAssigned = 1, kScattered = 2 };
+
+constexpr int kDefaultSlotsPerWg = 5;
+constexpr int kDefaultTileCols = 256;
+
+}  // namespace
+
+struct np_layer {
+    np_layer_desc desc{};
+    int W = 0, Kw = 0, n_tables = 0;
+    std::vector<uint64_t> h_masks;  // copy of the centroid tables (validation, |S|)
+    std::vector<uint64_t> h_res;    // host mirror of the resident set
+    int32_t n_active = 0, n_in = 0;
+    int64_t total_active = 0, total_in = 0;
+    int state = kFresh;
+    const uint16_t* store_dev = nullptr;
+    bool store_is_host = false;
+
+    uint64_t* d_masks = nullptr;
+    uint16_t* buf = nullptr;
+    int32_t* slot_map = nullptr;
+    int32_t* owner = nullptr;
+    uint64_t* res = nullptr;
+    uint64_t* freeb = nullptr;
+    int32_t* lists = nullptr;  // d_in | slot_in | d_out | act, K each
+    int32_t* counts = nullptr;
+    float* hval = nullptr;
+    float* partials = nullptr;
+    uint32_t* sync = nullptr;
+    LayerDev* ldev = nullptr;
+    hipEvent_t ev_scatter = nullptr;
+
+    int spw = kDefaultSlotsPerWg;
+    int tw = kDefaultTileCols;
+    size_t partials_floats = 0;
+    int sync_words = 0;
+
+    int32_t* d_in() const { return lists; }
+    int32_t* slot_in() const { return lists + desc.k_max; }
+    int32_t* d_out() const { return lists + 2 * (size_t)desc.k_max; }
+    int32_t* act() const { return lists + 3 * (size_t)desc.k_max; }
+    size_t bundle_elems() const { return (size_t)desc.n_rows * desc.d_model; }
+};
+
+namespace {
+
+int pow2_floor(int v) {
+    int p = 1;
+    while (p * 2 <= v) p *= 2;
+    return p;
+}
+
+int ffn_threads(int d) {
+    const int cpr = d / 8;
+    return (cpr + 255) / 256 <= 2 ? 256 : 512;
+}
+
+int q_of(const np_layer* L) { return (L->desc.d_model + L->tw - 1) / L->tw; }
+
+// FFN launch shape for n active slots.
+bool ffn_shape(const np_layer* L, int n, FfnShape* sh) {
+    const int d = L->desc.d_model;
+    sh->nt = ffn_threads(d);
+    const int cpr = d / 8;
+    const int cl = std::min(sh->nt, pow2_floor(cpr));
+    sh->jx = (cpr + cl - 1) / cl;
+    sh->tw = L->tw;
+    sh->q = q_of(L);
+    const int win = ffn_win_max();
+    int p1 = std::max(1, (n + L->spw - 1) / L->spw);
+    const int per_chunk_max = win / sh->q;  // slots per chunk the window can hold
+    if (per_chunk_max < 1) return false;
+    p1 = std::max(p1, (n + per_chunk_max - 1) / per_chunk_max);
+    if (p1 > kP1Cap) return false;
+    p1 = std::min(p1, std::max(1, n));
+    sh->p1 = p1;
+    sh->nwg = p1 + sh->q - 1;
+    sh->win_max = win;
+    return sh->jx <= 4;
+}
+
+np_status alloc_ffn_scratch(np_layer* L) {
+    const int q = q_of(L);
+    const size_t need = (size_t)(kP1Cap + q) * L->tw;
+    if (L->partials && L->partials_floats >= need) return NP_OK;
+    if (L->partials) (void)hipFree(L->partials);
+    L->partials = nullptr;
+    if (hipMalloc(&L->partials, need * sizeof(float)) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(NP_ENOMEM, "cannot allocate %zu FFN partial floats", need);
+    }
+    L->partials_floats = need;
+    return NP_OK;
+}
+
+void free_layer(np_layer* L) {
+    void* ptrs[] = {L->d_masks, L->buf, L->slot_map, L->owner, L->res, L->freeb, L->lists,
+                    L->counts, L->hval, L->partials, L->sync, L->ldev};
+    for (void* p : ptrs)
+        if (p) (void)hipFree(p);
+    if (L->ev_scatter) (void)hipEventDestroy(L->ev_scatter);
+    delete L;
+}
+
+// Device state as np_layer_create leaves it (synchronous).
+np_status init_state(np_layer* L) {
+    const int K = L->desc.k_max, M = L->desc.d_ff;
+    NP_HIP(hipMemset(L->buf, 0, (size_t)K * L->bundle_elems() * 2));
+    NP_HIP(hipMemset(L->slot_map, 0xFF, (size_t)M * 4));
+    NP_HIP(hipMemset(L->owner, 0xFF, (size_t)K * 4));
+    NP_HIP(hipMemset(L->res, 0, (size_t)L->W * 8));
+    std::vector<uint64_t> fb(L->Kw, ~0ull);
+    if (K & 63) fb[L->Kw - 1] = (1ull << (K & 63)) - 1;
+    NP_HIP(hipMemcpy(L->freeb, fb.data(), (size_t)L->Kw * 8, hipMemcpyHostToDevice));
+    NP_HIP(hipMemset(L->lists, 0, (size_t)4 * K * 4));
+    NP_HIP(hipMemset(L->counts, 0, 4 * 4));
+    NP_HIP(hipDeviceSynchronize());
+    std::fill(L->h_res.begin(), L->h_res.end(), 0ull);
+    L->n_active = 0;
+    L->n_in = 0;
+    L->total_active = 0;
+    L->total_in = 0;
+    L->state = kFresh;
+    return NP_OK;
+}
+
+// Host copy of the combined mask words for (gate_cid, up_cid); returns |S|.
+int combine_host(const np_layer* L, int32_t g, int32_t u, uint64_t* out) {
+    const uint64_t* ma = L->h_masks.data() + (size_t)g * L->W;
+    const uint64_t* mb = L->h_masks.data() + ((size_t)(L->n_tables - 1) * L->desc.n_centroids + u) * L->W;
+    int n = 0;
+    for (int w = 0; w < L->W; ++w) {
+        uint64_t s;
+        switch (L->desc.mask_mode) {
+            case NP_MASK_UNION: s = ma[w] | mb[w]; break;
+            case NP_MASK_INTERSECT: s = ma[w] & mb[w]; break;
+            default: s = ma[w]; break;
+        }
+        out[w] = s;
+        n += __builtin_popcountll(s);
+    }
+    return n;
+}
+
+// Validation shared by np_delta_assign and np_decode_step.
+np_status check_cids(const np_layer* L, int32_t g, int32_t u, int32_t* eff_u) {
+    const int C = L->desc.n_centroids;
+    if (g < 0 || g >= C) return fail(NP_EINVAL, "gate centroid id %d out of range [0, %d)", g, C);
+    if (L->desc.mask_mode == NP_MASK_SINGLE) {
+        *eff_u = g;
+    } else {
+        if (u < 0 || u >= C) return fail(NP_EINVAL, "up centroid id %d out of range [0, %d)", u, C);
+        *eff_u = u;
+    }
+    return NP_OK;
+}
+
+int scatter_grid(int n_in) { return std::max(1, std::min(n_in, 4096)); }
+
+np_status enqueue_ffn(np_layer* L, const float* x, float* y, hipStream_t s) {
+    FfnShape sh;
+    if (!ffn_shape(L, L->n_active, &sh))
+        return fail(NP_EINVAL, "no FFN launch shape for d_model=%d n=%d tile=%d", L->desc.d_model,
+                    L->n_active, L->tw);
+    FfnArgs a;
+    a.buf = L->buf;
+    a.act = L->act();
+    a.counts = L->counts;
+    a.x = x;
+    a.y = y;
+    a.hval = L->hval;
+    a.partials = L->partials;
+    a.flags = L->sync;
+    a.tcnt = L->sync + kP1Cap;
+    a.ctl = L->sync + kP1Cap + kMaxTiles;
+    a.d = L->desc.d_model;
+    a.K = L->desc.k_max;
+    a.R = L->desc.n_rows;
+    a.p1 = sh.p1;
+    a.q = sh.q;
+    a.tw = sh.tw;
+    a.nwg = sh.nwg;
+    NP_HIP(launch_sparse_ffn(a, sh, L->desc.n_rows == 3, s));
+    return NP_OK;
+}
+
+np_status enqueue_scatter(np_layer* L, hipStream_t s) {
+    NP_HIP(launch_scatter(L->counts, L->d_in(), L->slot_in(), L->store_dev, L->buf, L->desc.d_ff,
+                          L->desc.k_max, (int32_t)L->bundle_elems(), scatter_grid(L->n_in), s));
+    return NP_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+std::map<int, hipEvent_t>& assign_events() {
+    thread_local std::map<int, hipEvent_t> ev;
+    return ev;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* np_last_error(void) { return g_err.c_str(); }
+
+np_status np_layer_create(const np_layer_desc* desc, np_layer** out) {
+    if (!desc || !out) return fail(NP_EINVAL, "desc and out must not be NULL");
+    *out = nullptr;
+    const np_layer_desc& D = *desc;
+    if (D.d_model < 8 || D.d_model > kMaxDModel || D.d_model % 8)
+        return fail(NP_EINVAL, "d_model=%d must be a multiple of 8 in [8, %d]", D.d_model, kMaxDModel);
+    if (D.d_ff < 1 || D.d_ff > kMaxDff) return fail(NP_EINVAL, "d_ff=%d must be in [1, %d]", D.d_ff, kMaxDff);
+    if (D.k_max < 1 || D.k_max > std::min(D.d_ff, kMaxKmax))
+        return fail(NP_EINVAL, "k_max=%d must be in [1, min(d_ff, %d)]", D.k_max, kMaxKmax);
+    if (D.n_rows != 2 && D.n_rows != 3) return fail(NP_EINVAL, "n_rows=%d must be 2 or 3", D.n_rows);
+    if (D.n_centroids < 1 || D.n_centroids > kMaxCentroids)
+        return fail(NP_EINVAL, "n_centroids=%d must be in [1, %d]", D.n_centroids, kMaxCentroids);
+    if (D.mask_mode < NP_MASK_UNION || D.mask_mode > NP_MASK_SINGLE)
+        return fail(NP_EINVAL, "unknown mask_mode %d", D.mask_mode);
+    if (D.act != NP_ACT_RELU) return fail(NP_EINVAL, "unsupported activation %d", D.act);
+    if (!D.masks || !D.row_store) return fail(NP_EINVAL, "masks and row_store must not be NULL");
+    if (!aligned16(D.row_store)) return fail(NP_EINVAL, "row_store must be 16-byte aligned");
+    int ndev = 0;
+    NP_HIP(hipGetDeviceCount(&ndev));
+    if (D.device < 0 || D.device >= ndev) return fail(NP_EINVAL, "device %d out of range [0, %d)", D.device, ndev);
+
+    np_layer* L = new np_layer();
+    L->desc = D;
+    L->desc.masks = nullptr;
+    L->W = (D.d_ff + 63) / 64;
+    L->Kw = (D.k_max + 63) / 64;
+    L->n_tables = D.mask_mode == NP_MASK_SINGLE ? 1 : 2;
+    const size_t mask_words = (size_t)L->n_tables * D.n_centroids * L->W;
+    L->h_masks.assign(D.masks, D.masks + mask_words);
+    L->h_res.assign(L->W, 0ull);
+    if (D.d_ff & 63) {
+        const uint64_t stray = ~((1ull << (D.d_ff & 63)) - 1);
+        for (size_t m = 0; m < (size_t)L->n_tables * D.n_centroids; ++m)
+            if (L->h_masks[m * L->W + L->W - 1] & stray) {
+                delete L;
+                return fail(NP_EINVAL, "mask %zu has bits at or above d_ff=%d", m, D.d_ff);
+            }
+    }
+
+    DeviceGuard g(D.device);
+    if (!g.ok) {
+        delete L;
+        return fail(NP_EHIP, "hipSetDevice(%d) failed", D.device);
+    }
+    // Classify the row store: device memory of this device, or pinned host memory.
+    hipPointerAttribute_t attr;
+    std::memset(&attr, 0, sizeof attr);
+    hipError_t pe = hipPointerGetAttributes(&attr, D.row_store);
+    if (pe != hipSuccess) {
+        (void)hipGetLastError();
+        delete L;
+        return fail(NP_EINVAL, "row_store is neither device memory nor pinned host memory");
+    }
+    if (attr.type == hipMemoryTypeDevice) {
+        if (attr.device != D.device) {
+            delete L;
+            return fail(NP_EINVAL, "row_store lives on device %d, layer on device %d", attr.device, D.device);
+        }
+        L->store_dev = static_cast<const uint16_t*>(D.row_store);
+    } else if (attr.type == hipMemoryTypeHost) {
+        void* dp = nullptr;
+        if (hipHostGetDevicePointer(&dp, const_cast<void*>(D.row_store), 0) != hipSuccess || !dp) {
+            (void)hipGetLastError();
+            delete L;
+            return fail(NP_EINVAL, "pinned row_store is not mapped for device access");
+        }
+        L->store_dev = static_cast<const uint16_t*>(dp);
+        L->store_is_host = true;
+    } else {
+        delete L;
+        return fail(NP_EINVAL, "row_store memory type %d is not supported", (int)attr.type);
+    }
+
+    const int K = D.k_max, M = D.d_ff;
+    auto dmalloc = [&](void** p, size_t bytes) -> bool {
+        if (hipMalloc(p, bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            return false;
+        }
+        return true;
+    };
+    const size_t buf_bytes = (size_t)K * L->bundle_elems() * 2;
+    L->sync_words = kSyncWords;
+    bool ok = dmalloc((void**)&L->d_masks, mask_words * 8) && dmalloc((void**)&L->buf, buf_bytes) &&
+              dmalloc((void**)&L->slot_map, (size_t)M * 4) && dmalloc((void**)&L->owner, (size_t)K * 4) &&
+              dmalloc((void**)&L->res, (size_t)L->W * 8) && dmalloc((void**)&L->freeb, (size_t)L->Kw * 8) &&
+              dmalloc((void**)&L->lists, (size_t)4 * K * 4) && dmalloc((void**)&L->counts, 4 * 4) &&
+              dmalloc((void**)&L->hval, (size_t)K * 4) &&
+              dmalloc((void**)&L->sync, (size_t)L->sync_words * 4) &&
+              dmalloc((void**)&L->ldev, sizeof(LayerDev));
+    if (!ok) {
+        free_layer(L);
+        return fail(NP_ENOMEM, "device allocation failed (slot buffer %zu bytes)", buf_bytes);
+    }
+    np_status st = alloc_ffn_scratch(L);
+    if (st != NP_OK) {
+        free_layer(L);
+        return st;
+    }
+    LayerDev ld;
+    ld.masks = L->d_masks;
+    ld.res = L->res;
+    ld.freeb = L->freeb;
+    ld.slot_map = L->slot_map;
+    ld.owner = L->owner;
+    ld.d_in = L->d_in();
+    ld.slot_in = L->slot_in();
+    ld.d_out = L->d_out();
+    ld.act = L->act();
+    ld.counts = L->counts;
+    ld.W = L->W;
+    ld.Kw = L->Kw;
+    ld.M = M;
+    ld.K = K;
+    ld.mode = D.mask_mode;
+    ld.n_tables = L->n_tables;
+    ld.C = D.n_centroids;
+    ld.pad = 0;
+    hipError_t e = hipMemcpy(L->ldev, &ld, sizeof ld, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(L->d_masks, L->h_masks.data(), mask_words * 8, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemset(L->sync, 0, (size_t)L->sync_words * 4);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&L->ev_scatter, hipEventDisableTiming);
+    if (e != hipSuccess) {
+        free_layer(L);
+        return fail(NP_EHIP, "layer setup failed: %s", hipGetErrorString(e));
+    }
+    st = init_state(L);
+    if (st != NP_OK) {
+        free_layer(L);
+        return st;
+    }
+    *out = L;
+    return NP_OK;
+}
+
+np_status np_layer_destroy(np_layer* L) {
+    if (!L) return fail(NP_EINVAL, "layer must not be NULL");
+    DeviceGuard g(L->desc.device);
+    (void)hipDeviceSynchronize();
+    free_layer(L);
+    return NP_OK;
+}
+
+np_status np_layer_reset(np_layer* L) {
+    if (!L) return fail(NP_EINVAL, "layer must not be NULL");
+    DeviceGuard g(L->desc.device);
+    NP_HIP(hipDeviceSynchronize());
+    return init_state(L);
+}
+
+np_status np_layer_set_ffn_shape(np_layer* L, int32_t slots_per_wg, int32_t tile_cols) {
+    if (!L) return fail(NP_EINVAL, "layer must not be NULL");
+    if (slots_per_wg && (slots_per_wg < 1 || slots_per_wg > 16))
+        return fail(NP_EINVAL, "slots_per_wg=%d must be in [1, 16]", slots_per_wg);
+    if (tile_cols) {
+        const int ct = tile_cols / 8;
+        if (tile_cols % 8 || tile_cols < 64 || tile_cols > 1024 || (ct & (ct - 1)) ||
+            ct > ffn_threads(L->desc.d_model))
+            return fail(NP_EINVAL, "tile_cols=%d must be 8 * (power of two), 64..1024", tile_cols);
+    }
+    DeviceGuard g(L->desc.device);
+    NP_HIP(hipDeviceSynchronize());
+    const int old_spw = L->spw, old_tw = L->tw;
+    if (slots_per_wg) L->spw = slots_per_wg;
+    if (tile_cols) L->tw = tile_cols;
+    FfnShape sh;
+    if (!ffn_shape(L, L->desc.k_max, &sh)) {
+        L->spw = old_spw;
+        L->tw = old_tw;
+        return fail(NP_EINVAL, "shape (%d, %d) cannot cover k_max=%d", slots_per_wg, tile_cols, L->desc.k_max);
+    }
+    np_status st = alloc_ffn_scratch(L);
+    if (st != NP_OK) {
+        L->spw = old_spw;
+        L->tw = old_tw;
+    }
+    return st;
+}
+
+np_status np_delta_assign(np_layer* L, int32_t gate_cid, int32_t up_cid, void* stream) {
+    if (!L) return fail(NP_EINVAL, "layer must not be NULL");
+    if (L->state == kAssigned)
+        return fail(NP_ESTATE, "previous delta not scattered: call np_scatter_rows first");
+    int32_t u;
+    np_status st = check_cids(L, gate_cid, up_cid, &u);
+    if (st != NP_OK) return st;
+    std::vector<uint64_t> S(L->W);
+    const int n = combine_host(L, gate_cid, u, S.data());
+    if (n > L->desc.k_max)
+        return fail(NP_ECAPACITY, "|S| = %d exceeds k_max = %d", n, L->desc.k_max);
+    int n_in = 0;
+    for (int w = 0; w < L->W; ++w) n_in += __builtin_popcountll(S[w] & ~L->h_res[w]);
+    DeviceGuard g(L->desc.device);
+    DeltaLaunch a;
+    a.layers[0] = L->ldev;
+    a.cid[0][0] = gate_cid;
+    a.cid[0][1] = u;
+    a.n_layers = 1;
+    NP_HIP(launch_delta_assign(a, (hipStream_t)stream));
+    L->h_res.swap(S);
+    L->n_active = n;
+    L->n_in = n_in;
+    L->total_active += n;
+    L->total_in += n_in;
+    L->state = kAssigned;
+    return NP_OK;
+}
+
+np_status np_scatter_rows(np_layer* L, void* stream) {
+    if (!L) return fail(NP_EINVAL, "layer must not be NULL");
+    if (L->state != kAssigned) return fail(NP_ESTATE, "np_scatter_rows needs a preceding np_delta_assign");
+    DeviceGuard g(L->desc.device);
+    np_status st = enqueue_scatter(L, (hipStream_t)stream);
+    if (st != NP_OK) return st;
+    L->state = kScattered;
+    return NP_OK;
+}
+
+np_status np_sparse_ffn(np_layer* L, const float* x, float* y, void* stream) {
+    if (!L) return fail(NP_EINVAL, "layer must not be NULL");
+    if (!x || !y || !aligned16(x) || !aligned16(y)) return fail(NP_EINVAL, "x and y must be 16-byte aligned device pointers");
+    if (L->state != kScattered) return fail(NP_ESTATE, "np_sparse_ffn needs the last delta scattered");
+    DeviceGuard g(L->desc.device);
+    return enqueue_ffn(L, x, y, (hipStream_t)stream);
+}
+
+np_status np_decode_step(np_layer* const* layers, int32_t n_layers, const int32_t* cids, const float* x,
+                         float* y, void* compute_stream, void* copy_stream) {
+    if (!layers || !cids || n_layers < 1) return fail(NP_EINVAL, "layers, cids and n_layers >= 1 required");
+    if (!x || !y || !aligned16(x) || !aligned16(y)) return fail(NP_EINVAL, "x and y must be 16-byte aligned device pointers");
+    const np_layer* L0 = layers[0];
+    if (!L0) return fail(NP_EINVAL, "layer 0 is NULL");
+    const int dev = L0->desc.device, d = L0->desc.d_model;
+    std::vector<std::vector<uint64_t>> S(n_layers);
+    std::vector<int> n_act(n_layers), n_in(n_layers), u_eff(n_layers);
+    for (int l = 0; l < n_layers; ++l) {
+        const np_layer* L = layers[l];
+        if (!L) return fail(NP_EINVAL, "layer %d is NULL", l);
+        if (L->desc.device != dev || L->desc.d_model != d)
+            return fail(NP_EINVAL, "layer %d: all layers must share device and d_model", l);
+        for (int k = 0; k < l; ++k)
+            if (layers[k] == L) return fail(NP_EINVAL, "layer %d appears twice", l);
+        if (L->state == kAssigned) return fail(NP_ESTATE, "layer %d has an unscattered delta", l);
+        int32_t u;
+        np_status st = check_cids(L, cids[2 * l], cids[2 * l + 1], &u);
+        if (st != NP_OK) return fail(st, "layer %d: %s", l, g_err.c_str());
+        u_eff[l] = u;
+        S[l].resize(L->W);
+        n_act[l] = combine_host(L, cids[2 * l], u, S[l].data());
+        if (n_act[l] > L->desc.k_max)
+            return fail(NP_ECAPACITY, "layer %d: |S| = %d exceeds k_max = %d", l, n_act[l], L->desc.k_max);
+        int ni = 0;
+        for (int w = 0; w < L->W; ++w) ni += __builtin_popcountll(S[l][w] & ~L->h_res[w]);
+        n_in[l] = ni;
+    }
+    DeviceGuard g(dev);
+    hipStream_t cs = (hipStream_t)compute_stream, ps = (hipStream_t)copy_stream;
+    const bool two = cs != ps;
+    hipEvent_t ev_assign = nullptr;
+    if (two) {
+        auto& evs = assign_events();
+        auto it = evs.find(dev);
+        if (it == evs.end()) {
+            NP_HIP(hipEventCreateWithFlags(&ev_assign, hipEventDisableTiming));
+            evs[dev] = ev_assign;
+        } else {
+            ev_assign = it->second;
+        }
+    }
+    for (int l0 = 0; l0 < n_layers; l0 += kMaxLayersPerLaunch) {
+        DeltaLaunch a;
+        a.n_layers = std::min(kMaxLayersPerLaunch, n_layers - l0);
+        for (int k = 0; k < a.n_layers; ++k) {
+            a.layers[k] = layers[l0 + k]->ldev;
+            a.cid[k][0] = cids[2 * (l0 + k)];
+            a.cid[k][1] = u_eff[l0 + k];
+        }
+        NP_HIP(launch_delta_assign(a, cs));
+    }
+    for (int l = 0; l < n_layers; ++l) {
+        np_layer* L = layers[l];
+        L->h_res.swap(S[l]);
+        L->n_active = n_act[l];
+        L->n_in = n_in[l];
+        L->total_active += n_act[l];
+        L->total_in += n_in[l];
+        L->state = kAssigned;
+    }
+    if (two) {
+        NP_HIP(hipEventRecord(ev_assign, cs));
+        NP_HIP(hipStreamWaitEvent(ps, ev_assign, 0));
+    }
+    for (int l = 0; l < n_layers; ++l) {
+        np_layer* L = layers[l];
+        np_status st = enqueue_scatter(L, two ? ps : cs);
+        if (st != NP_OK) return st;
+        L->state = kScattered;
+        if (two) {
+            NP_HIP(hipEventRecord(L->ev_scatter, ps));
+            NP_HIP(hipStreamWaitEvent(cs, L->ev_scatter, 0));
+        }
+        st = enqueue_ffn(L, x + (size_t)l * d, y + (size_t)l * d, cs);
+        if (st != NP_OK) return st;
+    }
+    return NP_OK;
+}
+
+np_status np_layer_read_state(const np_layer* L, int32_t* slot_map, int32_t* owner, int32_t* d_in,
+                              int32_t* slot_in, int32_t* d_out, int32_t* act_slots, int32_t* counts) {
+    if (!L) return fail(NP_EINVAL, "layer must not be NULL");
+    DeviceGuard g(L->desc.device);
+    NP_HIP(hipDeviceSynchronize());
+    const size_t K = L->desc.k_max;
+    if (slot_map) NP_HIP(hipMemcpy(slot_map, L->slot_map, (size_t)L->desc.d_ff * 4, hipMemcpyDeviceToHost));
+    if (owner) NP_HIP(hipMemcpy(owner, L->owner, K * 4, hipMemcpyDeviceToHost));
+    if (d_in) NP_HIP(hipMemcpy(d_in, L->d_in(), K * 4, hipMemcpyDeviceToHost));
+    if (slot_in) NP_HIP(hipMemcpy(slot_in, L->slot_in(), K * 4, hipMemcpyDeviceToHost));
+    if (d_out) NP_HIP(hipMemcpy(d_out, L->d_out(), K * 4, hipMemcpyDeviceToHost));
+    if (act_slots) NP_HIP(hipMemcpy(act_slots, L->act(), K * 4, hipMemcpyDeviceToHost));
+    int32_t c[4];
+    NP_HIP(hipMemcpy(c, L->counts, sizeof c, hipMemcpyDeviceToHost));
+    if (counts) std::memcpy(counts, c, sizeof c);
+    if (c[3]) return fail(NP_EDEVICE, "device error bits 0x%x", c[3]);
+    return NP_OK;
+}
+
+np_status np_layer_read_rows(const np_layer* L, const int32_t* slots, int32_t n, void* dst) {
+    if (!L || !dst || n < 0) return fail(NP_EINVAL, "layer and dst must not be NULL, n >= 0");
+    DeviceGuard g(L->desc.device);
+    NP_HIP(hipDeviceSynchronize());
+    const size_t bb = L->bundle_elems() * 2;
+    if (!slots) {
+        if (n != L->desc.k_max) return fail(NP_EINVAL, "slots == NULL requires n == k_max");
+        NP_HIP(hipMemcpy(dst, L->buf, (size_t)n * bb, hipMemcpyDeviceToHost));
+        return NP_OK;
+    }
+    for (int i = 0; i < n; ++i)
+        if (slots[i] < 0 || slots[i] >= L->desc.k_max)
+            return fail(NP_EINVAL, "slot %d out of range [0, %d)", slots[i], L->desc.k_max);
+    for (int i = 0; i < n; ++i)
+        NP_HIP(hipMemcpy((char*)dst + (size_t)i * bb, (const char*)L->buf + (size_t)slots[i] * bb, bb,
+                         hipMemcpyDeviceToHost));
+    return NP_OK;
+}
+
+np_status np_layer_info(const np_layer* L, int32_t* out6) {
+    if (!L || !out6) return fail(NP_EINVAL, "layer and out must not be NULL");
+    out6[0] = L->desc.d_model;
+    out6[1] = L->desc.d_ff;
+    out6[2] = L->desc.k_max;
+    out6[3] = L->desc.n_rows;
+    out6[4] = L->n_active;
+    out6[5] = L->n_in;
+    return NP_OK;
+}
+
+np_status np_layer_counters(const np_layer* L, int64_t* out2) {
+    if (!L || !out2) return fail(NP_EINVAL, "layer and out must not be NULL");
+    out2[0] = L->total_active;
+    out2[1] = L->total_in;
+    return NP_OK;
+}
+
+np_status np_probe_read(const void* src, int64_t bytes, float* sink, void* stream) {
+    if (!src || !sink || bytes <= 0 || bytes % 16 || !aligned16(src))
+        return fail(NP_EINVAL, "probe_read needs 16-byte aligned src, bytes > 0 and a multiple of 16");
+    NP_HIP(launch_probe_read(src, bytes, sink, (hipStream_t)stream));
+    return NP_OK;
+}
+
+np_status np_probe_copy(void* dst, const void* src, int64_t bytes, void* stream) {
+    if (!src || !dst || bytes <= 0 || bytes % 16 || !aligned16(src) || !aligned16(dst))
+        return fail(NP_EINVAL, "probe_copy needs 16-byte aligned pointers, bytes a multiple of 16");
+    NP_HIP(launch_probe_copy(dst, src, bytes, (hipStream_t)stream));
+    return NP_OK;
+}
+
+}  // extern "C"

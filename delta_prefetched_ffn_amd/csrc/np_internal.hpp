@@ -1,0 +1,88 @@
+// Internal declarations shared by the host library and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace np {
+
+// Library limits (also documented in include/np.h).
+constexpr int kMaxDModel = 16384;
+constexpr int kMaxDff = 65536;
+constexpr int kMaxKmax = 65536;
+constexpr int kMaxCentroids = 65536;
+constexpr int kMaxWords = kMaxDff / 64;  // mask words per set
+constexpr int kMaxKWords = kMaxKmax / 64;
+constexpr int kMaxLayersPerLaunch = 64;
+
+// Device error bits (counts[3]).
+constexpr int kErrFreeExhausted = 1;   // delta assign: no free slot for an incoming neuron
+constexpr int kErrBadList = 2;         // scatter/FFN: a list entry out of range
+constexpr int kErrWindow = 4;          // FFN: window larger than the LDS staging
+constexpr int kErrSpin = 8;            // FFN: a wait hit its iteration limit
+
+// Everything a kernel needs about one layer; lives in device memory.
+struct LayerDev {
+    const uint64_t* masks;   // [n_tables][C][W]
+    uint64_t* res;           // [W]  resident set R
+    uint64_t* freeb;         // [Kw] free slots
+    int32_t* slot_map;       // [M]
+    int32_t* owner;          // [K]
+    int32_t* d_in;           // [K]
+    int32_t* slot_in;        // [K]
+    int32_t* d_out;          // [K]
+    int32_t* act;            // [K] ascending occupied slots
+    int32_t* counts;         // [4] n_in, n_out, n_active, error bits
+    int32_t W, Kw, M, K;
+    int32_t mode, n_tables, C, pad;
+};
+
+struct DeltaLaunch {
+    const LayerDev* layers[kMaxLayersPerLaunch];
+    int32_t cid[kMaxLayersPerLaunch][2];
+    int32_t n_layers;
+};
+
+// FFN launch shape (chosen on the host from the host-known |S|).
+struct FfnShape {
+    int nt;        // threads per workgroup
+    int p1;        // gate/up chunks (= workgroups with gate/up work)
+    int q;         // column tiles of the down phase
+    int tw;        // columns per tile (multiple of 8)
+    int nwg;       // p1 + q - 1 workgroups
+    int jx;        // 16-byte x chunks per thread (gate/up phase)
+    int win_max;   // LDS window capacity (positions)
+};
+
+struct FfnArgs {
+    const uint16_t* buf;    // [K][R][d]
+    const int32_t* act;     // [K]
+    int32_t* counts;        // [4]
+    const float* x;         // [d]
+    float* y;               // [d]
+    float* hval;            // [K]
+    float* partials;        // [nwg][tw]
+    uint32_t* flags;        // [p1] per-chunk "h ready" epochs
+    uint32_t* tcnt;         // [q] per-tile arrival counters (0 between launches)
+    uint32_t* ctl;          // [2] finished-workgroup counter, epoch
+    int32_t d, K, R;
+    int32_t p1, q, tw, nwg;
+};
+
+// Launchers (return hipError_t from the launch).
+hipError_t launch_delta_assign(const DeltaLaunch& a, hipStream_t s);
+hipError_t launch_scatter(int32_t* counts, const int32_t* d_in, const int32_t* slot_in,
+                          const uint16_t* store, uint16_t* buf, int32_t M, int32_t K,
+                          int32_t bundle_elems, int grid, hipStream_t s);
+hipError_t launch_sparse_ffn(const FfnArgs& a, const FfnShape& sh, bool gated, hipStream_t s);
+hipError_t launch_probe_read(const void* src, int64_t bytes, float* sink, hipStream_t s);
+hipError_t launch_probe_copy(void* dst, const void* src, int64_t bytes, hipStream_t s);
+
+// FFN sync area of a layer: flags at [0, kP1Cap), tile counters at
+// [kP1Cap, kP1Cap + kMaxTiles), then the done counter and the epoch. The
+// layout is fixed so that launches with different shapes never alias.
+constexpr int kP1Cap = 4096;
+constexpr int kMaxTiles = kMaxDModel / 64;
+constexpr int kSyncWords = kP1Cap + kMaxTiles + 2;
+
+}  // namespace np

@@ -1,0 +1,193 @@
+/*
+ * np.h -- delta-prefetched sparse FFN for AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * The method: "NeuroPrefetcher: Storage-Aware Sparse LLM Inference via Delta
+ * Prefetching" (Dhar et al.). For every sparse FFN layer and every decode
+ * token at batch 1:
+ *   1. the predicted active neuron set is decoded from the layer's gate and
+ *      up centroid bitmasks (section 3.4; section 3.1: the centroid table is
+ *      always resident);
+ *   2. it is diffed against the rows resident in a fixed K_max-slot buffer
+ *      (section 3.4, "by set difference");
+ *   3. outgoing neurons release their slots and incoming neurons take freed
+ *      slots, tracked by a slot map that is -1 for non-resident neurons
+ *      (section 3.4; no compaction);
+ *   4. the incoming neurons' [gate|up|down^T] bundles are scattered from the
+ *      backing row store into their slots (section 3.5, the fused
+ *      deinterleave-and-scatter on its own stream);
+ *   5. the sparse FFN y = sum_{i in S} down_i * relu(gate_i . x) * (up_i . x)
+ *      runs over the resident slots only (section 3.4: row i of gate, up and
+ *      down^T per active neuron; the slot map locates the rows). A non-gated
+ *      [up|down^T] bundle (LLM in a flash, section 3.2) gives
+ *      y = sum_{i in S} down_i * relu(up_i . x).
+ *
+ * Conventions used by every call:
+ *   - Every call returns np_status; NP_OK is 0. On any error the call has
+ *     enqueued nothing and changed no state; np_last_error() returns a
+ *     thread-local description of the last failure of the calling thread.
+ *   - All argument, range, capacity and call-order checks run on the host,
+ *     synchronously, before anything is enqueued.
+ *   - "stream" arguments are hipStream_t handles passed as void*; NULL means
+ *     the device's null stream. Compute calls are asynchronous on their
+ *     stream; np_layer_read_* calls synchronize the layer's device.
+ *   - A layer is not thread-safe, and its calls must be ordered (one stream,
+ *     or the caller's events). Different layers may be driven from
+ *     different threads.
+ *   - Bit b of mask word w is neuron 64*w + b. Bundles are bf16 (raw 16-bit
+ *     patterns), rows in the order gate, up, down^T (n_rows = 3) or up,
+ *     down^T (n_rows = 2), d_model values per row, no padding.
+ *   - The library owns every device allocation it makes; the caller owns the
+ *     row store, x and y buffers and the streams.
+ *
+ * Limits checked at np_layer_create: d_model % 8 == 0 (128-bit rows),
+ * 8 <= d_model <= 16384, 1 <= d_ff <= 65536, 1 <= k_max <= min(d_ff, 65536),
+ * n_rows in {2, 3}, 1 <= n_centroids <= 65536.
+ */
+#ifndef NP_H
+#define NP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NP_OK = 0,
+    NP_EINVAL = 1,     /* bad argument, shape, pointer or centroid ID            */
+    NP_ECAPACITY = 2,  /* |S| > k_max for the requested centroid IDs             */
+    NP_ENOMEM = 3,     /* device or host allocation failed                       */
+    NP_EHIP = 4,       /* a HIP runtime call failed (text in np_last_error)      */
+    NP_ESTATE = 5,     /* call-order violation (see np_delta_assign)             */
+    NP_EDEVICE = 6     /* a kernel reported an inconsistency (np_layer_read_*)   */
+} np_status;
+
+/* How the two centroid masks combine into the active set (section 3.4 of the
+ * paper intersects them; the Llama-shaped workloads use their union; SINGLE
+ * uses one table for a non-gated FFN). */
+typedef enum { NP_MASK_UNION = 0, NP_MASK_INTERSECT = 1, NP_MASK_SINGLE = 2 } np_mask_mode;
+
+typedef enum { NP_ACT_RELU = 0 } np_act;
+
+typedef struct np_layer np_layer; /* opaque: one sparse FFN layer */
+
+typedef struct np_layer_desc {
+    int32_t d_model;     /* d: values per row                                    */
+    int32_t d_ff;        /* M: neurons                                           */
+    int32_t k_max;       /* K_max: resident slots                                */
+    int32_t n_rows;      /* 3 = [gate|up|down^T], 2 = [up|down^T]                */
+    int32_t n_centroids; /* C: masks per table                                   */
+    int32_t mask_mode;   /* np_mask_mode                                         */
+    int32_t act;         /* np_act                                               */
+    int32_t device;      /* HIP device ordinal of the layer                      */
+    /* host uint64 [n_tables][n_centroids][ceil(d_ff/64)], n_tables = 1 for
+     * SINGLE else 2 (gate table, then up table). COPIED at create. Bits at
+     * or above d_ff in the last word must be zero (NP_EINVAL otherwise). */
+    const uint64_t* masks;
+    /* bf16 [d_ff][n_rows][d_model], 16-byte aligned, BORROWED: the caller
+     * keeps it alive and unchanged while the layer exists. It may be device
+     * memory of `device` (the backing store sits in HBM) or pinned host
+     * memory from hipHostMalloc (the scatter kernel then pulls the delta
+     * bundles over the host link). Pageable host memory gives NP_EINVAL. */
+    const void* row_store;
+} np_layer_desc;
+
+/* Validates desc, allocates the slot buffer bf16 [k_max][n_rows][d_model]
+ * (zero-filled), the slot map int32 [d_ff] (= -1), the owner table int32
+ * [k_max] (= -1), the resident and free bitsets, the delta lists and the
+ * FFN scratch, and copies the masks to the device. */
+np_status np_layer_create(const np_layer_desc* desc, np_layer** out);
+
+/* Frees everything the layer allocated (synchronizes its device first). */
+np_status np_layer_destroy(np_layer* layer);
+
+/* Back to the state np_layer_create leaves (empty buffer, zero-filled); the
+ * next np_delta_assign is a cold start that fetches the whole active set
+ * (section 3.4). Synchronous. */
+np_status np_layer_reset(np_layer* layer);
+
+/* Steps 1-3 for one layer (section 3.4). Builds S from mask gate_cid of the
+ * gate table and up_cid of the up table (up_cid is ignored for SINGLE),
+ * computes D_in = S \ R and D_out = R \ S in ascending neuron order,
+ * releases the slots of D_out, gives the i-th neuron of D_in the i-th free
+ * slot in ascending slot order, updates the slot map and owner table, and
+ * lists the occupied slots in ascending order. Then R = S.
+ * Errors: NP_EINVAL (cid out of range), NP_ECAPACITY (|S| > k_max; state
+ * unchanged), NP_ESTATE (the previous assignment has not been scattered). */
+np_status np_delta_assign(np_layer* layer, int32_t gate_cid, int32_t up_cid, void* stream);
+
+/* Step 4 (section 3.5): copies the bundle of each neuron of the last D_in
+ * from the row store into its assigned slot with 128-bit loads and stores.
+ * Errors: NP_ESTATE unless np_delta_assign was the previous state change. */
+np_status np_scatter_rows(np_layer* layer, void* stream);
+
+/* Step 5: y[d_model] = sum over the resident (= active) slots of
+ * down * act(gate . x) * (up . x), bf16 weights, fp32 arithmetic and
+ * accumulation, fixed-order (run-to-run identical) reduction.
+ * x and y are device fp32 [d_model], 16-byte aligned, not overlapping.
+ * Errors: NP_ESTATE unless the last assignment has been scattered. */
+np_status np_sparse_ffn(np_layer* layer, const float* x, float* y, void* stream);
+
+/* One decode token over n_layers layers of one device with equal d_model
+ * (sections 3.1, 3.4, 3.5): validates every layer's cids on the host (a
+ * failure leaves every layer unchanged), then on compute_stream one launch
+ * assigns the deltas of all layers; on copy_stream the layer-l scatter
+ * waits for that launch; the layer-l FFN on compute_stream waits for the
+ * layer-l scatter, so scatters of later layers overlap earlier FFNs.
+ * cids: host int32 [n_layers][2] (gate, up). x, y: device fp32
+ * [n_layers][d_model]. copy_stream may equal compute_stream. Every layer
+ * must be in the fresh or scattered state (NP_ESTATE otherwise). */
+np_status np_decode_step(np_layer* const* layers, int32_t n_layers, const int32_t* cids,
+                         const float* x, float* y, void* compute_stream, void* copy_stream);
+
+/* Synchronizes the layer's device, then copies the current state to host
+ * buffers (any pointer may be NULL): slot_map int32 [d_ff], owner int32
+ * [k_max], d_in / slot_in / d_out int32 [k_max] (lists of the last
+ * assignment), act_slots int32 [k_max] (ascending occupied slots), counts
+ * int32 [4] = {n_in, n_out, n_active, device error bits}.
+ * Returns NP_EDEVICE if a kernel of this layer reported an inconsistency
+ * (nonzero error bits; the data is still copied). */
+np_status np_layer_read_state(const np_layer* layer, int32_t* slot_map, int32_t* owner,
+                              int32_t* d_in, int32_t* slot_in, int32_t* d_out,
+                              int32_t* act_slots, int32_t* counts);
+
+/* Synchronizes, then copies the bundles of the given slots (each < k_max)
+ * into dst (host, n * n_rows * d_model bf16). slots == NULL with
+ * n == k_max copies the whole buffer. */
+np_status np_layer_read_rows(const np_layer* layer, const int32_t* slots, int32_t n, void* dst);
+
+/* Host-side view: out[0..5] = {d_model, d_ff, k_max, n_rows, n_active of the
+ * last accepted assignment, n_in of the last accepted assignment}. */
+np_status np_layer_info(const np_layer* layer, int32_t* out6);
+
+/* Host-side running totals since create/reset: out2[0] = sum of |S| and
+ * out2[1] = sum of |D_in| over every accepted assignment (bundles read by the
+ * FFN and bundles written by the scatter, in units of one bundle). */
+np_status np_layer_counters(const np_layer* layer, int64_t* out2);
+
+/* FFN launch shape of this layer: about slots_per_wg active slots per
+ * workgroup for the gate/up phase (1..16, default 5) and tile_cols output
+ * columns per workgroup for the down phase (multiple of 8, 64..1024,
+ * default 256). 0 keeps the current value. Changes speed, not results'
+ * validity (the summation order depends on the shape, so bit patterns of y
+ * may change within fp32 rounding). */
+np_status np_layer_set_ffn_shape(np_layer* layer, int32_t slots_per_wg, int32_t tile_cols);
+
+/* Thread-local text of the calling thread's last error ("" if none). */
+const char* np_last_error(void);
+
+/* ---- measurement probes (roofline denominators and counter scaling) ---- */
+
+/* Streaming read of `bytes` (multiple of 16) at src (device or pinned host);
+ * writes one float per workgroup into sink (device, >= 65536 floats) so the
+ * loads are not dead. */
+np_status np_probe_read(const void* src, int64_t bytes, float* sink, void* stream);
+
+/* Plain 128-bit copy kernel, bytes a multiple of 16, no overlap. */
+np_status np_probe_copy(void* dst, const void* src, int64_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NP_H */

@@ -1,0 +1,89 @@
+"""GPU parity at the full workload shapes, in the launch configuration the
+benchmark times (np_decode_step on a compute and a copy stream).
+
+Every (step, layer): delta lists, slot map, owner table and active-slot list
+bit-exact against the oracle. Written rows bit-exact on three layers at every
+16th step; whole buffer of layer 0 at the end (stale rows included). FFN
+outputs on sampled (step, layer) pairs, computed one by one by the oracle from
+regenerated bundles, within max-abs 2e-2 and relative L2 5e-3.
+"""
+import time
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from tests.harness import OracleRun, check_y, compare_state, make_layer, torch_mod
+from workload.gen import CONFIGS, Workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(f"[full-config] {msg}", flush=True)
+
+
+def run_full(num: int, where: str = "device", steps: int | None = None, ffn_samples: int = 10):
+    from delta_prefetched_ffn_amd import binding as B
+    torch = torch_mod()
+    assert torch.cuda.is_available()
+    wl = Workload(CONFIGS[num])
+    c = wl.cfg
+    T = c.T if steps is None else steps
+    t0 = time.time()
+    layers = []
+    for l in range(c.L):
+        layers.append(make_layer(wl, l, where)[0])
+    _log(f"config {num}: {c.L} layers built ({where} store) in {time.time() - t0:.1f}s")
+    orc = OracleRun(wl, keep_buffer=False)
+    x_all = wl.x_all()[:T]
+    x = torch.from_numpy(np.ascontiguousarray(x_all)).cuda()
+    y = torch.zeros_like(x)
+    cs, ps = torch.cuda.Stream(), torch.cuda.Stream()
+    row_layers = sorted({0, c.L // 2, c.L - 1})
+    last_written = np.full(c.K, -1, dtype=np.int64)  # layer 0: neuron whose bundle a slot last received
+    for t in range(T):
+        B.decode_step(layers, wl.cids()[t], x[t].data_ptr(), y[t].data_ptr(), cs.cuda_stream, ps.cuda_stream)
+        for l in range(c.L):
+            st = layers[l].read_state()
+            S, res = orc.step(t, l)
+            compare_state(st, orc.layers[l], res, S, f"cfg{num} t={t} l={l}")
+            if l == 0:
+                last_written[res.slot_in] = res.d_in
+            if l in row_layers and (t % 16 == 0 or t == T - 1) and res.d_in.size:
+                got = layers[l].read_rows(res.slot_in)
+                assert np.array_equal(got, wl.bundles(l, res.d_in)), f"cfg{num} t={t} l={l}: rows"
+        if t % 32 == 0:
+            _log(f"config {num}: step {t}/{T} state ok ({time.time() - t0:.1f}s)")
+    torch.cuda.synchronize()
+    # whole buffer of layer 0, stale rows included
+    buf = layers[0].read_rows()
+    written = np.nonzero(last_written >= 0)[0]
+    assert np.array_equal(buf[written], wl.bundles(0, last_written[written]))
+    unwritten = np.nonzero(last_written < 0)[0]
+    assert (buf[unwritten] == 0).all()
+    # sampled FFN outputs
+    yh = y.cpu().numpy()
+    rng = np.random.default_rng(num)
+    picks = {(0, 0), (T - 1, c.L - 1)} | {(int(rng.integers(T)), int(rng.integers(c.L))) for _ in range(ffn_samples)}
+    for t, l in sorted(picks):
+        S = orc.active(t, l)
+        ref = O.sparse_ffn(wl.bundles(l, S), c.R, c.d, np.arange(S.size, dtype=np.int32), x_all[t, l])
+        check_y(yh[t, l], ref, f"cfg{num} t={t} l={l}")
+    _log(f"config {num}: {T} steps, {len(picks)} FFN samples ok in {time.time() - t0:.1f}s")
+    for layer in layers:
+        layer.close()
+    del layers
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("num", [2, 3, 4, 5])
+def test_full_config_device_store(num):
+    run_full(num, "device")
+
+
+@pytest.mark.timeout(600)
+def test_full_config2_pinned_host_store():
+    """The row store in pinned host memory: the scatter pulls bundles over the host link."""
+    run_full(2, "host", steps=12, ffn_samples=4)

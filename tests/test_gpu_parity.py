@@ -1,0 +1,203 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bit-exact: delta lists, slot assignments, slot map, owner table, active-slot
+list and buffer bytes. FFN output: max |dy| <= 2e-2 and relative L2 <= 5e-3
+against the fp64 oracle; bit-exact on exact dyadic inputs.
+"""
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from tests.harness import OracleRun, check_y, compare_state, make_layer, torch_mod, upload_store
+from workload.gen import CONFIGS, Config, Workload, small_config
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    t = torch_mod()
+    assert t.cuda.is_available(), "GPU tests need a visible GPU"
+    from delta_prefetched_ffn_amd import binding
+    binding.lib()  # fails loudly if the HIP library is missing
+    return t
+
+
+def _stream(torch):
+    return torch.cuda.current_stream().cuda_stream
+
+
+@pytest.mark.parametrize("where", ["device", "host"])
+def test_config1_single_layer_calls(torch, where):
+    wl = Workload(CONFIGS[1])
+    c = wl.cfg
+    layer, store = make_layer(wl, 0, where)
+    orc = OracleRun(wl)
+    x_all = wl.x_all()
+    x = torch.from_numpy(x_all).cuda()
+    y = torch.zeros_like(x)
+    s = _stream(torch)
+    for t in range(c.T):
+        g, u = (int(v) for v in wl.cids()[t, 0])
+        layer.delta_assign(g, u, s)
+        layer.scatter_rows(s)
+        layer.sparse_ffn(x[t, 0].data_ptr(), y[t, 0].data_ptr(), s)
+        st = layer.read_state()
+        S, res = orc.step(t, 0, store)
+        compare_state(st, orc.layers[0], res, S, f"t={t}")
+        assert np.array_equal(layer.read_rows(), orc.layers[0].buf), f"t={t}: buffer differs"
+        check_y(y[t, 0].cpu().numpy(), O.sparse_ffn(store, c.R, c.d, S, x_all[t, 0]), f"t={t}")
+    layer.close()
+
+
+SMALL = [
+    small_config(901, L=3, d=64, M=200, K=96, C=8, mode="union", m=40, swap=6, T=8),
+    small_config(902, L=2, d=200, M=1000, K=333, C=6, mode="union", m=150, swap=20, T=8),
+    small_config(903, L=2, d=1000, M=130, K=50, C=5, mode="intersect", m=40, swap=8, T=8),
+    small_config(904, L=2, d=4096, M=700, K=300, C=5, mode="single", R=2, m=250, swap=40, T=8),
+    small_config(905, L=2, d=5120, M=640, K=256, C=4, mode="union", m=100, swap=20, T=6),
+    small_config(906, L=2, d=7168, M=1100, K=700, C=4, mode="union", m=300, swap=50, T=6),
+    small_config(907, L=1, d=8, M=64, K=64, C=3, mode="union", m=20, swap=4, T=6),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: f"d{c.d}_M{c.M}_K{c.K}_{c.mode}_R{c.R}")
+@pytest.mark.parametrize("streams", [1, 2])
+def test_small_shapes_decode_step(torch, cfg, streams):
+    from delta_prefetched_ffn_amd import binding as B
+    wl = Workload(cfg)
+    layers, stores = zip(*[make_layer(wl, l) for l in range(cfg.L)])
+    orc = OracleRun(wl)
+    x_all = wl.x_all()
+    x = torch.from_numpy(x_all).cuda()
+    y = torch.zeros_like(x)
+    cs = torch.cuda.Stream()
+    ps = torch.cuda.Stream() if streams == 2 else cs
+    for t in range(cfg.T):
+        B.decode_step(layers, wl.cids()[t], x[t].data_ptr(), y[t].data_ptr(), cs.cuda_stream, ps.cuda_stream)
+        for l, layer in enumerate(layers):
+            st = layer.read_state()
+            S, res = orc.step(t, l, stores[l])
+            compare_state(st, orc.layers[l], res, S, f"t={t} l={l}")
+            assert np.array_equal(layer.read_rows(), orc.layers[l].buf), f"t={t} l={l}: buffer"
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+    orc2 = OracleRun(wl, keep_buffer=False)
+    for t in range(cfg.T):
+        for l in range(cfg.L):
+            S = orc2.active(t, l)
+            check_y(yh[t, l], O.sparse_ffn(stores[l], cfg.R, cfg.d, S, x_all[t, l]), f"t={t} l={l}")
+    for layer in layers:
+        layer.close()
+
+
+def _dyadic_store(rng, M, R, d):
+    """Gate/up rows: 8 nonzeros in {+-1,+-2}/64; down rows: dense {-2..2}/64. Exact in bf16."""
+    w = np.zeros((M, R, d), dtype=np.float32)
+    for n in range(M):
+        for r in range(R - 1):
+            cols = rng.choice(d, size=8, replace=False)
+            w[n, r, cols] = rng.choice([-2, -1, 1, 2], size=8) / 64.0
+        w[n, R - 1] = rng.integers(-2, 3, size=d) / 64.0
+    return (w.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("R", [3, 2])
+def test_exact_dyadic_inputs_bit_exact(torch, R):
+    """Every partial sum is a dyadic rational below 2^24 units: fp32 is exact in any order."""
+    from delta_prefetched_ffn_amd import binding as B
+    rng = np.random.default_rng(40 + R)
+    M, d, K = 512, 4096, 256
+    store = _dyadic_store(rng, M, R, d)
+    mode = "union" if R == 3 else "single"
+    cfg = Config(950 + R, "dyadic", L=1, d=d, M=M, R=R, K=K, C=4, mode=mode, T=4, m=100, swap=10)
+    wl = Workload(cfg)
+    layer, _ = make_layer(wl, 0, store=store)
+    orc = OracleRun(wl, keep_buffer=False)
+    s = _stream(torch)
+    for t in range(cfg.T):
+        x_np = (rng.integers(-8, 9, size=d) / 8.0).astype(np.float32)
+        x = torch.from_numpy(x_np).cuda()
+        y = torch.empty_like(x)
+        g, u = (int(v) for v in wl.cids()[t, 0])
+        layer.delta_assign(g, u, s)
+        layer.scatter_rows(s)
+        layer.sparse_ffn(x.data_ptr(), y.data_ptr(), s)
+        S = orc.active(t, 0)
+        assert S.size <= 256
+        ref = O.sparse_ffn(store, R, d, S, x_np)
+        got = y.cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, ref), f"t={t}: max diff {np.abs(got - ref).max()}"
+    layer.close()
+
+
+def test_decode_paths_agree_and_repeat_bitwise(torch):
+    """One stream, two streams and per-layer calls give bit-identical y; reruns too."""
+    from delta_prefetched_ffn_amd import binding as B
+    cfg = small_config(960, L=3, d=4096, M=3000, K=600, C=6, mode="union", m=250, swap=30, T=6)
+    wl = Workload(cfg)
+    x_all = wl.x_all()
+    x = torch.from_numpy(x_all).cuda()
+    outs = []
+    for path in ["two", "one", "calls", "two"]:
+        layers = [make_layer(wl, l)[0] for l in range(cfg.L)]
+        y = torch.zeros_like(x)
+        cs, ps = torch.cuda.Stream(), torch.cuda.Stream()
+        for t in range(cfg.T):
+            if path == "calls":
+                for l, layer in enumerate(layers):
+                    g, u = (int(v) for v in wl.cids()[t, l])
+                    layer.delta_assign(g, u, cs.cuda_stream)
+                    layer.scatter_rows(cs.cuda_stream)
+                    layer.sparse_ffn(x[t, l].data_ptr(), y[t, l].data_ptr(), cs.cuda_stream)
+            else:
+                B.decode_step(layers, wl.cids()[t], x[t].data_ptr(), y[t].data_ptr(), cs.cuda_stream,
+                              (ps if path == "two" else cs).cuda_stream)
+        torch.cuda.synchronize()
+        outs.append(y.cpu().numpy())
+        for layer in layers:
+            layer.close()
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
+
+
+def test_edge_cases_empty_full_turnover_and_exact_capacity(torch):
+    from delta_prefetched_ffn_amd import binding as B
+    M, K, d, R = 256, 64, 128, 3
+    W = M // 64
+
+    def mask(ids):
+        m = np.zeros(M, dtype=bool)
+        m[list(ids)] = True
+        return np.packbits(m.astype(np.uint8), bitorder="little").view("<u8").astype(np.uint64)
+
+    sets = [[], list(range(0, 64)), list(range(0, 64)), list(range(64, 128)), list(range(100, 140)), [],
+            list(range(192, 256))]
+    gate = np.stack([mask(s) for s in sets])
+    up = np.stack([mask([]) for _ in sets])
+    masks = np.stack([gate, up])
+    rng = np.random.default_rng(3)
+    store = ((rng.standard_normal((M, R, d)).astype(np.float32) * 0.02).view(np.uint32) >> 16).astype(np.uint16)
+    dev = upload_store(store, "device")
+    layer = B.Layer(d_model=d, d_ff=M, k_max=K, n_rows=R, masks=masks, mask_mode=B.MASK_UNION,
+                    row_store=dev.data_ptr(), keepalive=dev)
+    ol = O.OracleLayer(M, K, R, d)
+    s = _stream(torch)
+    x_np = rng.standard_normal(d).astype(np.float32)
+    x = torch.from_numpy(x_np).cuda()
+    for i, S_ids in enumerate(sets):
+        y = torch.full((d,), float("nan"), device="cuda")
+        layer.delta_assign(i, i, s)
+        layer.scatter_rows(s)
+        layer.sparse_ffn(x.data_ptr(), y.data_ptr(), s)
+        st = layer.read_state()
+        S = np.array(S_ids, dtype=np.int32)
+        res = ol.step(S)
+        ol.copy_bundles(store, res)
+        compare_state(st, ol, res, S, f"step {i}")
+        assert np.array_equal(layer.read_rows(), ol.buf)
+        yh = y.cpu().numpy()
+        if not S_ids:
+            assert (yh == 0).all()
+        check_y(yh, O.sparse_ffn(store, R, d, S, x_np), f"step {i}")
+    layer.close()

@@ -7,37 +7,38 @@
 // does not matter.
 //
 // Batch-1 decode is a memory-bound GEMV (about 1 flop per byte), so there is no
-// MFMA here: the kernel is built so that every weight byte crosses HBM exactly
-// once and the HBM queues fill immediately.
+// MFMA here. The kernel is built so that every weight byte crosses HBM once,
+// every workgroup has all of its loads in flight right after it learns its slot
+// list, and the cross-workgroup exchanges cost one round trip each.
 //
 // Decomposition (n active slots, listed in ascending slot order):
 //   * The slot list is cut into P1 balanced chunks. Workgroup w < P1 computes
 //     h for its chunk (phase 1): full-row dot products of the gate and up rows
 //     with x (x lives in registers: each lane always covers the same 16-byte
-//     column chunks), reduced across the workgroup, then h goes to global
-//     memory and a per-chunk flag is released.
+//     column chunks), reduced across the workgroup.
 //   * The down rows are cut into Q column tiles of TW columns. Workgroup w
 //     (0 <= w < P1 + Q - 1) takes tile w mod Q over the window of chunks
-//     [w - Q + 1, w] (phase 2): it issues its down-row loads first, then
-//     waits for the flags of the window's chunks -- all produced by
-//     workgroups with lower IDs or by itself, so the wait always ends once
-//     the earlier workgroups, dispatched first, finish phase 1 -- and
-//     accumulates h * down into TW fp32 partial sums.
+//     [w - Q + 1, w] (phase 2). Its down-row loads are issued before phase 1,
+//     so they overlap the gate/up traffic.
 //   * Over the contributors of a tile (w = t, t + Q, ...) the windows cover
-//     every chunk exactly once. The last contributor to arrive sums the
-//     tile's partials in ascending contributor order (fixed order, so results
-//     are identical run to run) and writes y.
-// Partial traffic is (P1 + Q - 1) * TW * 4 bytes, about 1% of the row bytes.
-// The epoch word makes the flags reusable without clearing; the last
-// workgroup of a launch advances it, and each tile's last contributor resets
-// that tile's counter, so consecutive launches need no memset.
+//     every chunk exactly once. The highest contributor of a tile sums the
+//     tile's partials in ascending contributor order (fixed order: results are
+//     identical run to run) and writes y.
+//
+// Exchanges between workgroups carry their own validity: every h value and
+// every partial sum is stored as one 64-bit word (launch sequence number,
+// value) with an L2-coherent (agent-scope) store, and the reader re-reads a
+// word until its sequence number is this launch's. So there are no flags, no
+// fences and no counters, and a reader waits only for workgroups with lower
+// IDs, which the dispatcher starts first: every wait ends. A wait also gives
+// up after a fixed number of polls and reports an error bit instead of hanging.
 #include "np_internal.hpp"
 
 namespace np {
 namespace {
 
-constexpr int kWinMax = 2048;         // staged window positions per workgroup
-constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr int kWinMax = 2048;            // staged window positions per workgroup
+constexpr uint32_t kSpinLimit = 1u << 20;
 
 __device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -66,12 +67,18 @@ __device__ inline void axpy8(float* acc, const float h, const uint4 v) {
     acc[7] = fmaf(h, bf_hi(v.w), acc[7]);
 }
 
-__device__ inline uint32_t ld_acquire(const uint32_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+__device__ inline uint64_t ld_pair(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ inline void st_pair(uint64_t* p, uint32_t seq, float v) {
+    __hip_atomic_store(p, ((uint64_t)__float_as_uint(v) << 32) | seq, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint32_t pair_seq(uint64_t p) { return (uint32_t)p; }
+__device__ inline float pair_val(uint64_t p) { return __uint_as_float((uint32_t)(p >> 32)); }
 
 // NT threads; JX 16-byte x chunks per lane; SB slots per phase-1 batch per row lane;
-// U2 rows per lane per phase-2 batch.
+// U2 down rows per lane per phase-2 batch.
 template <int NT, int JX, bool GATED, int SB, int U2>
 __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     constexpr int kWaves = NT / 64;
@@ -81,15 +88,32 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     __shared__ int s_act[kWinMax];
     __shared__ float s_red1[kWaves * SB * NR1];
     __shared__ float s_red2[NT * 8];
-    __shared__ int s_last;
 
     const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int d = a.d;
-    uint32_t* flags = a.flags;
-    uint32_t* tcnt = a.tcnt;
-    uint32_t* done = a.ctl;
-    uint32_t* epoch = a.ctl + 1;
-    const uint32_t tgt = __hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    const int d = a.d, cpr = d >> 3;
+    const uint32_t seq = a.seq;
+
+    // Phase-1 lane geometry: CL lanes share a row (power of two), RL row lanes.
+    int CL = NT;
+    while (CL > cpr && CL > 1) CL >>= 1;
+    const int RL = NT / CL;
+    const int rl = tid / CL, cl = tid % CL;
+
+    // x for this lane's fixed column chunks (only workgroups with gate/up work need it).
+    float xv[JX][8];
+#pragma unroll
+    for (int j = 0; j < JX; ++j) {
+        const int c = cl + CL * j;
+        if (w < a.p1 && c < cpr) {
+            const float4 p = reinterpret_cast<const float4*>(a.x)[2 * c];
+            const float4 q = reinterpret_cast<const float4*>(a.x)[2 * c + 1];
+            xv[j][0] = p.x; xv[j][1] = p.y; xv[j][2] = p.z; xv[j][3] = p.w;
+            xv[j][4] = q.x; xv[j][5] = q.y; xv[j][6] = q.z; xv[j][7] = q.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xv[j][e] = 0.f;
+        }
+    }
 
     int n = a.counts[2];
     n = n < 0 ? 0 : (n > a.K ? a.K : n);
@@ -105,58 +129,62 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
         phi = plo + kWinMax;
     }
     const int wn = phi - plo;
-    for (int i = tid; i < wn; i += NT) {
-        int s = a.act[plo + i];
-        if ((unsigned)s >= (unsigned)a.K) {
-            err |= kErrBadList;
-            s = 0;
+    {
+        constexpr int kStage = (kWinMax + NT - 1) / NT;
+        int v[kStage];
+#pragma unroll
+        for (int k = 0; k < kStage; ++k) {
+            const int i = tid + k * NT;
+            v[k] = i < wn ? a.act[plo + i] : 0;
         }
-        s_act[i] = s;
+#pragma unroll
+        for (int k = 0; k < kStage; ++k) {
+            const int i = tid + k * NT;
+            const bool bad = (unsigned)v[k] >= (unsigned)a.K;
+            err |= bad ? kErrBadList : 0;
+            if (i < wn) s_act[i] = bad ? 0 : v[k];
+        }
     }
     __syncthreads();
+
+    // Phase-2 geometry and the first batch of down-row loads (issued before phase 1).
+    const int t = w % a.q;
+    const int col0 = t * a.tw;
+    const int tcols = min(a.tw, d - col0);
+    const int CT = a.tw >> 3;                 // lanes per row segment
+    const int RL2 = NT / CT;                  // row lanes
+    const int c2 = tid % CT, r2 = tid / CT;
+    const bool cok = (c2 << 3) < tcols;
+    const uint4* dbase = reinterpret_cast<const uint4*>(a.buf) + (size_t)(R - 1) * cpr + (col0 >> 3) + c2;
+    const size_t slot_stride = (size_t)R * cpr;
+    uint4 dv[U2];
+#pragma unroll
+    for (int u = 0; u < U2; ++u) {
+        const int i = r2 + u * RL2;
+        if (cok && i < wn) dv[u] = dbase[(size_t)s_act[i] * slot_stride];
+    }
 
     // ---------------- phase 1: h for chunk w ----------------
     if (w < a.p1) {
         const int c0 = max(cbeg(w), plo), c1 = min(cbeg(w + 1), phi);
-        const int CPR = d >> 3;                              // 16-byte chunks per row
-        int CL = NT;                                         // lanes per row lane (power of 2)
-        while (CL > CPR && CL > 1) CL >>= 1;
-        const int RL = NT / CL;                              // row lanes
-        const int rl = tid / CL, cl = tid % CL;
-
-        float xv[JX][8];
-#pragma unroll
-        for (int j = 0; j < JX; ++j) {
-            const int c = cl + CL * j;
-            if (c < CPR) {
-                const float4 p = reinterpret_cast<const float4*>(a.x)[2 * c];
-                const float4 q = reinterpret_cast<const float4*>(a.x)[2 * c + 1];
-                xv[j][0] = p.x; xv[j][1] = p.y; xv[j][2] = p.z; xv[j][3] = p.w;
-                xv[j][4] = q.x; xv[j][5] = q.y; xv[j][6] = q.z; xv[j][7] = q.w;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) xv[j][e] = 0.f;
-            }
-        }
-
         for (int b0 = c0; b0 < c1; b0 += SB * RL) {
-            float part[SB][NR1];
             uint4 wv[SB][NR1][JX];
 #pragma unroll
             for (int i = 0; i < SB; ++i) {
                 const int pos = b0 + rl * SB + i;
                 const bool ok = pos < c1;
                 const int slot = ok ? s_act[pos - plo] : 0;
-                const uint4* row = reinterpret_cast<const uint4*>(a.buf + (size_t)slot * R * d);
+                const uint4* row = reinterpret_cast<const uint4*>(a.buf) + (size_t)slot * slot_stride;
 #pragma unroll
                 for (int r = 0; r < NR1; ++r)
 #pragma unroll
                     for (int j = 0; j < JX; ++j) {
                         const int c = cl + CL * j;
-                        if (ok && c < CPR) wv[i][r][j] = row[r * CPR + c];
+                        if (ok && c < cpr) wv[i][r][j] = row[r * cpr + c];
                         else wv[i][r][j] = make_uint4(0, 0, 0, 0);
                     }
             }
+            float part[SB][NR1];
 #pragma unroll
             for (int i = 0; i < SB; ++i)
 #pragma unroll
@@ -166,7 +194,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
                     for (int j = 0; j < JX; ++j) acc += dot8(wv[i][r][j], xv[j]);
                     part[i][r] = acc;
                 }
-            // reduce each partial over the CL lanes of the row lane
+            // reduce over the CL lanes of each row lane: butterfly within the wave ...
             const int xr_lim = CL < 64 ? CL : 64;
 #pragma unroll
             for (int i = 0; i < SB; ++i)
@@ -174,6 +202,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
                 for (int r = 0; r < NR1; ++r)
                     for (int off = xr_lim >> 1; off > 0; off >>= 1)
                         part[i][r] += __shfl_xor(part[i][r], off, 64);
+            // ... then across the waves of the row lane through LDS
             if (CL >= 64) {
                 if (lane == 0) {
 #pragma unroll
@@ -200,67 +229,45 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
                                 v[r] = part[i][r];
                             }
                         }
-                        float h;
-                        if (GATED) h = fmaxf(v[0], 0.f) * v[1];
-                        else h = fmaxf(v[0], 0.f);
-                        a.hval[pos] = h;
+                        const float h = GATED ? fmaxf(v[0], 0.f) * v[1] : fmaxf(v[0], 0.f);
+                        st_pair(&a.hpair[pos], seq, h);
                     }
                 }
             }
-            if (CL >= 64) __syncthreads();
+            if (CL >= 64 && b0 + SB * RL < c1) __syncthreads();  // s_red1 is reused by the next batch
         }
-        __threadfence();
-        __syncthreads();
-        if (tid == 0) __hip_atomic_store(&flags[w], tgt, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
 
     // ---------------- phase 2: down tile t over the window ----------------
-    const int t = w % a.q;
-    const int col0 = t * a.tw;
-    const int tcols = min(a.tw, d - col0);
-    const int CT = a.tw >> 3;                 // lanes per row segment
-    const int RL2 = NT / CT;                  // row lanes
-    const int c2 = tid % CT, r2 = tid / CT;
-    const bool cok = (c2 << 3) < tcols;
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-
-    const uint4* dbase = reinterpret_cast<const uint4*>(a.buf) + (size_t)(R - 1) * (d >> 3) + (col0 >> 3) + c2;
-    const size_t slot_stride = (size_t)R * (d >> 3);
-
-    uint4 dv[U2];
-    int i0 = r2;                              // first window row of this lane
-#pragma unroll
-    for (int u = 0; u < U2; ++u) {
-        const int i = i0 + u * RL2;
-        if (cok && i < wn) dv[u] = dbase[(size_t)s_act[i] * slot_stride];
-    }
-
-    // Wait for the h values of the other chunks of the window (lower workgroup IDs).
-    if (lane == 0) {
-        for (int c = wlo; c <= whi; ++c) {
-            if (c == w) continue;
-            uint32_t it = 0;
-            while (ld_acquire(&flags[c]) != tgt) {
-                __builtin_amdgcn_s_sleep(2);
-                if (++it > kSpinLimit) {
-                    err |= kErrSpin;
-                    break;
-                }
-            }
-        }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-
-    while (true) {
+    for (int i0 = r2;;) {
+        uint64_t hp[U2];
 #pragma unroll
         for (int u = 0; u < U2; ++u) {
             const int i = i0 + u * RL2;
-            if (cok && i < wn) {
-                const float h = __hip_atomic_load(&a.hval[plo + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                axpy8(acc, h, dv[u]);
+            hp[u] = (cok && i < wn) ? ld_pair(&a.hpair[plo + i]) : (uint64_t)seq;
+        }
+        // h values of the window's other chunks come from lower workgroup IDs: poll until ready
+        for (uint32_t it = 0;; ++it) {
+            bool ready = true;
+#pragma unroll
+            for (int u = 0; u < U2; ++u) ready &= pair_seq(hp[u]) == seq;
+            if (ready) break;
+            if (it >= kSpinLimit) {
+                err |= kErrSpin;
+                break;
             }
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int u = 0; u < U2; ++u)
+                if (pair_seq(hp[u]) != seq) hp[u] = ld_pair(&a.hpair[plo + i0 + u * RL2]);
+        }
+#pragma unroll
+        for (int u = 0; u < U2; ++u) {
+            const int i = i0 + u * RL2;
+            if (cok && i < wn) axpy8(acc, pair_val(hp[u]), dv[u]);
         }
         i0 += U2 * RL2;
         if (i0 >= wn) break;
@@ -271,48 +278,57 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
         }
     }
 
-    // Reduce the RL2 row lanes: s_red2[r2][c2*8 + e].
+    // Reduce the RL2 row lanes: s_red2[r2][c2 * 8 + e].
 #pragma unroll
     for (int e = 0; e < 8; ++e) s_red2[r2 * a.tw + (c2 << 3) + e] = acc[e];
     __syncthreads();
+
+    const int ncontrib = (a.nwg - 1 - t) / a.q + 1;
+    const bool reducer = w == t + a.q * (ncontrib - 1);
     for (int j = tid; j < tcols; j += NT) {
         float s = 0.f;
         for (int r = 0; r < RL2; ++r) s += s_red2[r * a.tw + j];
-        __hip_atomic_store(&a.partials[(size_t)w * a.tw + j], s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __threadfence();
-    __syncthreads();
-    const int ncontrib = (a.nwg - 1 - t) / a.q + 1;
-    if (tid == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&tcnt[t], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (old == (uint32_t)(ncontrib - 1));
-    }
-    __syncthreads();
-    if (s_last) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        for (int j = tid; j < tcols; j += NT) {
-            float s = 0.f;
-            for (int k = 0; k < ncontrib; ++k)
-                s += __hip_atomic_load(&a.partials[(size_t)(t + k * a.q) * a.tw + j], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-            a.y[col0 + j] = s;
+        if (!reducer) {
+            st_pair(&a.ppair[(size_t)w * a.tw + j], seq, s);
+            continue;
         }
-        if (tid == 0) __hip_atomic_store(&tcnt[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // The tile's highest contributor: sum every contributor's partial in ascending order.
+        float y = 0.f;
+        constexpr int kB = 16;
+        for (int k0 = 0; k0 < ncontrib - 1; k0 += kB) {
+            uint64_t pp[kB];
+#pragma unroll
+            for (int k = 0; k < kB; ++k)
+                pp[k] = k0 + k < ncontrib - 1 ? ld_pair(&a.ppair[(size_t)(t + (k0 + k) * a.q) * a.tw + j])
+                                              : (uint64_t)seq;
+            for (uint32_t it = 0;; ++it) {
+                bool ready = true;
+#pragma unroll
+                for (int k = 0; k < kB; ++k) ready &= pair_seq(pp[k]) == seq;
+                if (ready) break;
+                if (it >= kSpinLimit) {
+                    err |= kErrSpin;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+                for (int k = 0; k < kB; ++k)
+                    if (pair_seq(pp[k]) != seq)
+                        pp[k] = ld_pair(&a.ppair[(size_t)(t + (k0 + k) * a.q) * a.tw + j]);
+            }
+#pragma unroll
+            for (int k = 0; k < kB; ++k)
+                if (k0 + k < ncontrib - 1) y += pair_val(pp[k]);
+        }
+        a.y[col0 + j] = y + s;
     }
     if (err) atomicOr(&a.counts[3], err);
-    if (tid == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        if (old == (uint32_t)(a.nwg - 1)) {
-            __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(epoch, tgt, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
 }
 
 template <int NT, int JX, bool G>
 hipError_t launch_t(const FfnArgs& a, const FfnShape& sh, hipStream_t s) {
-    constexpr int SB = (JX <= 2) ? 8 : 4;
-    hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, 8>), dim3(sh.nwg), dim3(NT), 0, s, a);
+    constexpr int SB = (JX <= 2) ? 6 : 4;
+    hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, 12>), dim3(sh.nwg), dim3(NT), 0, s, a);
     return hipGetLastError();
 }
 

@@ -81,16 +81,15 @@ struct np_layer {
     uint64_t* freeb = nullptr;
     int32_t* lists = nullptr;  // d_in | slot_in | d_out | act, K each
     int32_t* counts = nullptr;
-    float* hval = nullptr;
-    float* partials = nullptr;
-    uint32_t* sync = nullptr;
+    uint64_t* hpair = nullptr;
+    uint64_t* ppair = nullptr;
+    uint32_t ffn_seq = 0;
     LayerDev* ldev = nullptr;
     hipEvent_t ev_scatter = nullptr;
 
     int spw = kDefaultSlotsPerWg;
     int tw = kDefaultTileCols;
-    size_t partials_floats = 0;
-    int sync_words = 0;
+    size_t ppair_words = 0;
 
     int32_t* d_in() const { return lists; }
     int32_t* slot_in() const { return lists + desc.k_max; }
@@ -139,20 +138,24 @@ bool ffn_shape(const np_layer* L, int n, FfnShape* sh) {
 np_status alloc_ffn_scratch(np_layer* L) {
     const int q = q_of(L);
     const size_t need = (size_t)(kP1Cap + q) * L->tw;
-    if (L->partials && L->partials_floats >= need) return NP_OK;
-    if (L->partials) (void)hipFree(L->partials);
-    L->partials = nullptr;
-    if (hipMalloc(&L->partials, need * sizeof(float)) != hipSuccess) {
+    if (L->ppair && L->ppair_words >= need) return NP_OK;
+    if (L->ppair) (void)hipFree(L->ppair);
+    L->ppair = nullptr;
+    if (hipMalloc(&L->ppair, need * sizeof(uint64_t)) != hipSuccess) {
         (void)hipGetLastError();
-        return fail(NP_ENOMEM, "cannot allocate %zu FFN partial floats", need);
+        return fail(NP_ENOMEM, "cannot allocate %zu FFN partial words", need);
     }
-    L->partials_floats = need;
+    if (hipMemset(L->ppair, 0, need * sizeof(uint64_t)) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(NP_EHIP, "cannot clear FFN partial words");
+    }
+    L->ppair_words = need;
     return NP_OK;
 }
 
 void free_layer(np_layer* L) {
     void* ptrs[] = {L->d_masks, L->buf, L->slot_map, L->owner, L->res, L->freeb, L->lists,
-                    L->counts, L->hval, L->partials, L->sync, L->ldev};
+                    L->counts, L->hpair, L->ppair, L->ldev};
     for (void* p : ptrs)
         if (p) (void)hipFree(p);
     if (L->ev_scatter) (void)hipEventDestroy(L->ev_scatter);
@@ -225,11 +228,10 @@ np_status enqueue_ffn(np_layer* L, const float* x, float* y, hipStream_t s) {
     a.counts = L->counts;
     a.x = x;
     a.y = y;
-    a.hval = L->hval;
-    a.partials = L->partials;
-    a.flags = L->sync;
-    a.tcnt = L->sync + kP1Cap;
-    a.ctl = L->sync + kP1Cap + kMaxTiles;
+    a.hpair = L->hpair;
+    a.ppair = L->ppair;
+    if (++L->ffn_seq == 0) L->ffn_seq = 1;  // 0 marks never-written words
+    a.seq = L->ffn_seq;
     a.d = L->desc.d_model;
     a.K = L->desc.k_max;
     a.R = L->desc.n_rows;
@@ -342,13 +344,11 @@ np_status np_layer_create(const np_layer_desc* desc, np_layer** out) {
         return true;
     };
     const size_t buf_bytes = (size_t)K * L->bundle_elems() * 2;
-    L->sync_words = kSyncWords;
     bool ok = dmalloc((void**)&L->d_masks, mask_words * 8) && dmalloc((void**)&L->buf, buf_bytes) &&
               dmalloc((void**)&L->slot_map, (size_t)M * 4) && dmalloc((void**)&L->owner, (size_t)K * 4) &&
               dmalloc((void**)&L->res, (size_t)L->W * 8) && dmalloc((void**)&L->freeb, (size_t)L->Kw * 8) &&
               dmalloc((void**)&L->lists, (size_t)4 * K * 4) && dmalloc((void**)&L->counts, 4 * 4) &&
-              dmalloc((void**)&L->hval, (size_t)K * 4) &&
-              dmalloc((void**)&L->sync, (size_t)L->sync_words * 4) &&
+              dmalloc((void**)&L->hpair, (size_t)K * 8) &&
               dmalloc((void**)&L->ldev, sizeof(LayerDev));
     if (!ok) {
         free_layer(L);
@@ -380,7 +380,7 @@ np_status np_layer_create(const np_layer_desc* desc, np_layer** out) {
     ld.pad = 0;
     hipError_t e = hipMemcpy(L->ldev, &ld, sizeof ld, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy(L->d_masks, L->h_masks.data(), mask_words * 8, hipMemcpyHostToDevice);
-    if (e == hipSuccess) e = hipMemset(L->sync, 0, (size_t)L->sync_words * 4);
+    if (e == hipSuccess) e = hipMemset(L->hpair, 0, (size_t)K * 8);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&L->ev_scatter, hipEventDisableTiming);
     if (e != hipSuccess) {
         free_layer(L);

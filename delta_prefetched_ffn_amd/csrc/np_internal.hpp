@@ -60,11 +60,9 @@ struct FfnArgs {
     int32_t* counts;        // [4]
     const float* x;         // [d]
     float* y;               // [d]
-    float* hval;            // [K]
-    float* partials;        // [nwg][tw]
-    uint32_t* flags;        // [p1] per-chunk "h ready" epochs
-    uint32_t* tcnt;         // [q] per-tile arrival counters (0 between launches)
-    uint32_t* ctl;          // [2] finished-workgroup counter, epoch
+    uint64_t* hpair;        // [K] (launch sequence, h) words
+    uint64_t* ppair;        // [nwg][tw] (launch sequence, partial sum) words
+    uint32_t seq;           // this launch's sequence number (never 0)
     int32_t d, K, R;
     int32_t p1, q, tw, nwg;
 };
@@ -78,11 +76,8 @@ hipError_t launch_sparse_ffn(const FfnArgs& a, const FfnShape& sh, bool gated, h
 hipError_t launch_probe_read(const void* src, int64_t bytes, float* sink, hipStream_t s);
 hipError_t launch_probe_copy(void* dst, const void* src, int64_t bytes, hipStream_t s);
 
-// FFN sync area of a layer: flags at [0, kP1Cap), tile counters at
-// [kP1Cap, kP1Cap + kMaxTiles), then the done counter and the epoch. The
-// layout is fixed so that launches with different shapes never alias.
+// Gate/up chunks per FFN launch are capped; the partial-sum area is sized for it.
 constexpr int kP1Cap = 4096;
 constexpr int kMaxTiles = kMaxDModel / 64;
-constexpr int kSyncWords = kP1Cap + kMaxTiles + 2;
 
 }  // namespace np

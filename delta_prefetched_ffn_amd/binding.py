@@ -64,7 +64,7 @@ def lib() -> ctypes.CDLL:
         "np_layer_read_rows": [vp, vp, i32, vp],
         "np_layer_info": [vp, vp],
         "np_layer_counters": [vp, vp],
-        "np_layer_set_ffn_shape": [vp, i32, i32],
+        "np_layer_set_ffn_shape": [vp, i32, i32, i32],
         "np_probe_read": [vp, i64, vp, vp],
         "np_probe_copy": [vp, vp, i64, vp],
     }
@@ -128,8 +128,8 @@ class Layer:
     def sparse_ffn(self, x_ptr: int, y_ptr: int, stream: int = 0) -> None:
         _check(lib().np_sparse_ffn(self.h, x_ptr, y_ptr, stream or None))
 
-    def set_ffn_shape(self, slots_per_wg: int = 0, tile_cols: int = 0) -> None:
-        _check(lib().np_layer_set_ffn_shape(self.h, slots_per_wg, tile_cols))
+    def set_ffn_shape(self, slots_per_wg: int = 0, tile_cols: int = 0, threads: int = 0) -> None:
+        _check(lib().np_layer_set_ffn_shape(self.h, slots_per_wg, tile_cols, threads))
 
     def info(self) -> dict:
         out = np.zeros(6, dtype=np.int32)

@@ -67,6 +67,16 @@ __device__ inline void axpy8(float* acc, const float h, const uint4 v) {
     acc[7] = fmaf(h, bf_hi(v.w), acc[7]);
 }
 
+// Weight rows are read through a raw buffer resource covering the slot buffer: a lane
+// with nothing to load uses an offset past the end, which returns zeros without a
+// memory access. Every load is then an unconditional instruction, so the compiler
+// can wait for exactly the loads a computation needs.
+constexpr uint32_t kNoLoad = 0xFFFFFFF0u;
+__device__ inline uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 __device__ inline uint64_t ld_pair(const uint64_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -77,6 +87,27 @@ __device__ inline void st_pair(uint64_t* p, uint32_t seq, float v) {
 __device__ inline uint32_t pair_seq(uint64_t p) { return (uint32_t)p; }
 __device__ inline float pair_val(uint64_t p) { return __uint_as_float((uint32_t)(p >> 32)); }
 
+// One wave waits until the words addr(k), k < count, all carry this launch's sequence
+// number: each lane watches one word, the wave votes, and it sleeps between polls. A
+// waiting workgroup so costs one 8-byte load per producer per poll, not one per value:
+// polling must not compete with the bulk row traffic. Returns false at the poll limit.
+template <typename AddrFn>
+__device__ inline bool wave_wait(AddrFn addr, int count, uint32_t seq) {
+    const int lane = threadIdx.x & 63;
+    for (int k0 = 0; k0 < count; k0 += 64) {
+        const int k = k0 + lane;
+        const uint64_t* p = k < count ? addr(k) : nullptr;
+        bool ready = p == nullptr;
+        for (uint32_t it = 0;; ++it) {
+            if (!ready) ready = pair_seq(ld_pair(p)) == seq;
+            if (__all(ready)) break;
+            if (it >= kSpinLimit) return false;
+            __builtin_amdgcn_s_sleep(4);
+        }
+    }
+    return true;
+}
+
 // NT threads; JX 16-byte x chunks per lane; SB slots per phase-1 batch per row lane;
 // U2 down rows per lane per phase-2 batch.
 template <int NT, int JX, bool GATED, int SB, int U2>
@@ -86,7 +117,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     constexpr int NR1 = GATED ? 2 : 1;  // rows dotted with x per slot
 
     __shared__ int s_act[kWinMax];
-    __shared__ float s_red1[kWaves * SB * NR1];
+    __shared__ float s_red1[kWaves * SB * NR1];  // wave sums of the gate/up dot products
     __shared__ float s_red2[NT * 8];
 
     const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -115,7 +146,10 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
         }
     }
 
-    int n = a.counts[2];
+    // |S| comes from the host (it validated the capacity with it); the device count,
+    // read in parallel, is only checked against it.
+    const int n_dev = a.counts[2];
+    int n = a.n < 0 ? n_dev : a.n;
     n = n < 0 ? 0 : (n > a.K ? a.K : n);
     auto cbeg = [&](int c) { return (int)(((long long)c * n) / a.p1); };
 
@@ -147,7 +181,96 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     }
     __syncthreads();
 
-    // Phase-2 geometry and the first batch of down-row loads (issued before phase 1).
+    // ---------------- phase 1 loads: gate/up rows of chunk w (issued first) ----------------
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.buf, (short)0, (int)a.buf_bytes, 0x00020000);
+    const uint32_t slot_bytes = (uint32_t)R * cpr * 16u;
+    const bool has1 = w < a.p1;
+    const int c0 = has1 ? max(cbeg(w), plo) : 0, c1 = has1 ? min(cbeg(w + 1), phi) : 0;
+    uint4 wv[SB][NR1][JX];
+    auto load_batch = [&](int b0) {
+#pragma unroll
+        for (int i = 0; i < SB; ++i) {
+            const int pos = b0 + rl + RL * i;
+            const bool ok = pos < c1;
+            const uint32_t rowoff = ok ? (uint32_t)s_act[pos - plo] * slot_bytes : 0u;
+#pragma unroll
+            for (int r = 0; r < NR1; ++r)
+#pragma unroll
+                for (int j = 0; j < JX; ++j) {
+                    const int c = cl + CL * j;
+                    wv[i][r][j] = bload(rs, ok && c < cpr ? rowoff + (uint32_t)(r * cpr + c) * 16u : kNoLoad);
+                }
+        }
+    };
+    // h for the batch starting at b0: dot products, reduction over the row lane, store.
+    auto compute_batch = [&](int b0) {
+        constexpr int V = SB * NR1;  // partial dot products per lane (a power of two <= 64)
+        float v[V];
+#pragma unroll
+        for (int i = 0; i < SB; ++i)
+#pragma unroll
+            for (int r = 0; r < NR1; ++r) {
+                float acc = 0.f;
+#pragma unroll
+                for (int j = 0; j < JX; ++j) acc += dot8(wv[i][r][j], xv[j]);
+                v[i * NR1 + r] = acc;
+            }
+        if (CL >= 64) {
+            // Transposing butterfly over the wave: each exchange halves the values a lane
+            // holds (the lane with the offset bit set keeps the upper half), so V values need
+            // V - 1 + log2(64 / V) exchanges instead of 6 V. Afterwards lane L holds the wave
+            // sum of value vi(L), vi = the lane bits 5, 4, ... read as a binary number.
+#pragma unroll
+            for (int st = 0; (V >> st) > 1; ++st) {
+                const int m = V >> st, off = 32 >> st;
+                const bool upper = (lane & off) != 0;
+#pragma unroll
+                for (int j = 0; j < m / 2; ++j) {
+                    const float send = upper ? v[j] : v[j + m / 2];
+                    const float keep = upper ? v[j + m / 2] : v[j];
+                    v[j] = keep + __shfl_xor(send, off, 64);
+                }
+            }
+#pragma unroll
+            for (int off = 32 / V; off > 0; off >>= 1) v[0] += __shfl_xor(v[0], off, 64);
+            if ((lane & (64 / V - 1)) == 0) s_red1[wave * V + (lane / (64 / V))] = v[0];
+            __syncthreads();
+            // across the waves of each row lane: lane cl = i of the row lane finishes slot i
+            if (cl < SB) {
+                const int pos = b0 + rl + RL * cl;
+                if (pos < c1) {
+                    float g[NR1];
+#pragma unroll
+                    for (int r = 0; r < NR1; ++r) {
+                        float sm = 0.f;
+                        for (int k = 0; k < CL / 64; ++k) sm += s_red1[(rl * (CL / 64) + k) * V + cl * NR1 + r];
+                        g[r] = sm;
+                    }
+                    const float h = GATED ? fmaxf(g[0], 0.f) * g[1] : fmaxf(g[0], 0.f);
+                    st_pair(&a.hpair[pos], seq, h);
+                }
+            }
+        } else {
+            // a row lane lives inside one wave: butterfly over its CL lanes
+#pragma unroll
+            for (int k = 0; k < V; ++k)
+                for (int off = CL >> 1; off > 0; off >>= 1) v[k] += __shfl_xor(v[k], off, 64);
+            if (cl == 0) {
+#pragma unroll
+                for (int i = 0; i < SB; ++i) {
+                    const int pos = b0 + rl + RL * i;
+                    if (pos < c1) {
+                        const float h = GATED ? fmaxf(v[i * NR1], 0.f) * v[i * NR1 + NR1 - 1] : fmaxf(v[i], 0.f);
+                        st_pair(&a.hpair[pos], seq, h);
+                    }
+                }
+            }
+        }
+    };
+    if (has1) load_batch(c0);
+
+    // ---------------- phase 2 loads: first batch of the down tile (overlaps phase 1) -------------
     const int t = w % a.q;
     const int col0 = t * a.tw;
     const int tcols = min(a.tw, d - col0);
@@ -155,90 +278,41 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     const int RL2 = NT / CT;                  // row lanes
     const int c2 = tid % CT, r2 = tid / CT;
     const bool cok = (c2 << 3) < tcols;
-    const uint4* dbase = reinterpret_cast<const uint4*>(a.buf) + (size_t)(R - 1) * cpr + (col0 >> 3) + c2;
-    const size_t slot_stride = (size_t)R * cpr;
+    const uint32_t dcol = ((uint32_t)(R - 1) * cpr + (col0 >> 3) + c2) * 16u;
     uint4 dv[U2];
 #pragma unroll
     for (int u = 0; u < U2; ++u) {
         const int i = r2 + u * RL2;
-        if (cok && i < wn) dv[u] = dbase[(size_t)s_act[i] * slot_stride];
+        dv[u] = bload(rs, cok && i < wn ? (uint32_t)s_act[i] * slot_bytes + dcol : kNoLoad);
     }
 
-    // ---------------- phase 1: h for chunk w ----------------
-    if (w < a.p1) {
-        const int c0 = max(cbeg(w), plo), c1 = min(cbeg(w + 1), phi);
-        for (int b0 = c0; b0 < c1; b0 += SB * RL) {
-            uint4 wv[SB][NR1][JX];
-#pragma unroll
-            for (int i = 0; i < SB; ++i) {
-                const int pos = b0 + rl * SB + i;
-                const bool ok = pos < c1;
-                const int slot = ok ? s_act[pos - plo] : 0;
-                const uint4* row = reinterpret_cast<const uint4*>(a.buf) + (size_t)slot * slot_stride;
-#pragma unroll
-                for (int r = 0; r < NR1; ++r)
-#pragma unroll
-                    for (int j = 0; j < JX; ++j) {
-                        const int c = cl + CL * j;
-                        if (ok && c < cpr) wv[i][r][j] = row[r * cpr + c];
-                        else wv[i][r][j] = make_uint4(0, 0, 0, 0);
-                    }
-            }
-            float part[SB][NR1];
-#pragma unroll
-            for (int i = 0; i < SB; ++i)
-#pragma unroll
-                for (int r = 0; r < NR1; ++r) {
-                    float acc = 0.f;
-#pragma unroll
-                    for (int j = 0; j < JX; ++j) acc += dot8(wv[i][r][j], xv[j]);
-                    part[i][r] = acc;
-                }
-            // reduce over the CL lanes of each row lane: butterfly within the wave ...
-            const int xr_lim = CL < 64 ? CL : 64;
-#pragma unroll
-            for (int i = 0; i < SB; ++i)
-#pragma unroll
-                for (int r = 0; r < NR1; ++r)
-                    for (int off = xr_lim >> 1; off > 0; off >>= 1)
-                        part[i][r] += __shfl_xor(part[i][r], off, 64);
-            // ... then across the waves of the row lane through LDS
-            if (CL >= 64) {
-                if (lane == 0) {
-#pragma unroll
-                    for (int i = 0; i < SB; ++i)
-#pragma unroll
-                        for (int r = 0; r < NR1; ++r) s_red1[(wave * SB + i) * NR1 + r] = part[i][r];
-                }
-                __syncthreads();
-            }
-            if (cl == 0) {
-#pragma unroll
-                for (int i = 0; i < SB; ++i) {
-                    const int pos = b0 + rl * SB + i;
-                    if (pos < c1) {
-                        float v[NR1];
-#pragma unroll
-                        for (int r = 0; r < NR1; ++r) {
-                            if (CL >= 64) {
-                                float s = 0.f;
-                                for (int k = 0; k < CL / 64; ++k)
-                                    s += s_red1[((rl * (CL / 64) + k) * SB + i) * NR1 + r];
-                                v[r] = s;
-                            } else {
-                                v[r] = part[i][r];
-                            }
-                        }
-                        const float h = GATED ? fmaxf(v[0], 0.f) * v[1] : fmaxf(v[0], 0.f);
-                        st_pair(&a.hpair[pos], seq, h);
-                    }
-                }
-            }
-            if (CL >= 64 && b0 + SB * RL < c1) __syncthreads();  // s_red1 is reused by the next batch
+    // ---------------- phase 1 compute: h for chunk w ----------------
+    if (has1) {
+        compute_batch(c0);
+        for (int b0 = c0 + SB * RL; b0 < c1; b0 += SB * RL) {
+            if (CL >= 64) __syncthreads();  // s_red1 is reused by this batch
+            load_batch(b0);
+            compute_batch(b0);
         }
     }
 
     // ---------------- phase 2: down tile t over the window ----------------
+    // The other chunks of the window belong to lower workgroup IDs. Wave 0 watches the last
+    // h of each of them; the whole workgroup then reads its h values once.
+    {
+        const int others = has1 ? w - wlo : whi - wlo + 1;  // chunks wlo .. wlo + others - 1
+        bool ok = true;
+        if (wave == 0)
+            ok = wave_wait(
+                [&](int k) -> const uint64_t* {
+                    const int c = wlo + k;
+                    const int e = cbeg(c + 1);
+                    return e > cbeg(c) ? &a.hpair[e - 1] : nullptr;
+                },
+                others, seq);
+        if (!ok) err |= kErrSpin;
+        __syncthreads();
+    }
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
@@ -249,7 +323,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
             const int i = i0 + u * RL2;
             hp[u] = (cok && i < wn) ? ld_pair(&a.hpair[plo + i]) : (uint64_t)seq;
         }
-        // h values of the window's other chunks come from lower workgroup IDs: poll until ready
+        // a value stored just before its chunk's watched word may still be in flight
         for (uint32_t it = 0;; ++it) {
             bool ready = true;
 #pragma unroll
@@ -259,7 +333,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
                 err |= kErrSpin;
                 break;
             }
-            __builtin_amdgcn_s_sleep(1);
+            __builtin_amdgcn_s_sleep(4);
 #pragma unroll
             for (int u = 0; u < U2; ++u)
                 if (pair_seq(hp[u]) != seq) hp[u] = ld_pair(&a.hpair[plo + i0 + u * RL2]);
@@ -274,7 +348,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
 #pragma unroll
         for (int u = 0; u < U2; ++u) {
             const int i = i0 + u * RL2;
-            if (cok && i < wn) dv[u] = dbase[(size_t)s_act[i] * slot_stride];
+            dv[u] = bload(rs, cok && i < wn ? (uint32_t)s_act[i] * slot_bytes + dcol : kNoLoad);
         }
     }
 
@@ -285,62 +359,88 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
 
     const int ncontrib = (a.nwg - 1 - t) / a.q + 1;
     const bool reducer = w == t + a.q * (ncontrib - 1);
-    for (int j = tid; j < tcols; j += NT) {
-        float s = 0.f;
-        for (int r = 0; r < RL2; ++r) s += s_red2[r * a.tw + j];
-        if (!reducer) {
-            st_pair(&a.ppair[(size_t)w * a.tw + j], seq, s);
-            continue;
-        }
-        // The tile's highest contributor: sum every contributor's partial in ascending order.
-        float y = 0.f;
-        constexpr int kB = 16;
-        for (int k0 = 0; k0 < ncontrib - 1; k0 += kB) {
-            uint64_t pp[kB];
+    float own = 0.f;                          // this workgroup's partial of column tid (tid < tcols)
+    if (tid < tcols) {
+        for (int r = 0; r < RL2; ++r) own += s_red2[r * a.tw + tid];
+        if (!reducer) st_pair(&a.ppair[(size_t)w * a.tw + tid], seq, own);
+    }
+    if (reducer) {
+        // The tile's highest contributor sums the other contributors' partials: G groups of
+        // threads per column each take contributors g, g + G, ... (ascending), then the group
+        // sums and this workgroup's own partial are added in a fixed order.
+        // Wave 0 watches the last column of every other contributor, then all threads load.
+        bool ok = true;
+        if (wave == 0)
+            ok = wave_wait([&](int k) -> const uint64_t* { return &a.ppair[(size_t)(t + k * a.q) * a.tw + tcols - 1]; },
+                           ncontrib - 1, seq);
+        if (!ok) err |= kErrSpin;
+        __syncthreads();                      // also: s_red2 is reused for the group sums
+        const int G = NT / a.tw;
+        const int j = tid % a.tw, g = tid / a.tw;
+        constexpr int kB = 8;
+        float gs = 0.f;
+        if (j < tcols) {
+            for (int k0 = g; k0 < ncontrib - 1; k0 += kB * G) {
+                uint64_t pp[kB];
 #pragma unroll
-            for (int k = 0; k < kB; ++k)
-                pp[k] = k0 + k < ncontrib - 1 ? ld_pair(&a.ppair[(size_t)(t + (k0 + k) * a.q) * a.tw + j])
-                                              : (uint64_t)seq;
-            for (uint32_t it = 0;; ++it) {
-                bool ready = true;
-#pragma unroll
-                for (int k = 0; k < kB; ++k) ready &= pair_seq(pp[k]) == seq;
-                if (ready) break;
-                if (it >= kSpinLimit) {
-                    err |= kErrSpin;
-                    break;
+                for (int k = 0; k < kB; ++k) {
+                    const int kk = k0 + k * G;
+                    pp[k] = kk < ncontrib - 1 ? ld_pair(&a.ppair[(size_t)(t + kk * a.q) * a.tw + j]) : (uint64_t)seq;
                 }
-                __builtin_amdgcn_s_sleep(1);
+                for (uint32_t it = 0;; ++it) {
+                    bool ready = true;
+#pragma unroll
+                    for (int k = 0; k < kB; ++k) ready &= pair_seq(pp[k]) == seq;
+                    if (ready) break;
+                    if (it >= kSpinLimit) {
+                        err |= kErrSpin;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(4);
+#pragma unroll
+                    for (int k = 0; k < kB; ++k)
+                        if (pair_seq(pp[k]) != seq)
+                            pp[k] = ld_pair(&a.ppair[(size_t)(t + (k0 + k * G) * a.q) * a.tw + j]);
+                }
 #pragma unroll
                 for (int k = 0; k < kB; ++k)
-                    if (pair_seq(pp[k]) != seq)
-                        pp[k] = ld_pair(&a.ppair[(size_t)(t + (k0 + k) * a.q) * a.tw + j]);
+                    if (k0 + k * G < ncontrib - 1) gs += pair_val(pp[k]);
             }
-#pragma unroll
-            for (int k = 0; k < kB; ++k)
-                if (k0 + k < ncontrib - 1) y += pair_val(pp[k]);
         }
-        a.y[col0 + j] = y + s;
+        s_red2[g * a.tw + j] = gs;
+        __syncthreads();
+        if (tid < tcols) {
+            float yv = 0.f;
+            for (int gg = 0; gg < G; ++gg) yv += s_red2[gg * a.tw + tid];
+            a.y[col0 + tid] = yv + own;
+        }
     }
+    if (n_dev != n) err |= kErrCount;
     if (err) atomicOr(&a.counts[3], err);
 }
 
 template <int NT, int JX, bool G>
 hipError_t launch_t(const FfnArgs& a, const FfnShape& sh, hipStream_t s) {
-    constexpr int SB = (JX <= 2) ? 6 : 4;
-    hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, 12>), dim3(sh.nwg), dim3(NT), 0, s, a);
+    // Slots per row lane per phase-1 batch and down rows per lane per phase-2 batch,
+    // sized so that about five slots per workgroup take one batch each.
+    constexpr int SB = 4;
+    constexpr int U2 = NT >= 1024 ? 4 : (NT >= 512 ? 6 : 12);
+    hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2>), dim3(sh.nwg), dim3(NT), 0, s, a);
     return hipGetLastError();
 }
 
 template <int NT, bool G>
 hipError_t launch_jx(const FfnArgs& a, const FfnShape& sh, hipStream_t s) {
-    switch (sh.jx) {
-        case 1: return launch_t<NT, 1, G>(a, sh, s);
-        case 2: return launch_t<NT, 2, G>(a, sh, s);
-        case 3: return launch_t<NT, 3, G>(a, sh, s);
-        case 4: return launch_t<NT, 4, G>(a, sh, s);
-        default: return hipErrorInvalidValue;
+    if (sh.jx == 1) return launch_t<NT, 1, G>(a, sh, s);
+    if constexpr (NT < 1024) {  // 1024-thread workgroups hold one x chunk per lane
+        switch (sh.jx) {
+            case 2: return launch_t<NT, 2, G>(a, sh, s);
+            case 3: return launch_t<NT, 3, G>(a, sh, s);
+            case 4: return launch_t<NT, 4, G>(a, sh, s);
+            default: break;
+        }
     }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -348,6 +448,7 @@ hipError_t launch_jx(const FfnArgs& a, const FfnShape& sh, hipStream_t s) {
 hipError_t launch_sparse_ffn(const FfnArgs& a, const FfnShape& sh, bool gated, hipStream_t s) {
     if (sh.nt == 256) return gated ? launch_jx<256, true>(a, sh, s) : launch_jx<256, false>(a, sh, s);
     if (sh.nt == 512) return gated ? launch_jx<512, true>(a, sh, s) : launch_jx<512, false>(a, sh, s);
+    if (sh.nt == 1024) return gated ? launch_jx<1024, true>(a, sh, s) : launch_jx<1024, false>(a, sh, s);
     return hipErrorInvalidValue;
 }
 

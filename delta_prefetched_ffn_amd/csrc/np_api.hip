@@ -57,7 +57,7 @@ struct DeviceGuard {
 
 enum LayerState { kFresh = 0, kAssigned = 1, kScattered = 2 };
 
-constexpr int kDefaultSlotsPerWg = 5;
+constexpr int kDefaultSlotsPerWg = 0;  // 0: one workgroup per compute unit
 constexpr int kDefaultTileCols = 256;
 
 }  // namespace
@@ -89,6 +89,8 @@ struct np_layer {
 
     int spw = kDefaultSlotsPerWg;
     int tw = kDefaultTileCols;
+    int nt = 0;  // threads per FFN workgroup; 0 = by d_model
+    int cus = 256;  // compute units of the device
     size_t ppair_words = 0;
 
     int32_t* d_in() const { return lists; }
@@ -106,24 +108,33 @@ int pow2_floor(int v) {
     return p;
 }
 
-int ffn_threads(int d) {
+// 1024 threads (a whole compute unit) when x fits one 16-byte chunk per lane, else 512.
+int default_threads(int d) {
     const int cpr = d / 8;
-    return (cpr + 255) / 256 <= 2 ? 256 : 512;
+    if (cpr < 256) return 256;
+    return cpr <= 512 ? 1024 : 512;
 }
+
 
 int q_of(const np_layer* L) { return (L->desc.d_model + L->tw - 1) / L->tw; }
 
 // FFN launch shape for n active slots.
 bool ffn_shape(const np_layer* L, int n, FfnShape* sh) {
     const int d = L->desc.d_model;
-    sh->nt = ffn_threads(d);
+    sh->nt = L->nt ? L->nt : default_threads(d);
     const int cpr = d / 8;
     const int cl = std::min(sh->nt, pow2_floor(cpr));
     sh->jx = (cpr + cl - 1) / cl;
     sh->tw = L->tw;
     sh->q = q_of(L);
     const int win = ffn_win_max();
-    int p1 = std::max(1, (n + L->spw - 1) / L->spw);
+    int p1;
+    if (L->spw > 0) {
+        p1 = std::max(1, (n + L->spw - 1) / L->spw);
+    } else {
+        // One workgroup per compute unit, so the whole grid is resident at once.
+        p1 = std::max(1, L->cus - sh->q + 1);
+    }
     const int per_chunk_max = win / sh->q;  // slots per chunk the window can hold
     if (per_chunk_max < 1) return false;
     p1 = std::max(p1, (n + per_chunk_max - 1) / per_chunk_max);
@@ -132,7 +143,8 @@ bool ffn_shape(const np_layer* L, int n, FfnShape* sh) {
     sh->p1 = p1;
     sh->nwg = p1 + sh->q - 1;
     sh->win_max = win;
-    return sh->jx <= 4;
+    // 1024-thread workgroups keep x for one 16-byte chunk per lane in registers
+    return sh->jx <= (sh->nt == 1024 ? 1 : 4) && sh->tw <= sh->nt;
 }
 
 np_status alloc_ffn_scratch(np_layer* L) {
@@ -232,6 +244,8 @@ np_status enqueue_ffn(np_layer* L, const float* x, float* y, hipStream_t s) {
     a.ppair = L->ppair;
     if (++L->ffn_seq == 0) L->ffn_seq = 1;  // 0 marks never-written words
     a.seq = L->ffn_seq;
+    a.n = L->n_active;
+    a.buf_bytes = (uint32_t)((size_t)L->desc.k_max * L->bundle_elems() * 2);
     a.d = L->desc.d_model;
     a.K = L->desc.k_max;
     a.R = L->desc.n_rows;
@@ -278,6 +292,8 @@ np_status np_layer_create(const np_layer_desc* desc, np_layer** out) {
         return fail(NP_EINVAL, "unknown mask_mode %d", D.mask_mode);
     if (D.act != NP_ACT_RELU) return fail(NP_EINVAL, "unsupported activation %d", D.act);
     if (!D.masks || !D.row_store) return fail(NP_EINVAL, "masks and row_store must not be NULL");
+    if ((uint64_t)D.k_max * D.n_rows * D.d_model * 2 > kMaxBufBytes)
+        return fail(NP_EINVAL, "slot buffer k_max * n_rows * d_model * 2 bytes must stay below 4 GiB");
     if (!aligned16(D.row_store)) return fail(NP_EINVAL, "row_store must be 16-byte aligned");
     int ndev = 0;
     NP_HIP(hipGetDeviceCount(&ndev));
@@ -336,6 +352,13 @@ np_status np_layer_create(const np_layer_desc* desc, np_layer** out) {
     }
 
     const int K = D.k_max, M = D.d_ff;
+    {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, D.device) == hipSuccess && cus > 0)
+            L->cus = cus;
+        else
+            (void)hipGetLastError();
+    }
     auto dmalloc = [&](void** p, size_t bytes) -> bool {
         if (hipMalloc(p, bytes) != hipSuccess) {
             (void)hipGetLastError();
@@ -410,31 +433,36 @@ np_status np_layer_reset(np_layer* L) {
     return init_state(L);
 }
 
-np_status np_layer_set_ffn_shape(np_layer* L, int32_t slots_per_wg, int32_t tile_cols) {
+np_status np_layer_set_ffn_shape(np_layer* L, int32_t slots_per_wg, int32_t tile_cols, int32_t threads) {
     if (!L) return fail(NP_EINVAL, "layer must not be NULL");
-    if (slots_per_wg && (slots_per_wg < 1 || slots_per_wg > 16))
-        return fail(NP_EINVAL, "slots_per_wg=%d must be in [1, 16]", slots_per_wg);
+    if (slots_per_wg && slots_per_wg != -1 && (slots_per_wg < 1 || slots_per_wg > 16))
+        return fail(NP_EINVAL, "slots_per_wg=%d must be -1 or in [1, 16]", slots_per_wg);
     if (tile_cols) {
         const int ct = tile_cols / 8;
-        if (tile_cols % 8 || tile_cols < 64 || tile_cols > 1024 || (ct & (ct - 1)) ||
-            ct > ffn_threads(L->desc.d_model))
+        if (tile_cols % 8 || tile_cols < 64 || tile_cols > 1024 || (ct & (ct - 1)))
             return fail(NP_EINVAL, "tile_cols=%d must be 8 * (power of two), 64..1024", tile_cols);
     }
+    if (threads && threads != 256 && threads != 512 && threads != 1024)
+        return fail(NP_EINVAL, "threads=%d must be 256, 512 or 1024", threads);
     DeviceGuard g(L->desc.device);
     NP_HIP(hipDeviceSynchronize());
-    const int old_spw = L->spw, old_tw = L->tw;
-    if (slots_per_wg) L->spw = slots_per_wg;
+    const int old_spw = L->spw, old_tw = L->tw, old_nt = L->nt;
+    if (slots_per_wg) L->spw = slots_per_wg < 0 ? 0 : slots_per_wg;
     if (tile_cols) L->tw = tile_cols;
+    if (threads) L->nt = threads;
     FfnShape sh;
     if (!ffn_shape(L, L->desc.k_max, &sh)) {
         L->spw = old_spw;
         L->tw = old_tw;
-        return fail(NP_EINVAL, "shape (%d, %d) cannot cover k_max=%d", slots_per_wg, tile_cols, L->desc.k_max);
+        L->nt = old_nt;
+        return fail(NP_EINVAL, "shape (%d, %d, %d) cannot cover k_max=%d", slots_per_wg, tile_cols, threads,
+                    L->desc.k_max);
     }
     np_status st = alloc_ffn_scratch(L);
     if (st != NP_OK) {
         L->spw = old_spw;
         L->tw = old_tw;
+        L->nt = old_nt;
     }
     return st;
 }

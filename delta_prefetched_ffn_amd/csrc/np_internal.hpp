@@ -14,12 +14,14 @@ constexpr int kMaxCentroids = 65536;
 constexpr int kMaxWords = kMaxDff / 64;  // mask words per set
 constexpr int kMaxKWords = kMaxKmax / 64;
 constexpr int kMaxLayersPerLaunch = 64;
+constexpr uint64_t kMaxBufBytes = (1ull << 32) - 4096;  // slot buffer addressed by 32-bit offsets
 
 // Device error bits (counts[3]).
 constexpr int kErrFreeExhausted = 1;   // delta assign: no free slot for an incoming neuron
 constexpr int kErrBadList = 2;         // scatter/FFN: a list entry out of range
 constexpr int kErrWindow = 4;          // FFN: window larger than the LDS staging
 constexpr int kErrSpin = 8;            // FFN: a wait hit its iteration limit
+constexpr int kErrCount = 16;          // FFN: host and device active counts differ
 
 // Everything a kernel needs about one layer; lives in device memory.
 struct LayerDev {
@@ -63,6 +65,8 @@ struct FfnArgs {
     uint64_t* hpair;        // [K] (launch sequence, h) words
     uint64_t* ppair;        // [nwg][tw] (launch sequence, partial sum) words
     uint32_t seq;           // this launch's sequence number (never 0)
+    int32_t n;              // active slots (host-known), or -1 to read counts[2]
+    uint32_t buf_bytes;     // size of buf (below 4 GiB)
     int32_t d, K, R;
     int32_t p1, q, tw, nwg;
 };

@@ -41,7 +41,8 @@
  *
  * Limits checked at np_layer_create: d_model % 8 == 0 (128-bit rows),
  * 8 <= d_model <= 16384, 1 <= d_ff <= 65536, 1 <= k_max <= min(d_ff, 65536),
- * n_rows in {2, 3}, 1 <= n_centroids <= 65536.
+ * n_rows in {2, 3}, 1 <= n_centroids <= 65536, and the slot buffer
+ * (k_max * n_rows * d_model * 2 bytes) below 4 GiB.
  */
 #ifndef NP_H
 #define NP_H
@@ -166,12 +167,16 @@ np_status np_layer_info(const np_layer* layer, int32_t* out6);
 np_status np_layer_counters(const np_layer* layer, int64_t* out2);
 
 /* FFN launch shape of this layer: about slots_per_wg active slots per
- * workgroup for the gate/up phase (1..16, default 5) and tile_cols output
- * columns per workgroup for the down phase (multiple of 8, 64..1024,
- * default 256). 0 keeps the current value. Changes speed, not results'
- * validity (the summation order depends on the shape, so bit patterns of y
- * may change within fp32 rounding). */
-np_status np_layer_set_ffn_shape(np_layer* layer, int32_t slots_per_wg, int32_t tile_cols);
+ * workgroup for the gate/up phase (1..16; the default, -1, sizes the grid to
+ * one workgroup per compute unit), tile_cols output
+ * columns per workgroup for the down phase (8 * a power of two, 64..1024,
+ * default 256) and threads per workgroup (256, 512 or 1024; default by
+ * d_model; tile_cols must not exceed threads). 0 keeps the current value;
+ * slots_per_wg = -1 restores the per-compute-unit default.
+ * Synchronizes the device. The shape
+ * changes speed and the fp32 summation order, not what is computed.
+ * NP_EINVAL if the shape cannot cover k_max active slots. */
+np_status np_layer_set_ffn_shape(np_layer* layer, int32_t slots_per_wg, int32_t tile_cols, int32_t threads);
 
 /* Thread-local text of the calling thread's last error ("" if none). */
 const char* np_last_error(void);

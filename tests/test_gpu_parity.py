@@ -201,3 +201,48 @@ def test_edge_cases_empty_full_turnover_and_exact_capacity(torch):
             assert (yh == 0).all()
         check_y(yh, O.sparse_ffn(store, R, d, S, x_np), f"step {i}")
     layer.close()
+
+
+@pytest.mark.parametrize("shape", [(3, 128, 256), (5, 256, 512), (5, 256, 1024), (2, 64, 1024), (8, 128, 512),
+                                   (16, 256, 256), (1, 256, 256)])
+def test_ffn_launch_shapes(torch, shape):
+    """Every launch shape gives the oracle's y (tolerance) and exact results on dyadic inputs."""
+    from delta_prefetched_ffn_amd import binding as B
+    spw, tw, nt = shape
+    cfg = small_config(970, L=1, d=4096, M=2000, K=900, C=4, mode="union", m=300, swap=40, T=3)
+    wl = Workload(cfg)
+    layer, store = make_layer(wl, 0)
+    layer.set_ffn_shape(spw, tw, nt)
+    orc = OracleRun(wl, keep_buffer=False)
+    x_all = wl.x_all()
+    x = torch.from_numpy(x_all).cuda()
+    y = torch.zeros_like(x)
+    s = _stream(torch)
+    for t in range(cfg.T):
+        g, u = (int(v) for v in wl.cids()[t, 0])
+        layer.delta_assign(g, u, s)
+        layer.scatter_rows(s)
+        layer.sparse_ffn(x[t, 0].data_ptr(), y[t, 0].data_ptr(), s)
+        assert layer.read_state()["err"] == 0
+        S = orc.active(t, 0)
+        check_y(y[t, 0].cpu().numpy(), O.sparse_ffn(store, cfg.R, cfg.d, S, x_all[t, 0]), f"{shape} t={t}")
+    layer.close()
+    # exact arithmetic in the same shape
+    rng = np.random.default_rng(77)
+    dstore = _dyadic_store(rng, 512, 3, 4096)
+    dcfg = Config(980, "dyadic", L=1, d=4096, M=512, R=3, K=256, C=4, mode="union", T=2, m=100, swap=10)
+    dwl = Workload(dcfg)
+    dl, _ = make_layer(dwl, 0, store=dstore)
+    dl.set_ffn_shape(spw, tw, nt)
+    dorc = OracleRun(dwl, keep_buffer=False)
+    for t in range(dcfg.T):
+        x_np = (rng.integers(-8, 9, size=4096) / 8.0).astype(np.float32)
+        xd = torch.from_numpy(x_np).cuda()
+        yd = torch.empty_like(xd)
+        g, u = (int(v) for v in dwl.cids()[t, 0])
+        dl.delta_assign(g, u, s)
+        dl.scatter_rows(s)
+        dl.sparse_ffn(xd.data_ptr(), yd.data_ptr(), s)
+        ref = O.sparse_ffn(dstore, 3, 4096, dorc.active(t, 0), x_np)
+        assert np.array_equal(yd.cpu().numpy().astype(np.float64), ref), f"{shape} t={t}"
+    dl.close()

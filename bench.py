@@ -93,8 +93,9 @@ def cpu_baseline(wl, stores, seconds: float):
         list(ex.map(lambda l: one(0, l), range(c.L)))       # cold start, untimed
         t0 = time.perf_counter()
         tok, act, din = 0, 0, 0
-        while tok < c.T - 1:
-            for a, b in ex.map(lambda l: one(1 + tok, l), range(c.L)):
+        while True:  # tokens 1, 2, ..., T-1, 1, 2, ... until the time budget is spent
+            t = 1 + tok % (c.T - 1)
+            for a, b in ex.map(lambda l: one(t, l), range(c.L)):
                 act += a
                 din += b
             tok += 1
@@ -103,8 +104,8 @@ def cpu_baseline(wl, stores, seconds: float):
         dt = time.perf_counter() - t0
     eff = (act + din) * c.bundle_bytes
     return {"value": tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"tokens 1..{tok} of the same workload (all {c.L} layers, after an untimed cold "
-                      f"start), fp64 oracle, layers in parallel threads",
+            "sample": f"{tok} tokens of the same workload (tokens 1..{c.T - 1} in order, repeating; all "
+                      f"{c.L} layers; after an untimed cold start), fp64 oracle, layers in parallel threads",
             "effective_gbps": eff / dt / 1e9, "seconds": dt}
 
 
@@ -227,7 +228,18 @@ def main():
     e1.record(s)
     s.synchronize()
     probe_gbps = 5 * probe_bytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del buf
+    # plain 128-bit copy of a known size: the reference that scales the HBM byte counters
+    copy_bytes = 256 << 20
+    cdst = torch.empty(copy_bytes // 2, dtype=torch.int16, device="cuda")
+    B.probe_copy(cdst.data_ptr(), buf.data_ptr(), copy_bytes, s.cuda_stream)
+    e0.record(s)
+    for _ in range(3):
+        B.probe_copy(cdst.data_ptr(), buf.data_ptr(), copy_bytes, s.cuda_stream)
+    e1.record(s)
+    s.synchronize()
+    copy_gbps = 3 * 2 * copy_bytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    log(f"copy probe: {copy_gbps:.0f} GB/s (read + write)")
+    del buf, cdst
     log(f"streaming-read probe: {probe_gbps:.0f} GB/s")
     for L in layers:
         L.close()
@@ -293,6 +305,7 @@ def main():
                      "timing": "HIP events on the launch stream around back-to-back launches of the 31 layers",
                      "traffic_note": traffic_note},
         "hbm_read_probe_gbps": probe_gbps,
+        "hbm_copy_probe_gbps": copy_gbps,
         "pcie_inclusive": pcie,
         "cpu_baseline": cpu,
     }

@@ -169,6 +169,7 @@ def main():
     torch.cuda.synchronize()
     ts = time.perf_counter()
     run_tokens(layers, toks)
+    enqueued = time.perf_counter() - ts
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - ts
     after = np.array([L.counters() for L in layers], dtype=np.int64).sum(axis=0)
@@ -177,7 +178,8 @@ def main():
     tok_s = args.steps / elapsed
     eff_bytes = (act_bundles + in_bundles) * c.bundle_bytes
     eff_gbps = eff_bytes / elapsed / 1e9
-    log(f"decode: {ms_per_step:.3f} ms/token, {tok_s:.1f} tok/s, effective {eff_gbps:.1f} GB/s")
+    log(f"decode: {ms_per_step:.3f} ms/token, {tok_s:.1f} tok/s, effective {eff_gbps:.1f} GB/s "
+        f"(host enqueue {enqueued * 1e3 / args.steps:.3f} ms/token)")
 
     # ---------------- FFN kernel timing (roofline of the dominant kernel) ----------------
     ffn_toks = token_ids(1 + args.warmup + args.steps, args.ffn_steps, c.T)
@@ -298,6 +300,7 @@ def main():
         "mean_active_per_layer": act_bundles / (args.steps * c.L),
         "mean_delta_per_layer": in_bundles / (args.steps * c.L),
         "cold_start_ms": cold_ms,
+        "host_enqueue_ms_per_step": enqueued * 1e3 / args.steps,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": "k_sparse_ffn", "bytes_per_launch": ffn_bytes_per_launch,

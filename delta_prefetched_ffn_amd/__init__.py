@@ -6,4 +6,4 @@ The compute path is the HIP library libnp.so (C ABI in include/np.h);
 """
 from . import binding  # noqa: F401
 from .binding import (MASK_INTERSECT, MASK_SINGLE, MASK_UNION, MODES, Layer, NPError,  # noqa: F401
-                      decode_step, lib, probe_copy, probe_read)
+                      decode_step, decode_use_graphs, lib, probe_copy, probe_read)

@@ -29,7 +29,7 @@ _NAMES = {0: "NP_OK", 1: "NP_EINVAL", 2: "NP_ECAPACITY", 3: "NP_ENOMEM", 4: "NP_
 EXPORTS = ["np_layer_create", "np_layer_destroy", "np_layer_reset", "np_delta_assign",
            "np_scatter_rows", "np_sparse_ffn", "np_decode_step", "np_layer_read_state",
            "np_layer_read_rows", "np_layer_info", "np_layer_counters", "np_layer_set_ffn_shape", "np_last_error",
-           "np_probe_read", "np_probe_copy"]
+           "np_probe_read", "np_probe_copy", "np_decode_use_graphs"]
 
 
 class NPError(RuntimeError):
@@ -67,6 +67,7 @@ def lib() -> ctypes.CDLL:
         "np_layer_set_ffn_shape": [vp, i32, i32, i32],
         "np_probe_read": [vp, i64, vp, vp],
         "np_probe_copy": [vp, vp, i64, vp],
+        "np_decode_use_graphs": [i32],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -180,6 +181,11 @@ def decode_step(layers, cids: np.ndarray, x_ptr: int, y_ptr: int, compute_stream
     cs = compute_stream or None
     ps = cs if copy_stream is None else (copy_stream or None)
     _check(lib().np_decode_step(handles, len(layers), cids.ctypes.data, x_ptr, y_ptr, cs, ps))
+
+
+def decode_use_graphs(enable: bool) -> None:
+    """np_decode_use_graphs: replay decode steps as captured HIP graphs (default) or launch one by one."""
+    _check(lib().np_decode_use_graphs(1 if enable else 0))
 
 
 def probe_read(src_ptr: int, nbytes: int, sink_ptr: int, stream: int = 0) -> None:

@@ -60,10 +60,12 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
     const LayerDev L = *a.layers[blockIdx.x];
     const int tid = threadIdx.x;
     if (tid == 0) s_err = 0;
+    const int32_t cg = a.prm ? a.prm->cid[a.layer0 + blockIdx.x][0] : a.cid[blockIdx.x][0];
+    const int32_t cu = a.prm ? a.prm->cid[a.layer0 + blockIdx.x][1] : a.cid[blockIdx.x][1];
 
     // Step 1: active set S from the selected gate/up masks; R from the resident bits.
-    const uint64_t* ma = L.masks + (size_t)a.cid[blockIdx.x][0] * L.W;
-    const uint64_t* mb = L.masks + ((size_t)(L.n_tables - 1) * L.C + a.cid[blockIdx.x][1]) * L.W;
+    const uint64_t* ma = L.masks + (size_t)cg * L.W;
+    const uint64_t* mb = L.masks + ((size_t)(L.n_tables - 1) * L.C + cu) * L.W;
     for (int w = tid; w < L.W; w += kNT) {
         const uint64_t ga = ma[w], gb = mb[w];
         s_S[w] = L.mode == 0 ? (ga | gb) : L.mode == 1 ? (ga & gb) : ga;
@@ -176,7 +178,24 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
     }
 }
 
+__global__ void k_set_params(ParamsUpdate p, DecodeParams* dst) {
+    for (int i = threadIdx.x; i < p.count; i += blockDim.x) {
+        dst->cid[p.first + i][0] = p.cid[i][0];
+        dst->cid[p.first + i][1] = p.cid[i][1];
+        dst->seq[p.first + i] = p.seq[i];
+    }
+    if (threadIdx.x == 0 && p.first == 0) {
+        dst->x = p.x;
+        dst->y = p.y;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_set_params(const ParamsUpdate& p, DecodeParams* dst, hipStream_t s) {
+    hipLaunchKernelGGL(k_set_params, dim3(1), dim3(128), 0, s, p, dst);
+    return hipGetLastError();
+}
 
 hipError_t launch_delta_assign(const DeltaLaunch& a, hipStream_t s) {
     hipLaunchKernelGGL(k_delta_assign, dim3(a.n_layers), dim3(kNT), 0, s, a);

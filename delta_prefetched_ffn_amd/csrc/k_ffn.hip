@@ -122,7 +122,9 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
 
     const int w = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int d = a.d, cpr = d >> 3;
-    const uint32_t seq = a.seq;
+    // In a replayed decode step the per-token values come from the parameter block.
+    const uint32_t seq = a.prm ? a.prm->seq[a.layer] : a.seq;
+    const float* xg = a.prm ? a.prm->x + (size_t)a.layer * a.d : a.x;
 
     // Phase-1 lane geometry: CL lanes share a row (power of two), RL row lanes.
     int CL = NT;
@@ -136,8 +138,8 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     for (int j = 0; j < JX; ++j) {
         const int c = cl + CL * j;
         if (w < a.p1 && c < cpr) {
-            const float4 p = reinterpret_cast<const float4*>(a.x)[2 * c];
-            const float4 q = reinterpret_cast<const float4*>(a.x)[2 * c + 1];
+            const float4 p = reinterpret_cast<const float4*>(xg)[2 * c];
+            const float4 q = reinterpret_cast<const float4*>(xg)[2 * c + 1];
             xv[j][0] = p.x; xv[j][1] = p.y; xv[j][2] = p.z; xv[j][3] = p.w;
             xv[j][4] = q.x; xv[j][5] = q.y; xv[j][6] = q.z; xv[j][7] = q.w;
         } else {
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     // |S| comes from the host (it validated the capacity with it); the device count,
     // read in parallel, is only checked against it.
     const int n_dev = a.counts[2];
-    int n = a.n < 0 ? n_dev : a.n;
+    int n = (a.n < 0 || a.prm) ? n_dev : a.n;
     n = n < 0 ? 0 : (n > a.K ? a.K : n);
     auto cbeg = [&](int c) { return (int)(((long long)c * n) / a.p1); };
 
@@ -412,10 +414,11 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
         if (tid < tcols) {
             float yv = 0.f;
             for (int gg = 0; gg < G; ++gg) yv += s_red2[gg * a.tw + tid];
-            a.y[col0 + tid] = yv + own;
+            float* yg = a.prm ? a.prm->y + (size_t)a.layer * a.d : a.y;
+            yg[col0 + tid] = yv + own;
         }
     }
-    if (n_dev != n) err |= kErrCount;
+    if (!a.prm && n_dev != n) err |= kErrCount;
     if (err) atomicOr(&a.counts[3], err);
 }
 

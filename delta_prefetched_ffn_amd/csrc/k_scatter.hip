@@ -21,9 +21,38 @@ __global__ __launch_bounds__(kNT) void k_scatter_rows(int32_t* counts, const int
                                                       const uint4* __restrict__ store,
                                                       uint4* __restrict__ buf, int32_t M, int32_t K,
                                                       int32_t cb) {
-    const int n_in = counts[0];
+    const int n_in = min(counts[0], K);  // the lists hold at most K entries
     for (int i = blockIdx.x; i < n_in; i += gridDim.x) {
         const int n = d_in[i], s = slot_in[i];
+        if ((unsigned)n >= (unsigned)M || (unsigned)s >= (unsigned)K) {
+            if (threadIdx.x == 0) atomicOr(&counts[3], kErrBadList);
+            continue;
+        }
+        const uint4* src = store + (size_t)n * cb;
+        uint4* dst = buf + (size_t)s * cb;
+        for (int c = threadIdx.x; c < cb; c += kNT * kU) {
+            uint4 v[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                if (c + u * kNT < cb) v[u] = src[c + u * kNT];
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                if (c + u * kNT < cb) dst[c + u * kNT] = v[u];
+        }
+    }
+}
+
+// All layers of a decode step at once: blockIdx.y picks the layer, blockIdx.x strides over
+// that layer's incoming bundles.
+__global__ __launch_bounds__(kNT) void k_scatter_all(ScatterLaunch a) {
+    const LayerDev* L = a.layers[blockIdx.y];
+    int32_t* counts = L->counts;
+    const int M = L->M, K = L->K, cb = L->bundle16;
+    const int n_in = min(counts[0], K);  // the lists hold at most K entries
+    const uint4* store = reinterpret_cast<const uint4*>(L->store);
+    uint4* buf = reinterpret_cast<uint4*>(L->buf);
+    for (int i = blockIdx.x; i < n_in; i += gridDim.x) {
+        const int n = L->d_in[i], s = L->slot_in[i];
         if ((unsigned)n >= (unsigned)M || (unsigned)s >= (unsigned)K) {
             if (threadIdx.x == 0) atomicOr(&counts[3], kErrBadList);
             continue;
@@ -74,6 +103,11 @@ hipError_t launch_scatter(int32_t* counts, const int32_t* d_in, const int32_t* s
     hipLaunchKernelGGL(k_scatter_rows, dim3(grid), dim3(kNT), 0, s, counts, d_in, slot_in,
                        reinterpret_cast<const uint4*>(store), reinterpret_cast<uint4*>(buf), M, K,
                        bundle_elems / 8);
+    return hipGetLastError();
+}
+
+hipError_t launch_scatter_all(const ScatterLaunch& a, int wgs_per_layer, hipStream_t s) {
+    hipLaunchKernelGGL(k_scatter_all, dim3(wgs_per_layer, a.n_layers), dim3(kNT), 0, s, a);
     return hipGetLastError();
 }
 

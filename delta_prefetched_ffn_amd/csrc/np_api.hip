@@ -8,7 +8,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <atomic>
 #include <map>
+#include <memory>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -84,6 +87,7 @@ struct np_layer {
     uint64_t* hpair = nullptr;
     uint64_t* ppair = nullptr;
     uint32_t ffn_seq = 0;
+    uint64_t version = 0;  // bumped when cached decode graphs must be rebuilt
     LayerDev* ldev = nullptr;
     hipEvent_t ev_scatter = nullptr;
 
@@ -119,7 +123,9 @@ int default_threads(int d) {
 int q_of(const np_layer* L) { return (L->desc.d_model + L->tw - 1) / L->tw; }
 
 // FFN launch shape for n active slots.
-bool ffn_shape(const np_layer* L, int n, FfnShape* sh) {
+// fixed = true: a shape that serves every |S| <= k_max (captured decode graphs).
+bool ffn_shape(const np_layer* L, int n, FfnShape* sh, bool fixed = false) {
+    if (fixed) n = L->desc.k_max;
     const int d = L->desc.d_model;
     sh->nt = L->nt ? L->nt : default_threads(d);
     const int cpr = d / 8;
@@ -139,7 +145,7 @@ bool ffn_shape(const np_layer* L, int n, FfnShape* sh) {
     if (per_chunk_max < 1) return false;
     p1 = std::max(p1, (n + per_chunk_max - 1) / per_chunk_max);
     if (p1 > kP1Cap) return false;
-    p1 = std::min(p1, std::max(1, n));
+    if (!fixed) p1 = std::min(p1, std::max(1, n));
     sh->p1 = p1;
     sh->nwg = p1 + sh->q - 1;
     sh->win_max = win;
@@ -229,12 +235,14 @@ np_status check_cids(const np_layer* L, int32_t g, int32_t u, int32_t* eff_u) {
 
 int scatter_grid(int n_in) { return std::max(1, std::min(n_in, 4096)); }
 
-np_status enqueue_ffn(np_layer* L, const float* x, float* y, hipStream_t s) {
-    FfnShape sh;
-    if (!ffn_shape(L, L->n_active, &sh))
+// prm != nullptr: a launch captured into a decode graph (per-token values from prm).
+np_status enqueue_ffn(np_layer* L, const float* x, float* y, hipStream_t s, const DecodeParams* prm = nullptr,
+                      int layer = 0) {
+    FfnShape sh{};
+    if (!ffn_shape(L, L->n_active, &sh, prm != nullptr))
         return fail(NP_EINVAL, "no FFN launch shape for d_model=%d n=%d tile=%d", L->desc.d_model,
                     L->n_active, L->tw);
-    FfnArgs a;
+    FfnArgs a{};
     a.buf = L->buf;
     a.act = L->act();
     a.counts = L->counts;
@@ -242,9 +250,16 @@ np_status enqueue_ffn(np_layer* L, const float* x, float* y, hipStream_t s) {
     a.y = y;
     a.hpair = L->hpair;
     a.ppair = L->ppair;
-    if (++L->ffn_seq == 0) L->ffn_seq = 1;  // 0 marks never-written words
-    a.seq = L->ffn_seq;
-    a.n = L->n_active;
+    a.prm = prm;
+    a.layer = layer;
+    if (prm) {
+        a.seq = 0;
+        a.n = -1;
+    } else {
+        if (++L->ffn_seq == 0) L->ffn_seq = 1;  // 0 marks never-written words
+        a.seq = L->ffn_seq;
+        a.n = L->n_active;
+    }
     a.buf_bytes = (uint32_t)((size_t)L->desc.k_max * L->bundle_elems() * 2);
     a.d = L->desc.d_model;
     a.K = L->desc.k_max;
@@ -257,17 +272,177 @@ np_status enqueue_ffn(np_layer* L, const float* x, float* y, hipStream_t s) {
     return NP_OK;
 }
 
-np_status enqueue_scatter(np_layer* L, hipStream_t s) {
+np_status enqueue_scatter(np_layer* L, hipStream_t s, bool fixed_grid = false) {
+    const int grid = fixed_grid ? std::max(1, std::min(L->desc.k_max, 1024)) : scatter_grid(L->n_in);
     NP_HIP(launch_scatter(L->counts, L->d_in(), L->slot_in(), L->store_dev, L->buf, L->desc.d_ff,
-                          L->desc.k_max, (int32_t)L->bundle_elems(), scatter_grid(L->n_in), s));
+                          L->desc.k_max, (int32_t)L->bundle_elems(), grid, s));
     return NP_OK;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-std::map<int, hipEvent_t>& assign_events() {
-    thread_local std::map<int, hipEvent_t> ev;
-    return ev;
+// A token's launches go to one queue (assign, one scatter launch for all layers, the FFNs in
+// layer order) unless some backing store is in host memory and a separate copy stream is given:
+// then layer l's scatter runs on the copy stream and layer l's FFN waits only for it, so the
+// host-link transfers of later layers overlap earlier FFNs.
+bool one_queue(np_layer* const* layers, int n, hipStream_t cs, hipStream_t ps) {
+    if (cs == ps) return true;
+    for (int l = 0; l < n; ++l)
+        if (layers[l]->store_is_host) return false;
+    return true;
+}
+
+constexpr int kScatterWgsPerLayer = 64;
+
+// One token's launches. cid: host [n][2] (gate, effective up) ids; with prm (capture into a
+// decode graph) the ids, x and y come from the parameter block instead. ev: n + 2 events, used
+// only on the two-stream path.
+np_status enqueue_token(np_layer* const* layers, int n, const int32_t* cid, const float* x, float* y,
+                        hipStream_t cs, hipStream_t ps, const DecodeParams* prm, const hipEvent_t* ev) {
+    const int d = layers[0]->desc.d_model;
+    for (int l0 = 0; l0 < n; l0 += kMaxLayersPerLaunch) {
+        DeltaLaunch a{};
+        a.n_layers = std::min(kMaxLayersPerLaunch, n - l0);
+        for (int k = 0; k < a.n_layers; ++k) {
+            a.layers[k] = layers[l0 + k]->ldev;
+            a.cid[k][0] = cid ? cid[2 * (l0 + k)] : 0;
+            a.cid[k][1] = cid ? cid[2 * (l0 + k) + 1] : 0;
+        }
+        a.prm = prm;
+        a.layer0 = l0;
+        NP_HIP(launch_delta_assign(a, cs));
+    }
+    if (one_queue(layers, n, cs, ps)) {
+        for (int l0 = 0; l0 < n; l0 += kMaxLayersPerLaunch) {
+            ScatterLaunch sa{};
+            sa.n_layers = std::min(kMaxLayersPerLaunch, n - l0);
+            for (int k = 0; k < sa.n_layers; ++k) sa.layers[k] = layers[l0 + k]->ldev;
+            NP_HIP(launch_scatter_all(sa, kScatterWgsPerLayer, cs));
+        }
+        for (int l = 0; l < n; ++l) {
+            np_status st = enqueue_ffn(layers[l], prm ? nullptr : x + (size_t)l * d, prm ? nullptr : y + (size_t)l * d,
+                                       cs, prm, l);
+            if (st != NP_OK) return st;
+        }
+        return NP_OK;
+    }
+    NP_HIP(hipEventRecord(ev[0], cs));
+    NP_HIP(hipStreamWaitEvent(ps, ev[0], 0));
+    for (int l = 0; l < n; ++l) {
+        np_status st = enqueue_scatter(layers[l], ps, prm != nullptr);
+        if (st != NP_OK) return st;
+        NP_HIP(hipEventRecord(ev[2 + l], ps));
+        NP_HIP(hipStreamWaitEvent(cs, ev[2 + l], 0));
+        st = enqueue_ffn(layers[l], prm ? nullptr : x + (size_t)l * d, prm ? nullptr : y + (size_t)l * d, cs, prm, l);
+        if (st != NP_OK) return st;
+    }
+    NP_HIP(hipEventRecord(ev[1], ps));  // join the copy stream back to the compute stream
+    NP_HIP(hipStreamWaitEvent(cs, ev[1], 0));
+    return NP_OK;
+}
+
+// Events for the two-stream path of direct launches: per thread and device, grown on demand.
+np_status step_events(int dev, int n, const hipEvent_t** out) {
+    thread_local std::map<int, std::vector<hipEvent_t>> evs;
+    auto& v = evs[dev];
+    while ((int)v.size() < n + 2) {
+        hipEvent_t e;
+        NP_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+        v.push_back(e);
+    }
+    *out = v.data();
+    return NP_OK;
+}
+
+// ---- decode graphs: one token's launches captured once per (layer set, streams), replayed
+// with the per-token values written into a device parameter block just before.
+struct DecodePlan {
+    std::vector<np_layer*> layers;
+    std::vector<uint64_t> versions;
+    hipStream_t cs = nullptr, ps = nullptr;
+    int device = 0;
+    DecodeParams* prm = nullptr;
+    hipGraphExec_t exec = nullptr;
+    std::vector<hipEvent_t> events;
+    ~DecodePlan() {
+        if (exec) (void)hipGraphExecDestroy(exec);
+        for (hipEvent_t e : events) (void)hipEventDestroy(e);
+        if (prm) (void)hipFree(prm);
+    }
+};
+
+std::mutex g_plan_mu;
+std::vector<std::unique_ptr<DecodePlan>> g_plans;  // most recently used last
+std::atomic<int> g_use_graphs{1};
+constexpr size_t kMaxPlans = 8;
+
+void drop_plans_with(const np_layer* L) {
+    std::lock_guard<std::mutex> lk(g_plan_mu);
+    for (size_t i = 0; i < g_plans.size();) {
+        auto& ls = g_plans[i]->layers;
+        if (std::find(ls.begin(), ls.end(), L) != ls.end()) g_plans.erase(g_plans.begin() + i);
+        else ++i;
+    }
+}
+
+np_status capture_plan(DecodePlan* P) {
+    const int n = (int)P->layers.size();
+    const bool two = P->cs != P->ps;
+    NP_HIP(hipMalloc(&P->prm, sizeof(DecodeParams)));
+    NP_HIP(hipMemset(P->prm, 0, sizeof(DecodeParams)));
+    const int n_ev = two ? n + 2 : 0;  // used only by the two-stream structure
+    for (int i = 0; i < n_ev; ++i) {
+        hipEvent_t e;
+        NP_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+        P->events.push_back(e);
+    }
+    NP_HIP(hipStreamBeginCapture(P->cs, hipStreamCaptureModeRelaxed));
+    const np_status st = enqueue_token(P->layers.data(), n, nullptr, nullptr, nullptr, P->cs, P->ps, P->prm,
+                                       P->events.data());
+    hipGraph_t graph = nullptr;
+    const hipError_t ee = hipStreamEndCapture(P->cs, &graph);
+    if (st != NP_OK) {  // the failing call has set the message
+        if (graph) (void)hipGraphDestroy(graph);
+        return st;
+    }
+    if (ee != hipSuccess || !graph) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return fail(NP_EHIP, "decode graph capture failed: %s", hipGetErrorString(ee));
+    }
+    const hipError_t ie = hipGraphInstantiate(&P->exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (ie != hipSuccess) {
+        P->exec = nullptr;
+        return fail(NP_EHIP, "decode graph instantiation failed: %s", hipGetErrorString(ie));
+    }
+    return NP_OK;
+}
+
+// The cached plan for these layers and streams, captured on first use.
+DecodePlan* get_plan(np_layer* const* layers, int n, hipStream_t cs, hipStream_t ps, int dev, np_status* st) {
+    std::lock_guard<std::mutex> lk(g_plan_mu);
+    for (size_t i = 0; i < g_plans.size(); ++i) {
+        DecodePlan* P = g_plans[i].get();
+        if ((int)P->layers.size() != n || P->cs != cs || P->ps != ps) continue;
+        bool same = true;
+        for (int l = 0; l < n && same; ++l) same = P->layers[l] == layers[l] && P->versions[l] == layers[l]->version;
+        if (!same) continue;
+        auto keep = std::move(g_plans[i]);
+        g_plans.erase(g_plans.begin() + i);
+        g_plans.push_back(std::move(keep));
+        return g_plans.back().get();
+    }
+    auto P = std::make_unique<DecodePlan>();
+    P->layers.assign(layers, layers + n);
+    for (int l = 0; l < n; ++l) P->versions.push_back(layers[l]->version);
+    P->cs = cs;
+    P->ps = ps;
+    P->device = dev;
+    *st = capture_plan(P.get());
+    if (*st != NP_OK) return nullptr;
+    if (g_plans.size() >= kMaxPlans) g_plans.erase(g_plans.begin());
+    g_plans.push_back(std::move(P));
+    return g_plans.back().get();
 }
 
 }  // namespace
@@ -382,7 +557,7 @@ np_status np_layer_create(const np_layer_desc* desc, np_layer** out) {
         free_layer(L);
         return st;
     }
-    LayerDev ld;
+    LayerDev ld{};
     ld.masks = L->d_masks;
     ld.res = L->res;
     ld.freeb = L->freeb;
@@ -401,6 +576,10 @@ np_status np_layer_create(const np_layer_desc* desc, np_layer** out) {
     ld.n_tables = L->n_tables;
     ld.C = D.n_centroids;
     ld.pad = 0;
+    ld.store = L->store_dev;
+    ld.buf = L->buf;
+    ld.bundle16 = (int32_t)(L->bundle_elems() / 8);
+    ld.pad2 = 0;
     hipError_t e = hipMemcpy(L->ldev, &ld, sizeof ld, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy(L->d_masks, L->h_masks.data(), mask_words * 8, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemset(L->hpair, 0, (size_t)K * 8);
@@ -422,6 +601,7 @@ np_status np_layer_destroy(np_layer* L) {
     if (!L) return fail(NP_EINVAL, "layer must not be NULL");
     DeviceGuard g(L->desc.device);
     (void)hipDeviceSynchronize();
+    drop_plans_with(L);
     free_layer(L);
     return NP_OK;
 }
@@ -430,6 +610,7 @@ np_status np_layer_reset(np_layer* L) {
     if (!L) return fail(NP_EINVAL, "layer must not be NULL");
     DeviceGuard g(L->desc.device);
     NP_HIP(hipDeviceSynchronize());
+    ++L->version;
     return init_state(L);
 }
 
@@ -450,7 +631,7 @@ np_status np_layer_set_ffn_shape(np_layer* L, int32_t slots_per_wg, int32_t tile
     if (slots_per_wg) L->spw = slots_per_wg < 0 ? 0 : slots_per_wg;
     if (tile_cols) L->tw = tile_cols;
     if (threads) L->nt = threads;
-    FfnShape sh;
+    FfnShape sh{};
     if (!ffn_shape(L, L->desc.k_max, &sh)) {
         L->spw = old_spw;
         L->tw = old_tw;
@@ -464,6 +645,7 @@ np_status np_layer_set_ffn_shape(np_layer* L, int32_t slots_per_wg, int32_t tile
         L->tw = old_tw;
         L->nt = old_nt;
     }
+    ++L->version;
     return st;
 }
 
@@ -481,7 +663,7 @@ np_status np_delta_assign(np_layer* L, int32_t gate_cid, int32_t up_cid, void* s
     int n_in = 0;
     for (int w = 0; w < L->W; ++w) n_in += __builtin_popcountll(S[w] & ~L->h_res[w]);
     DeviceGuard g(L->desc.device);
-    DeltaLaunch a;
+    DeltaLaunch a{};
     a.layers[0] = L->ldev;
     a.cid[0][0] = gate_cid;
     a.cid[0][1] = u;
@@ -545,52 +727,70 @@ np_status np_decode_step(np_layer* const* layers, int32_t n_layers, const int32_
     }
     DeviceGuard g(dev);
     hipStream_t cs = (hipStream_t)compute_stream, ps = (hipStream_t)copy_stream;
-    const bool two = cs != ps;
-    hipEvent_t ev_assign = nullptr;
-    if (two) {
-        auto& evs = assign_events();
-        auto it = evs.find(dev);
-        if (it == evs.end()) {
-            NP_HIP(hipEventCreateWithFlags(&ev_assign, hipEventDisableTiming));
-            evs[dev] = ev_assign;
-        } else {
-            ev_assign = it->second;
+    auto commit_host_state = [&]() {
+        for (int l = 0; l < n_layers; ++l) {
+            np_layer* L = layers[l];
+            L->h_res.swap(S[l]);
+            L->n_active = n_act[l];
+            L->n_in = n_in[l];
+            L->total_active += n_act[l];
+            L->total_in += n_in[l];
+            L->state = kAssigned;
         }
-    }
-    for (int l0 = 0; l0 < n_layers; l0 += kMaxLayersPerLaunch) {
-        DeltaLaunch a;
-        a.n_layers = std::min(kMaxLayersPerLaunch, n_layers - l0);
-        for (int k = 0; k < a.n_layers; ++k) {
-            a.layers[k] = layers[l0 + k]->ldev;
-            a.cid[k][0] = cids[2 * (l0 + k)];
-            a.cid[k][1] = u_eff[l0 + k];
+    };
+
+    if (g_use_graphs.load() && n_layers <= kMaxGraphLayers && cs && ps) {
+        np_status st = NP_OK;
+        DecodePlan* P = get_plan(layers, n_layers, cs, ps, dev, &st);
+        if (P) {
+            for (int l0 = 0; l0 < n_layers; l0 += kParamsPerLaunch) {
+                ParamsUpdate pu{};
+                pu.first = l0;
+                pu.count = std::min(kParamsPerLaunch, n_layers - l0);
+                for (int k = 0; k < pu.count; ++k) {
+                    np_layer* L = layers[l0 + k];
+                    pu.cid[k][0] = cids[2 * (l0 + k)];
+                    pu.cid[k][1] = u_eff[l0 + k];
+                    if (++L->ffn_seq == 0) L->ffn_seq = 1;
+                    pu.seq[k] = L->ffn_seq;
+                }
+                pu.x = x;
+                pu.y = y;
+                NP_HIP(launch_set_params(pu, P->prm, cs));
+            }
+            NP_HIP(hipGraphLaunch(P->exec, cs));
+            commit_host_state();
+            for (int l = 0; l < n_layers; ++l) layers[l]->state = kScattered;
+            return NP_OK;
         }
-        NP_HIP(launch_delta_assign(a, cs));
+        if (st != NP_OK && st != NP_EHIP) return st;  // a real argument error, not a capture failure
+        // capture unavailable: fall through to direct launches
     }
-    for (int l = 0; l < n_layers; ++l) {
-        np_layer* L = layers[l];
-        L->h_res.swap(S[l]);
-        L->n_active = n_act[l];
-        L->n_in = n_in[l];
-        L->total_active += n_act[l];
-        L->total_in += n_in[l];
-        L->state = kAssigned;
-    }
-    if (two) {
-        NP_HIP(hipEventRecord(ev_assign, cs));
-        NP_HIP(hipStreamWaitEvent(ps, ev_assign, 0));
-    }
-    for (int l = 0; l < n_layers; ++l) {
-        np_layer* L = layers[l];
-        np_status st = enqueue_scatter(L, two ? ps : cs);
+
+    const hipEvent_t* ev = nullptr;
+    if (!one_queue(layers, n_layers, cs, ps)) {
+        np_status st = step_events(dev, n_layers, &ev);
         if (st != NP_OK) return st;
-        L->state = kScattered;
-        if (two) {
-            NP_HIP(hipEventRecord(L->ev_scatter, ps));
-            NP_HIP(hipStreamWaitEvent(cs, L->ev_scatter, 0));
-        }
-        st = enqueue_ffn(L, x + (size_t)l * d, y + (size_t)l * d, cs);
-        if (st != NP_OK) return st;
+    }
+    std::vector<int32_t> cid_eff(2 * n_layers);
+    for (int l = 0; l < n_layers; ++l) {
+        cid_eff[2 * l] = cids[2 * l];
+        cid_eff[2 * l + 1] = u_eff[l];
+    }
+    // the direct launches size their grids from the new host counts; a launch failure leaves the
+    // layers assigned-but-unscattered, so they need np_layer_reset before further use
+    commit_host_state();
+    np_status st = enqueue_token(layers, n_layers, cid_eff.data(), x, y, cs, ps, nullptr, ev);
+    if (st != NP_OK) return st;
+    for (int l = 0; l < n_layers; ++l) layers[l]->state = kScattered;
+    return NP_OK;
+}
+
+np_status np_decode_use_graphs(int32_t enable) {
+    g_use_graphs.store(enable ? 1 : 0);
+    if (!enable) {
+        std::lock_guard<std::mutex> lk(g_plan_mu);
+        g_plans.clear();
     }
     return NP_OK;
 }

@@ -37,12 +37,43 @@ struct LayerDev {
     int32_t* counts;         // [4] n_in, n_out, n_active, error bits
     int32_t W, Kw, M, K;
     int32_t mode, n_tables, C, pad;
+    const uint16_t* store;   // backing row store (device address; may be mapped host memory)
+    uint16_t* buf;           // [K][R][d] slot buffer
+    int32_t bundle16;        // 16-byte chunks per bundle
+    int32_t pad2;
+};
+
+// One launch scattering the deltas of many layers (blockIdx.y = layer).
+struct ScatterLaunch {
+    const LayerDev* layers[kMaxLayersPerLaunch];
+    int32_t n_layers;
+};
+
+// Per-token values of a replayed decode step, in device memory: written by k_set_params
+// (whose kernel arguments carry them) before the step's captured launches read them.
+constexpr int kMaxGraphLayers = 256;
+struct DecodeParams {
+    int32_t cid[kMaxGraphLayers][2];
+    uint32_t seq[kMaxGraphLayers];
+    const float* x;  // [n_layers][d]
+    float* y;        // [n_layers][d]
+};
+// What one k_set_params launch carries (kernel arguments are limited to 4 KiB).
+constexpr int kParamsPerLaunch = 128;
+struct ParamsUpdate {
+    int32_t first, count;
+    int32_t cid[kParamsPerLaunch][2];
+    uint32_t seq[kParamsPerLaunch];
+    const float* x;
+    float* y;
 };
 
 struct DeltaLaunch {
     const LayerDev* layers[kMaxLayersPerLaunch];
     int32_t cid[kMaxLayersPerLaunch][2];
     int32_t n_layers;
+    const DecodeParams* prm;  // if set, centroid IDs come from prm->cid[layer0 + i]
+    int32_t layer0;
 };
 
 // FFN launch shape (chosen on the host from the host-known |S|).
@@ -66,6 +97,8 @@ struct FfnArgs {
     uint64_t* ppair;        // [nwg][tw] (launch sequence, partial sum) words
     uint32_t seq;           // this launch's sequence number (never 0)
     int32_t n;              // active slots (host-known), or -1 to read counts[2]
+    const DecodeParams* prm;  // if set: seq, x and y come from prm (layer `layer`), n from counts[2]
+    int32_t layer;
     uint32_t buf_bytes;     // size of buf (below 4 GiB)
     int32_t d, K, R;
     int32_t p1, q, tw, nwg;
@@ -73,9 +106,11 @@ struct FfnArgs {
 
 // Launchers (return hipError_t from the launch).
 hipError_t launch_delta_assign(const DeltaLaunch& a, hipStream_t s);
+hipError_t launch_set_params(const ParamsUpdate& p, DecodeParams* dst, hipStream_t s);
 hipError_t launch_scatter(int32_t* counts, const int32_t* d_in, const int32_t* slot_in,
                           const uint16_t* store, uint16_t* buf, int32_t M, int32_t K,
                           int32_t bundle_elems, int grid, hipStream_t s);
+hipError_t launch_scatter_all(const ScatterLaunch& a, int wgs_per_layer, hipStream_t s);
 hipError_t launch_sparse_ffn(const FfnArgs& a, const FfnShape& sh, bool gated, hipStream_t s);
 hipError_t launch_probe_read(const void* src, int64_t bytes, float* sink, hipStream_t s);
 hipError_t launch_probe_copy(void* dst, const void* src, int64_t bytes, hipStream_t s);

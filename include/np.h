@@ -131,15 +131,31 @@ np_status np_sparse_ffn(np_layer* layer, const float* x, float* y, void* stream)
 
 /* One decode token over n_layers layers of one device with equal d_model
  * (sections 3.1, 3.4, 3.5): validates every layer's cids on the host (a
- * failure leaves every layer unchanged), then on compute_stream one launch
- * assigns the deltas of all layers; on copy_stream the layer-l scatter
- * waits for that launch; the layer-l FFN on compute_stream waits for the
- * layer-l scatter, so scatters of later layers overlap earlier FFNs.
- * cids: host int32 [n_layers][2] (gate, up). x, y: device fp32
- * [n_layers][d_model]. copy_stream may equal compute_stream. Every layer
- * must be in the fresh or scattered state (NP_ESTATE otherwise). */
+ * failure leaves every layer unchanged), then enqueues the token. When every
+ * row store is device memory, or copy_stream equals compute_stream, all work
+ * goes to compute_stream: one launch assigns the deltas of all layers, one
+ * launch copies the new bundles of all layers, then the FFNs run in layer
+ * order. When some row store is pinned host memory and the streams differ,
+ * layer l's scatter runs on copy_stream after the assignment and layer l's
+ * FFN on compute_stream waits only for it, so the host-link transfers of
+ * later layers overlap earlier FFNs; copy_stream is joined back into
+ * compute_stream at the end. cids: host int32 [n_layers][2] (gate, up).
+ * x, y: device fp32 [n_layers][d_model]. Every layer must be in the fresh
+ * or scattered state (NP_ESTATE otherwise); after NP_EHIP the layers need
+ * np_layer_reset. */
 np_status np_decode_step(np_layer* const* layers, int32_t n_layers, const int32_t* cids,
                          const float* x, float* y, void* compute_stream, void* copy_stream);
+
+/* Process-wide switch for np_decode_step. 1 (the default): the first call for a
+ * given (layer set, compute stream, copy stream) captures the step's launches
+ * into a HIP graph; every call then writes that token's centroid IDs, x and y
+ * pointers into a small device parameter block with one kernel launch and
+ * replays the graph on compute_stream, so a token costs two host calls instead
+ * of several per layer. The graph is rebuilt when a layer is reset, reshaped or
+ * destroyed. Streams must be non-NULL for the graph path (otherwise, and if
+ * capture fails, the launches are issued one by one). 0: always issue the
+ * launches one by one. Results are the same either way. */
+np_status np_decode_use_graphs(int32_t enable);
 
 /* Synchronizes the layer's device, then copies the current state to host
  * buffers (any pointer may be NULL): slot_map int32 [d_ff], owner int32

@@ -62,9 +62,10 @@ SMALL = [
 
 
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: f"d{c.d}_M{c.M}_K{c.K}_{c.mode}_R{c.R}")
-@pytest.mark.parametrize("streams", [1, 2])
-def test_small_shapes_decode_step(torch, cfg, streams):
+@pytest.mark.parametrize("streams,graphs", [(1, True), (2, True), (2, False)])
+def test_small_shapes_decode_step(torch, cfg, streams, graphs):
     from delta_prefetched_ffn_amd import binding as B
+    B.decode_use_graphs(graphs)
     wl = Workload(cfg)
     layers, stores = zip(*[make_layer(wl, l) for l in range(cfg.L)])
     orc = OracleRun(wl)
@@ -89,6 +90,7 @@ def test_small_shapes_decode_step(torch, cfg, streams):
             check_y(yh[t, l], O.sparse_ffn(stores[l], cfg.R, cfg.d, S, x_all[t, l]), f"t={t} l={l}")
     for layer in layers:
         layer.close()
+    B.decode_use_graphs(True)
 
 
 def _dyadic_store(rng, M, R, d):
@@ -132,15 +134,19 @@ def test_exact_dyadic_inputs_bit_exact(torch, R):
 
 
 def test_decode_paths_agree_and_repeat_bitwise(torch):
-    """One stream, two streams and per-layer calls give bit-identical y; reruns too."""
+    """Graph replay and direct launches, one stream and two streams, device and pinned-host row
+    stores (the latter takes the per-layer two-stream structure), and per-layer calls give
+    bit-identical y; reruns too."""
     from delta_prefetched_ffn_amd import binding as B
     cfg = small_config(960, L=3, d=4096, M=3000, K=600, C=6, mode="union", m=250, swap=30, T=6)
     wl = Workload(cfg)
     x_all = wl.x_all()
     x = torch.from_numpy(x_all).cuda()
     outs = []
-    for path in ["two", "one", "calls", "two"]:
-        layers = [make_layer(wl, l)[0] for l in range(cfg.L)]
+    for path in ["two", "one", "calls", "two-direct", "one-direct", "two-host", "two-host-direct", "two"]:
+        B.decode_use_graphs(not path.endswith("direct"))
+        where = "host" if "host" in path else "device"
+        layers = [make_layer(wl, l, where)[0] for l in range(cfg.L)]
         y = torch.zeros_like(x)
         cs, ps = torch.cuda.Stream(), torch.cuda.Stream()
         for t in range(cfg.T):
@@ -152,11 +158,13 @@ def test_decode_paths_agree_and_repeat_bitwise(torch):
                     layer.sparse_ffn(x[t, l].data_ptr(), y[t, l].data_ptr(), cs.cuda_stream)
             else:
                 B.decode_step(layers, wl.cids()[t], x[t].data_ptr(), y[t].data_ptr(), cs.cuda_stream,
-                              (ps if path == "two" else cs).cuda_stream)
+                              (ps if path.startswith("two") else cs).cuda_stream)
         torch.cuda.synchronize()
+        assert all(L.read_state()["err"] == 0 for L in layers)
         outs.append(y.cpu().numpy())
         for layer in layers:
             layer.close()
+    B.decode_use_graphs(True)
     for o in outs[1:]:
         assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
 

@@ -49,11 +49,16 @@ __device__ inline uint64_t drop_low_bits(uint64_t w, int r) {
     return w;
 }
 
+constexpr int kOwnRegs = 32;  // owner entries per thread loaded with the masks (K <= 8192 in one pass)
+
 __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
     __shared__ uint64_t s_S[kMaxWords];
     __shared__ uint64_t s_R[kMaxWords];
-    __shared__ uint64_t s_free[kMaxKWords];
-    __shared__ int s_fpre[kMaxKWords];
+    __shared__ uint64_t s_Fa[kMaxKWords];  // free slots before this step
+    __shared__ uint64_t s_F0[kMaxKWords];  // free slots after the release
+    __shared__ uint64_t s_F1[kMaxKWords];  // free slots after the assignment
+    __shared__ int s_fpre[kMaxKWords];     // exclusive prefix of |F0| per word
+    __shared__ int s_opre[kMaxKWords];     // exclusive prefix of occupied slots per word
     __shared__ int s_tmp[kWaves + 1];
     __shared__ int s_err;
 
@@ -63,18 +68,26 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
     const int32_t cg = a.prm ? a.prm->cid[a.layer0 + blockIdx.x][0] : a.cid[blockIdx.x][0];
     const int32_t cu = a.prm ? a.prm->cid[a.layer0 + blockIdx.x][1] : a.cid[blockIdx.x][1];
 
-    // Step 1: active set S from the selected gate/up masks; R from the resident bits.
+    // Step 1: active set S from the selected gate/up masks; R from the resident bits. The
+    // owner table (slot -> neuron) is read in the same round trip: it drives the release.
     const uint64_t* ma = L.masks + (size_t)cg * L.W;
     const uint64_t* mb = L.masks + ((size_t)(L.n_tables - 1) * L.C + cu) * L.W;
+    int own[kOwnRegs];
+#pragma unroll
+    for (int k = 0; k < kOwnRegs; ++k) {
+        const int sl = tid + k * kNT;
+        own[k] = sl < L.K ? L.owner[sl] : -1;
+    }
     for (int w = tid; w < L.W; w += kNT) {
         const uint64_t ga = ma[w], gb = mb[w];
         s_S[w] = L.mode == 0 ? (ga | gb) : L.mode == 1 ? (ga & gb) : ga;
         s_R[w] = L.res[w];
     }
-    for (int v = tid; v < L.Kw; v += kNT) s_free[v] = L.freeb[v];
+    for (int v = tid; v < L.Kw; v += kNT) s_Fa[v] = s_F0[v] = L.freeb[v];
     __syncthreads();
 
-    // Step 2: |D_in| and |D_out| per contiguous word range, scanned for list offsets.
+    // Step 2: |D_in| and |D_out| per contiguous word range, scanned for list offsets;
+    // D_out is written in ascending order.
     const int wpt = (L.W + kNT - 1) / kNT;
     const int w0 = min(tid * wpt, L.W), w1 = min(w0 + wpt, L.W);
     int c_in = 0, c_out = 0;
@@ -85,85 +98,127 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
     int n_in, n_out;
     const int base_in = block_excl_scan(c_in, &n_in, s_tmp);
     const int base_out = block_excl_scan(c_out, &n_out, s_tmp);
-
-    // Step 3: D_out in ascending order; release its slots (owner -1, slot map -1, free bit).
-    int k = base_out;
-    for (int w = w0; w < w1; ++w) {
-        uint64_t bits = s_R[w] & ~s_S[w];
-        while (bits) {
-            const int n = w * 64 + (__ffsll((unsigned long long)bits) - 1);
-            bits &= bits - 1;
-            L.d_out[k++] = n;
-            const int s = L.slot_map[n];
-            if ((unsigned)s < (unsigned)L.K) {
-                L.owner[s] = -1;
-                atomicOr((unsigned long long*)&s_free[s >> 6], 1ull << (s & 63));
-            } else {
-                atomicOr(&s_err, kErrBadList);
+    {
+        int k = base_out;
+        for (int w = w0; w < w1; ++w) {
+            uint64_t bits = s_R[w] & ~s_S[w];
+            while (bits) {
+                L.d_out[k++] = w * 64 + (__ffsll((unsigned long long)bits) - 1);
+                bits &= bits - 1;
             }
-            L.slot_map[n] = -1;
         }
     }
-    __syncthreads();
+
+    // Step 3: release the slots whose owner leaves the active set (slot map -1, free bit;
+    // the owner entry is cleared below unless the slot is taken again). Every slot is
+    // looked at once, so the owners of D_out are found without a slot-map lookup each.
+    auto release = [&](int sl, int n) {
+        if (n < 0) return 0;
+        if (n >= L.M) {
+            atomicOr(&s_err, kErrBadList);
+            return 0;
+        }
+        const uint64_t bit = 1ull << (n & 63);
+        if ((s_R[n >> 6] & bit) == 0) {  // an owned slot must belong to a resident neuron
+            atomicOr(&s_err, kErrBadList);
+            return 0;
+        }
+        if (s_S[n >> 6] & bit) return 0;  // stays resident
+        L.slot_map[n] = -1;
+        atomicOr((unsigned long long*)&s_F0[sl >> 6], 1ull << (sl & 63));
+        return 1;
+    };
+    int c_rel = 0;
+#pragma unroll
+    for (int k = 0; k < kOwnRegs; ++k) c_rel += release(tid + k * kNT, own[k]);
+    for (int sl = tid + kOwnRegs * kNT; sl < L.K; sl += kNT) c_rel += release(sl, L.owner[sl]);
+    int n_rel;
+    (void)block_excl_scan(c_rel, &n_rel, s_tmp);  // also orders the releases before what follows
+    if (tid == 0 && n_rel != n_out) atomicOr(&s_err, kErrBadList);
 
     // Free slots after the release: per-word prefix counts (ascending slot order).
     const int kpt = (L.Kw + kNT - 1) / kNT;
     const int v0 = min(tid * kpt, L.Kw), v1 = min(v0 + kpt, L.Kw);
     int c_free = 0;
-    for (int v = v0; v < v1; ++v) c_free += __popcll(s_free[v]);
+    for (int v = v0; v < v1; ++v) c_free += __popcll(s_F0[v]);
     int n_free;
-    int pre = block_excl_scan(c_free, &n_free, s_tmp);
-    for (int v = v0; v < v1; ++v) {
-        s_fpre[v] = pre;
-        pre += __popcll(s_free[v]);
-    }
-    __syncthreads();
-
-    // Step 4: the i-th incoming neuron (ascending) takes the i-th free slot (ascending).
-    k = base_in;
-    for (int w = w0; w < w1; ++w) {
-        uint64_t bits = s_S[w] & ~s_R[w];
-        while (bits) {
-            const int n = w * 64 + (__ffsll((unsigned long long)bits) - 1);
-            bits &= bits - 1;
-            const int idx = k++;
-            if (idx >= n_free) {
-                atomicOr(&s_err, kErrFreeExhausted);
-                continue;
-            }
-            int lo = 0, hi = L.Kw - 1;  // last word whose prefix is <= idx
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (s_fpre[mid] <= idx) lo = mid; else hi = mid - 1;
-            }
-            const uint64_t fw = drop_low_bits(s_free[lo], idx - s_fpre[lo]);
-            const int slot = lo * 64 + (__ffsll((unsigned long long)fw) - 1);
-            L.d_in[idx] = n;
-            L.slot_in[idx] = slot;
-            L.slot_map[n] = slot;
-            L.owner[slot] = n;
+    {
+        int pre = block_excl_scan(c_free, &n_free, s_tmp);
+        for (int v = v0; v < v1; ++v) {
+            s_fpre[v] = pre;
+            pre += __popcll(s_F0[v]);
         }
     }
-    __syncthreads();
-
-    // Taken slots leave the free set; occupied slots are listed in ascending order.
+    // Step 4 (set part): the n_in lowest free slots are taken; occupied slots per word.
     int c_occ = 0;
     for (int v = v0; v < v1; ++v) {
-        const int take = min(max(n_in - s_fpre[v], 0), __popcll(s_free[v]));
-        const uint64_t fw = drop_low_bits(s_free[v], take);
-        s_free[v] = fw;
+        const int take = min(max(n_in - s_fpre[v], 0), __popcll(s_F0[v]));
+        const uint64_t fw = drop_low_bits(s_F0[v], take);
+        s_F1[v] = fw;
         L.freeb[v] = fw;
+        uint64_t gone = s_F0[v] & ~s_Fa[v] & fw;  // released and not taken again: no owner
+        while (gone) {
+            L.owner[v * 64 + __ffsll((unsigned long long)gone) - 1] = -1;
+            gone &= gone - 1;
+        }
         const uint64_t valid = (v == L.Kw - 1 && (L.K & 63)) ? ((1ull << (L.K & 63)) - 1) : ~0ull;
         c_occ += __popcll(~fw & valid);
     }
     int n_act;
-    int o = block_excl_scan(c_occ, &n_act, s_tmp);
+    {
+        int pre = block_excl_scan(c_occ, &n_act, s_tmp);  // the barrier inside publishes s_fpre, s_F1
+        for (int v = v0; v < v1; ++v) {
+            s_opre[v] = pre;
+            const uint64_t valid = (v == L.Kw - 1 && (L.K & 63)) ? ((1ull << (L.K & 63)) - 1) : ~0ull;
+            pre += __popcll(~s_F1[v] & valid);
+        }
+    }
+    __syncthreads();
+
+    // Step 4 (lists): the i-th incoming neuron (ascending) takes the i-th free slot
+    // (ascending). Its position in the ascending occupied-slot list gets the neuron ID in
+    // act_src, so that the FFN can read the new bundle where it still is (the row store).
+    {
+        int k = base_in;
+        for (int w = w0; w < w1; ++w) {
+            uint64_t bits = s_S[w] & ~s_R[w];
+            while (bits) {
+                const int n = w * 64 + (__ffsll((unsigned long long)bits) - 1);
+                bits &= bits - 1;
+                const int idx = k++;
+                if (idx >= n_free) {
+                    atomicOr(&s_err, kErrFreeExhausted);
+                    continue;
+                }
+                int lo = 0, hi = L.Kw - 1;  // last word whose prefix is <= idx
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (s_fpre[mid] <= idx) lo = mid; else hi = mid - 1;
+                }
+                const uint64_t fw = drop_low_bits(s_F0[lo], idx - s_fpre[lo]);
+                const int slot = lo * 64 + (__ffsll((unsigned long long)fw) - 1);
+                const uint64_t below = (1ull << (slot & 63)) - 1;
+                const int pos = s_opre[lo] + __popcll(~s_F1[lo] & below);
+                L.d_in[idx] = n;
+                L.slot_in[idx] = slot;
+                L.slot_map[n] = slot;
+                L.owner[slot] = n;
+                L.act_src[pos] = n;
+            }
+        }
+    }
+    // Occupied slots in ascending order; slots kept from the last step have act_src -1.
     for (int v = v0; v < v1; ++v) {
         const uint64_t valid = (v == L.Kw - 1 && (L.K & 63)) ? ((1ull << (L.K & 63)) - 1) : ~0ull;
-        uint64_t occ = ~s_free[v] & valid;
+        const uint64_t taken = s_F0[v] & ~s_F1[v];
+        uint64_t occ = ~s_F1[v] & valid;
+        int o = s_opre[v];
         while (occ) {
-            L.act[o++] = v * 64 + (__ffsll((unsigned long long)occ) - 1);
+            const int b = __ffsll((unsigned long long)occ) - 1;
             occ &= occ - 1;
+            L.act[o] = v * 64 + b;
+            if (!((taken >> b) & 1)) L.act_src[o] = -1;
+            ++o;
         }
     }
 

@@ -25,6 +25,12 @@
 //     tile's partials in ascending contributor order (fixed order: results are
 //     identical run to run) and writes y.
 //
+// Read-through: in a decode step whose row store is device memory, a slot filled this
+// step is read from the row store (where its bundle already is) instead of from the slot
+// buffer, and the workgroup that reads a piece of such a bundle also writes it into the
+// slot. Every piece of every active bundle is read by exactly one workgroup, so the new
+// rows cross HBM once for reading and once for writing, and no separate scatter runs.
+//
 // Exchanges between workgroups carry their own validity: every h value and
 // every partial sum is stored as one 64-bit word (launch sequence number,
 // value) with an L2-coherent (agent-scope) store, and the reader re-reads a
@@ -67,15 +73,12 @@ __device__ inline void axpy8(float* acc, const float h, const uint4 v) {
     acc[7] = fmaf(h, bf_hi(v.w), acc[7]);
 }
 
-// Weight rows are read through a raw buffer resource covering the slot buffer: a lane
-// with nothing to load uses an offset past the end, which returns zeros without a
-// memory access. Every load is then an unconditional instruction, so the compiler
-// can wait for exactly the loads a computation needs.
-constexpr uint32_t kNoLoad = 0xFFFFFFF0u;
-__device__ inline uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    return make_uint4(v[0], v[1], v[2], v[3]);
-}
+// Weight rows are read with unconditional 16-byte loads: a lane with nothing to load
+// reads a fixed valid address (the start of the slot buffer) and its value is not used.
+// Every load is then an unconditional instruction, so the compiler can wait for exactly
+// the loads a computation needs.
+__device__ inline uint4 gload(const char* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ inline void gstore(char* p, const uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
 __device__ inline uint64_t ld_pair(const uint64_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -117,6 +120,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     constexpr int NR1 = GATED ? 2 : 1;  // rows dotted with x per slot
 
     __shared__ int s_act[kWinMax];
+    __shared__ int s_src[kWinMax];  // read-through: neuron whose bundle is in the row store, else -1
     __shared__ float s_red1[kWaves * SB * NR1];  // wave sums of the gate/up dot products
     __shared__ float s_red2[NT * 8];
 
@@ -167,26 +171,39 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     const int wn = phi - plo;
     {
         constexpr int kStage = (kWinMax + NT - 1) / NT;
-        int v[kStage];
+        int v[kStage], u[kStage];
 #pragma unroll
         for (int k = 0; k < kStage; ++k) {
             const int i = tid + k * NT;
             v[k] = i < wn ? a.act[plo + i] : 0;
+            u[k] = (a.act_src && i < wn) ? a.act_src[plo + i] : -1;
         }
 #pragma unroll
         for (int k = 0; k < kStage; ++k) {
             const int i = tid + k * NT;
             const bool bad = (unsigned)v[k] >= (unsigned)a.K;
-            err |= bad ? kErrBadList : 0;
-            if (i < wn) s_act[i] = bad ? 0 : v[k];
+            const bool badsrc = u[k] >= a.M;
+            err |= (bad || badsrc) ? kErrBadList : 0;
+            if (i < wn) {
+                s_act[i] = bad ? 0 : v[k];
+                s_src[i] = (bad || badsrc || u[k] < 0) ? -1 : u[k];
+            }
         }
     }
     __syncthreads();
 
     // ---------------- phase 1 loads: gate/up rows of chunk w (issued first) ----------------
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)a.buf, (short)0, (int)a.buf_bytes, 0x00020000);
-    const uint32_t slot_bytes = (uint32_t)R * cpr * 16u;
+    const size_t slot_bytes = (size_t)R * cpr * 16u;
+    const char* const buf_c = reinterpret_cast<const char*>(a.buf);
+    char* const buf_w = reinterpret_cast<char*>(a.buf);
+    const char* const store_c = reinterpret_cast<const char*>(a.store);
+    const bool rt = a.act_src != nullptr;
+    // Start of the bundle at window position p: its slot, or the row store for a slot
+    // filled this step (read-through).
+    auto row_base = [&](int p) -> const char* {
+        const int src = s_src[p];
+        return src >= 0 ? store_c + (size_t)src * slot_bytes : buf_c + (size_t)s_act[p] * slot_bytes;
+    };
     const bool has1 = w < a.p1;
     const int c0 = has1 ? max(cbeg(w), plo) : 0, c1 = has1 ? min(cbeg(w + 1), phi) : 0;
     uint4 wv[SB][NR1][JX];
@@ -195,19 +212,36 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
         for (int i = 0; i < SB; ++i) {
             const int pos = b0 + rl + RL * i;
             const bool ok = pos < c1;
-            const uint32_t rowoff = ok ? (uint32_t)s_act[pos - plo] * slot_bytes : 0u;
+            const char* rp = ok ? row_base(pos - plo) : buf_c;
 #pragma unroll
             for (int r = 0; r < NR1; ++r)
 #pragma unroll
                 for (int j = 0; j < JX; ++j) {
                     const int c = cl + CL * j;
-                    wv[i][r][j] = bload(rs, ok && c < cpr ? rowoff + (uint32_t)(r * cpr + c) * 16u : kNoLoad);
+                    wv[i][r][j] = gload(ok && c < cpr ? rp + (size_t)(r * cpr + c) * 16u : buf_c);
                 }
         }
     };
     // h for the batch starting at b0: dot products, reduction over the row lane, store.
     auto compute_batch = [&](int b0) {
         constexpr int V = SB * NR1;  // partial dot products per lane (a power of two <= 64)
+        if (rt) {
+            // read-through: the gate/up pieces of slots filled this step go into their slots
+#pragma unroll
+            for (int i = 0; i < SB; ++i) {
+                const int pos = b0 + rl + RL * i;
+                if (pos < c1 && s_src[pos - plo] >= 0) {
+                    char* dst = buf_w + (size_t)s_act[pos - plo] * slot_bytes;
+#pragma unroll
+                    for (int r = 0; r < NR1; ++r)
+#pragma unroll
+                        for (int j = 0; j < JX; ++j) {
+                            const int c = cl + CL * j;
+                            if (c < cpr) gstore(dst + (size_t)(r * cpr + c) * 16u, wv[i][r][j]);
+                        }
+                }
+            }
+        }
         float v[V];
 #pragma unroll
         for (int i = 0; i < SB; ++i)
@@ -215,7 +249,8 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
             for (int r = 0; r < NR1; ++r) {
                 float acc = 0.f;
 #pragma unroll
-                for (int j = 0; j < JX; ++j) acc += dot8(wv[i][r][j], xv[j]);
+                for (int j = 0; j < JX; ++j)
+                    if (cl + CL * j < cpr) acc += dot8(wv[i][r][j], xv[j]);
                 v[i * NR1 + r] = acc;
             }
         if (CL >= 64) {
@@ -280,12 +315,12 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     const int RL2 = NT / CT;                  // row lanes
     const int c2 = tid % CT, r2 = tid / CT;
     const bool cok = (c2 << 3) < tcols;
-    const uint32_t dcol = ((uint32_t)(R - 1) * cpr + (col0 >> 3) + c2) * 16u;
+    const size_t dcol = ((size_t)(R - 1) * cpr + (col0 >> 3) + c2) * 16u;
     uint4 dv[U2];
 #pragma unroll
     for (int u = 0; u < U2; ++u) {
         const int i = r2 + u * RL2;
-        dv[u] = bload(rs, cok && i < wn ? (uint32_t)s_act[i] * slot_bytes + dcol : kNoLoad);
+        dv[u] = gload(cok && i < wn ? row_base(i) + dcol : buf_c);
     }
 
     // ---------------- phase 1 compute: h for chunk w ----------------
@@ -343,14 +378,18 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
 #pragma unroll
         for (int u = 0; u < U2; ++u) {
             const int i = i0 + u * RL2;
-            if (cok && i < wn) axpy8(acc, pair_val(hp[u]), dv[u]);
+            if (cok && i < wn) {
+                axpy8(acc, pair_val(hp[u]), dv[u]);
+                // read-through: this tile's piece of the down row goes into its slot
+                if (rt && s_src[i] >= 0) gstore(buf_w + (size_t)s_act[i] * slot_bytes + dcol, dv[u]);
+            }
         }
         i0 += U2 * RL2;
         if (i0 >= wn) break;
 #pragma unroll
         for (int u = 0; u < U2; ++u) {
             const int i = i0 + u * RL2;
-            dv[u] = bload(rs, cok && i < wn ? (uint32_t)s_act[i] * slot_bytes + dcol : kNoLoad);
+            dv[u] = gload(cok && i < wn ? row_base(i) + dcol : buf_c);
         }
     }
 

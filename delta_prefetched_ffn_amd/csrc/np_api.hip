@@ -82,7 +82,7 @@ struct np_layer {
     int32_t* owner = nullptr;
     uint64_t* res = nullptr;
     uint64_t* freeb = nullptr;
-    int32_t* lists = nullptr;  // d_in | slot_in | d_out | act, K each
+    int32_t* lists = nullptr;  // d_in | slot_in | d_out | act | act_src, K each
     int32_t* counts = nullptr;
     uint64_t* hpair = nullptr;
     uint64_t* ppair = nullptr;
@@ -101,6 +101,7 @@ struct np_layer {
     int32_t* slot_in() const { return lists + desc.k_max; }
     int32_t* d_out() const { return lists + 2 * (size_t)desc.k_max; }
     int32_t* act() const { return lists + 3 * (size_t)desc.k_max; }
+    int32_t* act_src() const { return lists + 4 * (size_t)desc.k_max; }
     size_t bundle_elems() const { return (size_t)desc.n_rows * desc.d_model; }
 };
 
@@ -190,7 +191,7 @@ np_status init_state(np_layer* L) {
     std::vector<uint64_t> fb(L->Kw, ~0ull);
     if (K & 63) fb[L->Kw - 1] = (1ull << (K & 63)) - 1;
     NP_HIP(hipMemcpy(L->freeb, fb.data(), (size_t)L->Kw * 8, hipMemcpyHostToDevice));
-    NP_HIP(hipMemset(L->lists, 0, (size_t)4 * K * 4));
+    NP_HIP(hipMemset(L->lists, 0, (size_t)5 * K * 4));
     NP_HIP(hipMemset(L->counts, 0, 4 * 4));
     NP_HIP(hipDeviceSynchronize());
     std::fill(L->h_res.begin(), L->h_res.end(), 0ull);
@@ -236,8 +237,10 @@ np_status check_cids(const np_layer* L, int32_t g, int32_t u, int32_t* eff_u) {
 int scatter_grid(int n_in) { return std::max(1, std::min(n_in, 4096)); }
 
 // prm != nullptr: a launch captured into a decode graph (per-token values from prm).
+// read_through: the slots filled by the last assignment are read from the (device) row
+// store and written into the slot buffer by the FFN itself, in place of a scatter.
 np_status enqueue_ffn(np_layer* L, const float* x, float* y, hipStream_t s, const DecodeParams* prm = nullptr,
-                      int layer = 0) {
+                      int layer = 0, bool read_through = false) {
     FfnShape sh{};
     if (!ffn_shape(L, L->n_active, &sh, prm != nullptr))
         return fail(NP_EINVAL, "no FFN launch shape for d_model=%d n=%d tile=%d", L->desc.d_model,
@@ -245,6 +248,8 @@ np_status enqueue_ffn(np_layer* L, const float* x, float* y, hipStream_t s, cons
     FfnArgs a{};
     a.buf = L->buf;
     a.act = L->act();
+    a.act_src = read_through ? L->act_src() : nullptr;
+    a.store = read_through ? L->store_dev : nullptr;
     a.counts = L->counts;
     a.x = x;
     a.y = y;
@@ -264,6 +269,7 @@ np_status enqueue_ffn(np_layer* L, const float* x, float* y, hipStream_t s, cons
     a.d = L->desc.d_model;
     a.K = L->desc.k_max;
     a.R = L->desc.n_rows;
+    a.M = L->desc.d_ff;
     a.p1 = sh.p1;
     a.q = sh.q;
     a.tw = sh.tw;
@@ -281,9 +287,10 @@ np_status enqueue_scatter(np_layer* L, hipStream_t s, bool fixed_grid = false) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// A token's launches go to one queue (assign, one scatter launch for all layers, the FFNs in
-// layer order) unless some backing store is in host memory and a separate copy stream is given:
-// then layer l's scatter runs on the copy stream and layer l's FFN waits only for it, so the
+// A token's launches go to one queue (assign, the FFNs in layer order, which read their new
+// bundles through from device-memory row stores; one scatter launch first for host-memory
+// stores) unless some row store is in host memory and a separate copy stream is given: then
+// layer l's scatter runs on the copy stream and layer l's FFN waits only for it, so the
 // host-link transfers of later layers overlap earlier FFNs.
 bool one_queue(np_layer* const* layers, int n, hipStream_t cs, hipStream_t ps) {
     if (cs == ps) return true;
@@ -313,15 +320,21 @@ np_status enqueue_token(np_layer* const* layers, int n, const int32_t* cid, cons
         NP_HIP(launch_delta_assign(a, cs));
     }
     if (one_queue(layers, n, cs, ps)) {
-        for (int l0 = 0; l0 < n; l0 += kMaxLayersPerLaunch) {
-            ScatterLaunch sa{};
-            sa.n_layers = std::min(kMaxLayersPerLaunch, n - l0);
-            for (int k = 0; k < sa.n_layers; ++k) sa.layers[k] = layers[l0 + k]->ldev;
-            NP_HIP(launch_scatter_all(sa, kScatterWgsPerLayer, cs));
+        // Device-memory row stores: each FFN reads its new bundles from the store and writes
+        // them into their slots (read-through). Host-memory stores: one scatter launch first.
+        ScatterLaunch sa{};
+        for (int l = 0; l < n; ++l) {
+            if (!layers[l]->store_is_host) continue;
+            sa.layers[sa.n_layers++] = layers[l]->ldev;
+            if (sa.n_layers == kMaxLayersPerLaunch) {
+                NP_HIP(launch_scatter_all(sa, kScatterWgsPerLayer, cs));
+                sa.n_layers = 0;
+            }
         }
+        if (sa.n_layers > 0) NP_HIP(launch_scatter_all(sa, kScatterWgsPerLayer, cs));
         for (int l = 0; l < n; ++l) {
             np_status st = enqueue_ffn(layers[l], prm ? nullptr : x + (size_t)l * d, prm ? nullptr : y + (size_t)l * d,
-                                       cs, prm, l);
+                                       cs, prm, l, !layers[l]->store_is_host);
             if (st != NP_OK) return st;
         }
         return NP_OK;
@@ -545,7 +558,7 @@ np_status np_layer_create(const np_layer_desc* desc, np_layer** out) {
     bool ok = dmalloc((void**)&L->d_masks, mask_words * 8) && dmalloc((void**)&L->buf, buf_bytes) &&
               dmalloc((void**)&L->slot_map, (size_t)M * 4) && dmalloc((void**)&L->owner, (size_t)K * 4) &&
               dmalloc((void**)&L->res, (size_t)L->W * 8) && dmalloc((void**)&L->freeb, (size_t)L->Kw * 8) &&
-              dmalloc((void**)&L->lists, (size_t)4 * K * 4) && dmalloc((void**)&L->counts, 4 * 4) &&
+              dmalloc((void**)&L->lists, (size_t)5 * K * 4) && dmalloc((void**)&L->counts, 4 * 4) &&
               dmalloc((void**)&L->hpair, (size_t)K * 8) &&
               dmalloc((void**)&L->ldev, sizeof(LayerDev));
     if (!ok) {
@@ -567,6 +580,7 @@ np_status np_layer_create(const np_layer_desc* desc, np_layer** out) {
     ld.slot_in = L->slot_in();
     ld.d_out = L->d_out();
     ld.act = L->act();
+    ld.act_src = L->act_src();
     ld.counts = L->counts;
     ld.W = L->W;
     ld.Kw = L->Kw;

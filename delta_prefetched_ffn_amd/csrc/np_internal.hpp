@@ -34,6 +34,7 @@ struct LayerDev {
     int32_t* slot_in;        // [K]
     int32_t* d_out;          // [K]
     int32_t* act;            // [K] ascending occupied slots
+    int32_t* act_src;        // [K] per act position: the neuron if its slot was filled this step, else -1
     int32_t* counts;         // [4] n_in, n_out, n_active, error bits
     int32_t W, Kw, M, K;
     int32_t mode, n_tables, C, pad;
@@ -88,8 +89,12 @@ struct FfnShape {
 };
 
 struct FfnArgs {
-    const uint16_t* buf;    // [K][R][d]
+    uint16_t* buf;          // [K][R][d]
     const int32_t* act;     // [K]
+    // Read-through (null: off): bundles of slots filled this step are read from the row
+    // store (act_src gives the neuron) and written into their slots by this launch.
+    const int32_t* act_src; // [K]
+    const uint16_t* store;  // [M][R][d]
     int32_t* counts;        // [4]
     const float* x;         // [d]
     float* y;               // [d]
@@ -100,7 +105,7 @@ struct FfnArgs {
     const DecodeParams* prm;  // if set: seq, x and y come from prm (layer `layer`), n from counts[2]
     int32_t layer;
     uint32_t buf_bytes;     // size of buf (below 4 GiB)
-    int32_t d, K, R;
+    int32_t d, K, R, M;
     int32_t p1, q, tw, nwg;
 };
 

@@ -37,7 +37,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--ffn-steps", type=int, default=40, help="tokens in the per-kernel FFN timing pass")
+    p.add_argument("--ffn-steps", type=int, default=40,
+                   help="tokens in each of the two per-kernel FFN timing passes")
+    p.add_argument("--direct", action="store_true",
+                   help="issue each decode step's launches one by one instead of replaying a captured graph")
     p.add_argument("--pcie-steps", type=int, default=40, help="timed tokens with the store in pinned host memory")
     p.add_argument("--no-pcie", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -122,6 +125,7 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    B.decode_use_graphs(not args.direct)
     wl = Workload(CONFIGS[WORKLOAD])
     c = wl.cfg
     t0 = time.time()
@@ -182,38 +186,47 @@ def main():
         f"(host enqueue {enqueued * 1e3 / args.steps:.3f} ms/token)")
 
     # ---------------- FFN kernel timing (roofline of the dominant kernel) ----------------
-    ffn_toks = token_ids(1 + args.warmup + args.steps, args.ffn_steps, c.T)
+    # As in the decode step, each FFN follows its layer's delta assignment directly and reads
+    # the new bundles through from the row store (writing them into their slots). Even tokens:
+    # all 31 launches back to back between two events; odd tokens: each launch between its own
+    # events. Algorithmic bytes of a launch: active bundles read + new bundles written + x + y.
+    ffn_toks = token_ids(1 + args.warmup + args.steps, 2 * args.ffn_steps, c.T)
     s = cs
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(c.L)]
     burst = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    per_launch_ms, burst_ms, ffn_bytes, launches = 0.0, 0.0, 0, 0
-    for t in ffn_toks:
+    burst_ms, event_ms, burst_bytes, burst_act_bytes, burst_n, event_n = 0.0, 0.0, 0, 0, 0, 0
+    for i, t in enumerate(ffn_toks):
         ns = []
         for l, L in enumerate(layers):
             g, u = (int(v) for v in cids[t, l])
             L.delta_assign(g, u, s.cuda_stream)
-            L.scatter_rows(s.cuda_stream)
-            ns.append(L.info()["n_active"])
-        # burst: all FFN launches back to back between two events
-        burst[0].record(s)
-        for l, L in enumerate(layers):
-            L.sparse_ffn(x[t, l].data_ptr(), y[t, l].data_ptr(), s.cuda_stream)
-        burst[1].record(s)
-        # the same launches again, each bracketed by its own events
-        for l, L in enumerate(layers):
-            ev[l][0].record(s)
-            L.sparse_ffn(x[t, l].data_ptr(), y[t, l].data_ptr(), s.cuda_stream)
-            ev[l][1].record(s)
-        s.synchronize()
-        burst_ms += burst[0].elapsed_time(burst[1])
-        per_launch_ms += sum(a.elapsed_time(b) for a, b in ev)
-        ffn_bytes += sum(n * c.bundle_bytes + 2 * c.d * 4 for n in ns)
-        launches += c.L
-    ffn_bytes_per_launch = ffn_bytes / launches
-    avg_burst_us = burst_ms * 1e3 / launches
-    avg_event_us = per_launch_ms * 1e3 / launches
+            info = L.info()
+            ns.append((info["n_active"], info["n_in"]))
+        if i % 2 == 0:
+            burst[0].record(s)
+            for l, L in enumerate(layers):
+                L.sparse_ffn(x[t, l].data_ptr(), y[t, l].data_ptr(), s.cuda_stream)
+            burst[1].record(s)
+            s.synchronize()
+            burst_ms += burst[0].elapsed_time(burst[1])
+            burst_bytes += sum((na + ni) * c.bundle_bytes + 2 * c.d * 4 for na, ni in ns)
+            burst_act_bytes += sum(na * c.bundle_bytes for na, _ in ns)
+            burst_n += c.L
+        else:
+            for l, L in enumerate(layers):
+                ev[l][0].record(s)
+                L.sparse_ffn(x[t, l].data_ptr(), y[t, l].data_ptr(), s.cuda_stream)
+                ev[l][1].record(s)
+            s.synchronize()
+            event_ms += sum(a.elapsed_time(b) for a, b in ev)
+            event_n += c.L
+    ffn_bytes_per_launch = burst_bytes / burst_n
+    act_bytes_per_launch = burst_act_bytes / burst_n
+    avg_burst_us = burst_ms * 1e3 / burst_n
+    avg_event_us = event_ms * 1e3 / max(event_n, 1)
     achieved = ffn_bytes_per_launch / (avg_burst_us * 1e-6) / 1e9
-    log(f"k_sparse_ffn: {ffn_bytes_per_launch / 1e6:.2f} MB/launch, {avg_burst_us:.2f} us/launch "
+    log(f"k_sparse_ffn (read-through): {ffn_bytes_per_launch / 1e6:.2f} MB/launch "
+        f"({act_bytes_per_launch / 1e6:.2f} MB active rows), {avg_burst_us:.2f} us/launch "
         f"(back-to-back), {avg_event_us:.2f} us (own events) -> {achieved:.0f} GB/s")
     traffic, traffic_note = stored_traffic(ffn_bytes_per_launch)
 
@@ -301,11 +314,15 @@ def main():
         "mean_delta_per_layer": in_bundles / (args.steps * c.L),
         "cold_start_ms": cold_ms,
         "host_enqueue_ms_per_step": enqueued * 1e3 / args.steps,
+        "decode_launches": "one by one" if args.direct else "captured graph replay",
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": "k_sparse_ffn", "bytes_per_launch": ffn_bytes_per_launch,
+                     "active_row_bytes_per_launch": act_bytes_per_launch,
+                     "active_row_gbps": act_bytes_per_launch / (avg_burst_us * 1e-6) / 1e9,
                      "avg_launch_us": avg_burst_us, "avg_launch_us_own_events": avg_event_us,
-                     "timing": "HIP events on the launch stream around back-to-back launches of the 31 layers",
+                     "timing": "HIP events on the launch stream around back-to-back launches of the 31 layers, "
+                               "each right after its layer's delta assignment (read-through of the new bundles)",
                      "traffic_note": traffic_note},
         "hbm_read_probe_gbps": probe_gbps,
         "hbm_copy_probe_gbps": copy_gbps,

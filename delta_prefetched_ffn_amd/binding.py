@@ -184,7 +184,7 @@ def decode_step(layers, cids: np.ndarray, x_ptr: int, y_ptr: int, compute_stream
 
 
 def decode_use_graphs(enable: bool) -> None:
-    """np_decode_use_graphs: replay decode steps as captured HIP graphs (default) or launch one by one."""
+    """np_decode_use_graphs: replay decode steps as captured HIP graphs, or launch one by one (default)."""
     _check(lib().np_decode_use_graphs(1 if enable else 0))
 
 

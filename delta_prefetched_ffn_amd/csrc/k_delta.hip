@@ -63,27 +63,37 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
     __shared__ int s_err;
 
     const LayerDev L = *a.layers[blockIdx.x];
+    auto* const owner = gmem(L.owner);
+    auto* const slot_map = gmem(L.slot_map);
+    auto* const d_in = gmem(L.d_in);
+    auto* const slot_in = gmem(L.slot_in);
+    auto* const d_out = gmem(L.d_out);
+    auto* const act = gmem(L.act);
+    auto* const act_src = gmem(L.act_src);
+    auto* const res = gmem(L.res);
+    auto* const freeb = gmem(L.freeb);
+    auto* const counts = gmem(L.counts);
     const int tid = threadIdx.x;
     if (tid == 0) s_err = 0;
-    const int32_t cg = a.prm ? a.prm->cid[a.layer0 + blockIdx.x][0] : a.cid[blockIdx.x][0];
-    const int32_t cu = a.prm ? a.prm->cid[a.layer0 + blockIdx.x][1] : a.cid[blockIdx.x][1];
+    const int32_t cg = a.prm ? gmem(a.prm)->cid[a.layer0 + blockIdx.x][0] : a.cid[blockIdx.x][0];
+    const int32_t cu = a.prm ? gmem(a.prm)->cid[a.layer0 + blockIdx.x][1] : a.cid[blockIdx.x][1];
 
     // Step 1: active set S from the selected gate/up masks; R from the resident bits. The
     // owner table (slot -> neuron) is read in the same round trip: it drives the release.
-    const uint64_t* ma = L.masks + (size_t)cg * L.W;
-    const uint64_t* mb = L.masks + ((size_t)(L.n_tables - 1) * L.C + cu) * L.W;
+    const auto* ma = gmem(L.masks) + (size_t)cg * L.W;
+    const auto* mb = gmem(L.masks) + ((size_t)(L.n_tables - 1) * L.C + cu) * L.W;
     int own[kOwnRegs];
 #pragma unroll
     for (int k = 0; k < kOwnRegs; ++k) {
         const int sl = tid + k * kNT;
-        own[k] = sl < L.K ? L.owner[sl] : -1;
+        own[k] = sl < L.K ? owner[sl] : -1;
     }
     for (int w = tid; w < L.W; w += kNT) {
         const uint64_t ga = ma[w], gb = mb[w];
         s_S[w] = L.mode == 0 ? (ga | gb) : L.mode == 1 ? (ga & gb) : ga;
-        s_R[w] = L.res[w];
+        s_R[w] = res[w];
     }
-    for (int v = tid; v < L.Kw; v += kNT) s_Fa[v] = s_F0[v] = L.freeb[v];
+    for (int v = tid; v < L.Kw; v += kNT) s_Fa[v] = s_F0[v] = freeb[v];
     __syncthreads();
 
     // Step 2: |D_in| and |D_out| per contiguous word range, scanned for list offsets;
@@ -103,7 +113,7 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
         for (int w = w0; w < w1; ++w) {
             uint64_t bits = s_R[w] & ~s_S[w];
             while (bits) {
-                L.d_out[k++] = w * 64 + (__ffsll((unsigned long long)bits) - 1);
+                d_out[k++] = w * 64 + (__ffsll((unsigned long long)bits) - 1);
                 bits &= bits - 1;
             }
         }
@@ -124,14 +134,14 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
             return 0;
         }
         if (s_S[n >> 6] & bit) return 0;  // stays resident
-        L.slot_map[n] = -1;
+        slot_map[n] = -1;
         atomicOr((unsigned long long*)&s_F0[sl >> 6], 1ull << (sl & 63));
         return 1;
     };
     int c_rel = 0;
 #pragma unroll
     for (int k = 0; k < kOwnRegs; ++k) c_rel += release(tid + k * kNT, own[k]);
-    for (int sl = tid + kOwnRegs * kNT; sl < L.K; sl += kNT) c_rel += release(sl, L.owner[sl]);
+    for (int sl = tid + kOwnRegs * kNT; sl < L.K; sl += kNT) c_rel += release(sl, owner[sl]);
     int n_rel;
     (void)block_excl_scan(c_rel, &n_rel, s_tmp);  // also orders the releases before what follows
     if (tid == 0 && n_rel != n_out) atomicOr(&s_err, kErrBadList);
@@ -155,10 +165,10 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
         const int take = min(max(n_in - s_fpre[v], 0), __popcll(s_F0[v]));
         const uint64_t fw = drop_low_bits(s_F0[v], take);
         s_F1[v] = fw;
-        L.freeb[v] = fw;
+        freeb[v] = fw;
         uint64_t gone = s_F0[v] & ~s_Fa[v] & fw;  // released and not taken again: no owner
         while (gone) {
-            L.owner[v * 64 + __ffsll((unsigned long long)gone) - 1] = -1;
+            owner[v * 64 + __ffsll((unsigned long long)gone) - 1] = -1;
             gone &= gone - 1;
         }
         const uint64_t valid = (v == L.Kw - 1 && (L.K & 63)) ? ((1ull << (L.K & 63)) - 1) : ~0ull;
@@ -199,11 +209,11 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
                 const int slot = lo * 64 + (__ffsll((unsigned long long)fw) - 1);
                 const uint64_t below = (1ull << (slot & 63)) - 1;
                 const int pos = s_opre[lo] + __popcll(~s_F1[lo] & below);
-                L.d_in[idx] = n;
-                L.slot_in[idx] = slot;
-                L.slot_map[n] = slot;
-                L.owner[slot] = n;
-                L.act_src[pos] = n;
+                d_in[idx] = n;
+                slot_in[idx] = slot;
+                slot_map[n] = slot;
+                owner[slot] = n;
+                act_src[pos] = n;
             }
         }
     }
@@ -216,19 +226,19 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
         while (occ) {
             const int b = __ffsll((unsigned long long)occ) - 1;
             occ &= occ - 1;
-            L.act[o] = v * 64 + b;
-            if (!((taken >> b) & 1)) L.act_src[o] = -1;
+            act[o] = v * 64 + b;
+            if (!((taken >> b) & 1)) act_src[o] = -1;
             ++o;
         }
     }
 
     // Step 5: R = S.
-    for (int w = tid; w < L.W; w += kNT) L.res[w] = s_S[w];
+    for (int w = tid; w < L.W; w += kNT) res[w] = s_S[w];
     __syncthreads();
     if (tid == 0) {
-        L.counts[0] = n_in;
-        L.counts[1] = n_out;
-        L.counts[2] = n_act;
+        counts[0] = n_in;
+        counts[1] = n_out;
+        counts[2] = n_act;
         if (s_err) atomicOr(&L.counts[3], s_err);
     }
 }

@@ -49,16 +49,19 @@ constexpr uint32_t kSpinLimit = 1u << 20;
 __device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-__device__ inline float dot8(const uint4 v, const float* xv) {
+typedef float fv4 __attribute__((ext_vector_type(4)));
+
+// Dot product of 8 bf16 weights with 8 fp32 x values (lo: x[0..3], hi: x[4..7]).
+__device__ inline float dot8(const uint4 v, const fv4 lo, const fv4 hi) {
     float a = 0.f;
-    a = fmaf(bf_lo(v.x), xv[0], a);
-    a = fmaf(bf_hi(v.x), xv[1], a);
-    a = fmaf(bf_lo(v.y), xv[2], a);
-    a = fmaf(bf_hi(v.y), xv[3], a);
-    a = fmaf(bf_lo(v.z), xv[4], a);
-    a = fmaf(bf_hi(v.z), xv[5], a);
-    a = fmaf(bf_lo(v.w), xv[6], a);
-    a = fmaf(bf_hi(v.w), xv[7], a);
+    a = fmaf(bf_lo(v.x), lo.x, a);
+    a = fmaf(bf_hi(v.x), lo.y, a);
+    a = fmaf(bf_lo(v.y), lo.z, a);
+    a = fmaf(bf_hi(v.y), lo.w, a);
+    a = fmaf(bf_lo(v.z), hi.x, a);
+    a = fmaf(bf_hi(v.z), hi.y, a);
+    a = fmaf(bf_lo(v.w), hi.z, a);
+    a = fmaf(bf_hi(v.w), hi.w, a);
     return a;
 }
 
@@ -78,7 +81,13 @@ __device__ inline void axpy8(float* acc, const float h, const uint4 v) {
 // Every load is then an unconditional instruction, so the compiler can wait for exactly
 // the loads a computation needs.
 __device__ inline uint4 gload(const char* p) { return *reinterpret_cast<const uint4*>(p); }
-__device__ inline void gstore(char* p, const uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+// Read-through stores of new rows are streaming (non-temporal): nothing in this launch reads
+// them again, and they should not sit dirty in the L2 when the launch ends.
+__device__ inline void gstore(char* p, const uint4 v) {
+    typedef uint32_t uv4 __attribute__((ext_vector_type(4)));
+    uv4 t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, (NP_GLOBAL uv4*)p);
+}
 
 __device__ inline uint64_t ld_pair(const uint64_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -90,27 +99,6 @@ __device__ inline void st_pair(uint64_t* p, uint32_t seq, float v) {
 __device__ inline uint32_t pair_seq(uint64_t p) { return (uint32_t)p; }
 __device__ inline float pair_val(uint64_t p) { return __uint_as_float((uint32_t)(p >> 32)); }
 
-// One wave waits until the words addr(k), k < count, all carry this launch's sequence
-// number: each lane watches one word, the wave votes, and it sleeps between polls. A
-// waiting workgroup so costs one 8-byte load per producer per poll, not one per value:
-// polling must not compete with the bulk row traffic. Returns false at the poll limit.
-template <typename AddrFn>
-__device__ inline bool wave_wait(AddrFn addr, int count, uint32_t seq) {
-    const int lane = threadIdx.x & 63;
-    for (int k0 = 0; k0 < count; k0 += 64) {
-        const int k = k0 + lane;
-        const uint64_t* p = k < count ? addr(k) : nullptr;
-        bool ready = p == nullptr;
-        for (uint32_t it = 0;; ++it) {
-            if (!ready) ready = pair_seq(ld_pair(p)) == seq;
-            if (__all(ready)) break;
-            if (it >= kSpinLimit) return false;
-            __builtin_amdgcn_s_sleep(4);
-        }
-    }
-    return true;
-}
-
 // NT threads; JX 16-byte x chunks per lane; SB slots per phase-1 batch per row lane;
 // U2 down rows per lane per phase-2 batch.
 template <int NT, int JX, bool GATED, int SB, int U2>
@@ -121,6 +109,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
 
     __shared__ int s_act[kWinMax];
     __shared__ int s_src[kWinMax];  // read-through: neuron whose bundle is in the row store, else -1
+    __shared__ float s_h[kWinMax];  // h of the window positions
     __shared__ float s_red1[kWaves * SB * NR1];  // wave sums of the gate/up dot products
     __shared__ float s_red2[NT * 8];
 
@@ -128,29 +117,13 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     const int d = a.d, cpr = d >> 3;
     // In a replayed decode step the per-token values come from the parameter block.
     const uint32_t seq = a.prm ? a.prm->seq[a.layer] : a.seq;
-    const float* xg = a.prm ? a.prm->x + (size_t)a.layer * a.d : a.x;
+    const auto* xg = gmem(a.prm ? a.prm->x + (size_t)a.layer * a.d : a.x);
 
     // Phase-1 lane geometry: CL lanes share a row (power of two), RL row lanes.
     int CL = NT;
     while (CL > cpr && CL > 1) CL >>= 1;
     const int RL = NT / CL;
     const int rl = tid / CL, cl = tid % CL;
-
-    // x for this lane's fixed column chunks (only workgroups with gate/up work need it).
-    float xv[JX][8];
-#pragma unroll
-    for (int j = 0; j < JX; ++j) {
-        const int c = cl + CL * j;
-        if (w < a.p1 && c < cpr) {
-            const float4 p = reinterpret_cast<const float4*>(xg)[2 * c];
-            const float4 q = reinterpret_cast<const float4*>(xg)[2 * c + 1];
-            xv[j][0] = p.x; xv[j][1] = p.y; xv[j][2] = p.z; xv[j][3] = p.w;
-            xv[j][4] = q.x; xv[j][5] = q.y; xv[j][6] = q.z; xv[j][7] = q.w;
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) xv[j][e] = 0.f;
-        }
-    }
 
     // |S| comes from the host (it validated the capacity with it); the device count,
     // read in parallel, is only checked against it.
@@ -169,35 +142,46 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
         phi = plo + kWinMax;
     }
     const int wn = phi - plo;
-    {
-        constexpr int kStage = (kWinMax + NT - 1) / NT;
-        int v[kStage], u[kStage];
+
+    // The slot list of the window and its sources: unconditional loads (clamped indexes,
+    // values selected afterwards), so that staging waits for exactly these loads.
+    constexpr int kStage = (kWinMax + NT - 1) / NT;
+    const bool rt = a.read_through != 0;
+    int sv[kStage], su[kStage];
 #pragma unroll
-        for (int k = 0; k < kStage; ++k) {
-            const int i = tid + k * NT;
-            v[k] = i < wn ? a.act[plo + i] : 0;
-            u[k] = (a.act_src && i < wn) ? a.act_src[plo + i] : -1;
-        }
+    for (int k = 0; k < kStage; ++k) {
+        const int i = min(plo + tid + k * NT, a.K - 1);
+        sv[k] = a.act[i];
+        su[k] = a.act_src[i];
+    }
 #pragma unroll
-        for (int k = 0; k < kStage; ++k) {
-            const int i = tid + k * NT;
-            const bool bad = (unsigned)v[k] >= (unsigned)a.K;
-            const bool badsrc = u[k] >= a.M;
+    for (int k = 0; k < kStage; ++k) {
+        const int i = tid + k * NT;
+        const int u = rt ? su[k] : -1;
+        const bool bad = (unsigned)sv[k] >= (unsigned)a.K;
+        const bool badsrc = u >= a.M;
+        if (i < wn) {
             err |= (bad || badsrc) ? kErrBadList : 0;
-            if (i < wn) {
-                s_act[i] = bad ? 0 : v[k];
-                s_src[i] = (bad || badsrc || u[k] < 0) ? -1 : u[k];
-            }
+            s_act[i] = bad ? 0 : sv[k];
+            s_src[i] = (bad || badsrc || u < 0) ? -1 : u;
         }
     }
     __syncthreads();
+
+    // x for this lane's fixed column chunks (needed only once the rows arrive)
+    fv4 xr[JX][2];
+#pragma unroll
+    for (int j = 0; j < JX; ++j) {
+        const int c = min(cl + CL * j, cpr - 1);
+        xr[j][0] = reinterpret_cast<const NP_GLOBAL fv4*>(xg)[2 * c];
+        xr[j][1] = reinterpret_cast<const NP_GLOBAL fv4*>(xg)[2 * c + 1];
+    }
 
     // ---------------- phase 1 loads: gate/up rows of chunk w (issued first) ----------------
     const size_t slot_bytes = (size_t)R * cpr * 16u;
     const char* const buf_c = reinterpret_cast<const char*>(a.buf);
     char* const buf_w = reinterpret_cast<char*>(a.buf);
     const char* const store_c = reinterpret_cast<const char*>(a.store);
-    const bool rt = a.act_src != nullptr;
     // Start of the bundle at window position p: its slot, or the row store for a slot
     // filled this step (read-through).
     auto row_base = [&](int p) -> const char* {
@@ -250,7 +234,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
                 float acc = 0.f;
 #pragma unroll
                 for (int j = 0; j < JX; ++j)
-                    if (cl + CL * j < cpr) acc += dot8(wv[i][r][j], xv[j]);
+                    if (cl + CL * j < cpr) acc += dot8(wv[i][r][j], xr[j][0], xr[j][1]);
                 v[i * NR1 + r] = acc;
             }
         if (CL >= 64) {
@@ -286,6 +270,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
                     }
                     const float h = GATED ? fmaxf(g[0], 0.f) * g[1] : fmaxf(g[0], 0.f);
                     st_pair(&a.hpair[pos], seq, h);
+                    s_h[pos - plo] = h;
                 }
             }
         } else {
@@ -300,6 +285,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
                     if (pos < c1) {
                         const float h = GATED ? fmaxf(v[i * NR1], 0.f) * v[i * NR1 + NR1 - 1] : fmaxf(v[i], 0.f);
                         st_pair(&a.hpair[pos], seq, h);
+                        s_h[pos - plo] = h;
                     }
                 }
             }
@@ -334,52 +320,42 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     }
 
     // ---------------- phase 2: down tile t over the window ----------------
-    // The other chunks of the window belong to lower workgroup IDs. Wave 0 watches the last
-    // h of each of them; the whole workgroup then reads its h values once.
+    // The window's other chunks belong to lower workgroup IDs: their h words are polled, one
+    // word per thread, until they carry this launch's sequence number, and go into LDS next
+    // to this workgroup's own h (if any), so the down rows then take h from LDS.
     {
-        const int others = has1 ? w - wlo : whi - wlo + 1;  // chunks wlo .. wlo + others - 1
-        bool ok = true;
-        if (wave == 0)
-            ok = wave_wait(
-                [&](int k) -> const uint64_t* {
-                    const int c = wlo + k;
-                    const int e = cbeg(c + 1);
-                    return e > cbeg(c) ? &a.hpair[e - 1] : nullptr;
-                },
-                others, seq);
-        if (!ok) err |= kErrSpin;
+        const int n_other = (has1 ? c0 : phi) - plo;  // positions plo .. plo + n_other - 1
+        uint64_t hp[kStage];
+#pragma unroll
+        for (int k = 0; k < kStage; ++k) hp[k] = ld_pair(&a.hpair[min(plo + tid + k * NT, a.K - 1)]);
+        for (uint32_t it = 0;; ++it) {
+            bool ready = true;
+#pragma unroll
+            for (int k = 0; k < kStage; ++k) ready &= tid + k * NT >= n_other || pair_seq(hp[k]) == seq;
+            if (ready) break;
+            if (it >= kSpinLimit) {
+                err |= kErrSpin;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+            for (int k = 0; k < kStage; ++k)
+                if (tid + k * NT < n_other && pair_seq(hp[k]) != seq) hp[k] = ld_pair(&a.hpair[plo + tid + k * NT]);
+        }
+#pragma unroll
+        for (int k = 0; k < kStage; ++k)
+            if (tid + k * NT < n_other) s_h[tid + k * NT] = pair_val(hp[k]);
         __syncthreads();
     }
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     for (int i0 = r2;;) {
-        uint64_t hp[U2];
-#pragma unroll
-        for (int u = 0; u < U2; ++u) {
-            const int i = i0 + u * RL2;
-            hp[u] = (cok && i < wn) ? ld_pair(&a.hpair[plo + i]) : (uint64_t)seq;
-        }
-        // a value stored just before its chunk's watched word may still be in flight
-        for (uint32_t it = 0;; ++it) {
-            bool ready = true;
-#pragma unroll
-            for (int u = 0; u < U2; ++u) ready &= pair_seq(hp[u]) == seq;
-            if (ready) break;
-            if (it >= kSpinLimit) {
-                err |= kErrSpin;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(4);
-#pragma unroll
-            for (int u = 0; u < U2; ++u)
-                if (pair_seq(hp[u]) != seq) hp[u] = ld_pair(&a.hpair[plo + i0 + u * RL2]);
-        }
 #pragma unroll
         for (int u = 0; u < U2; ++u) {
             const int i = i0 + u * RL2;
             if (cok && i < wn) {
-                axpy8(acc, pair_val(hp[u]), dv[u]);
+                axpy8(acc, s_h[i], dv[u]);
                 // read-through: this tile's piece of the down row goes into its slot
                 if (rt && s_src[i] >= 0) gstore(buf_w + (size_t)s_act[i] * slot_bytes + dcol, dv[u]);
             }
@@ -409,13 +385,8 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
         // The tile's highest contributor sums the other contributors' partials: G groups of
         // threads per column each take contributors g, g + G, ... (ascending), then the group
         // sums and this workgroup's own partial are added in a fixed order.
-        // Wave 0 watches the last column of every other contributor, then all threads load.
-        bool ok = true;
-        if (wave == 0)
-            ok = wave_wait([&](int k) -> const uint64_t* { return &a.ppair[(size_t)(t + k * a.q) * a.tw + tcols - 1]; },
-                           ncontrib - 1, seq);
-        if (!ok) err |= kErrSpin;
-        __syncthreads();                      // also: s_red2 is reused for the group sums
+        // Every thread polls the partial words it sums.
+        __syncthreads();                      // s_red2 is reused for the group sums
         const int G = NT / a.tw;
         const int j = tid % a.tw, g = tid / a.tw;
         constexpr int kB = 8;
@@ -453,7 +424,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
         if (tid < tcols) {
             float yv = 0.f;
             for (int gg = 0; gg < G; ++gg) yv += s_red2[gg * a.tw + tid];
-            float* yg = a.prm ? a.prm->y + (size_t)a.layer * a.d : a.y;
+            auto* yg = gmem(a.prm ? a.prm->y + (size_t)a.layer * a.d : a.y);
             yg[col0 + tid] = yv + own;
         }
     }

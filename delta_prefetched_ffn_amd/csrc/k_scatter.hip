@@ -46,27 +46,29 @@ __global__ __launch_bounds__(kNT) void k_scatter_rows(int32_t* counts, const int
 // that layer's incoming bundles.
 __global__ __launch_bounds__(kNT) void k_scatter_all(ScatterLaunch a) {
     const LayerDev* L = a.layers[blockIdx.y];
-    int32_t* counts = L->counts;
     const int M = L->M, K = L->K, cb = L->bundle16;
-    const int n_in = min(counts[0], K);  // the lists hold at most K entries
-    const uint4* store = reinterpret_cast<const uint4*>(L->store);
-    uint4* buf = reinterpret_cast<uint4*>(L->buf);
+    const int n_in = min(gmem(L->counts)[0], K);  // the lists hold at most K entries
+    const auto* store = gmem(reinterpret_cast<const uint4*>(L->store));
+    auto* buf = gmem(reinterpret_cast<uint4*>(L->buf));
+    const auto* d_in = gmem(L->d_in);
+    const auto* slot_in = gmem(L->slot_in);
     for (int i = blockIdx.x; i < n_in; i += gridDim.x) {
-        const int n = L->d_in[i], s = L->slot_in[i];
+        const int n = d_in[i], s = slot_in[i];
         if ((unsigned)n >= (unsigned)M || (unsigned)s >= (unsigned)K) {
-            if (threadIdx.x == 0) atomicOr(&counts[3], kErrBadList);
+            if (threadIdx.x == 0) atomicOr(&L->counts[3], kErrBadList);
             continue;
         }
-        const uint4* src = store + (size_t)n * cb;
-        uint4* dst = buf + (size_t)s * cb;
+        const auto* src = store + (size_t)n * cb;
+        auto* dst = buf + (size_t)s * cb;
         for (int c = threadIdx.x; c < cb; c += kNT * kU) {
-            uint4 v[kU];
+            typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+            u4 v[kU];
 #pragma unroll
             for (int u = 0; u < kU; ++u)
-                if (c + u * kNT < cb) v[u] = src[c + u * kNT];
+                if (c + u * kNT < cb) v[u] = reinterpret_cast<const NP_GLOBAL u4*>(src)[c + u * kNT];
 #pragma unroll
             for (int u = 0; u < kU; ++u)
-                if (c + u * kNT < cb) dst[c + u * kNT] = v[u];
+                if (c + u * kNT < cb) reinterpret_cast<NP_GLOBAL u4*>(dst)[c + u * kNT] = v[u];
         }
     }
 }

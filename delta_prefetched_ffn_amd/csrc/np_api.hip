@@ -248,8 +248,9 @@ np_status enqueue_ffn(np_layer* L, const float* x, float* y, hipStream_t s, cons
     FfnArgs a{};
     a.buf = L->buf;
     a.act = L->act();
-    a.act_src = read_through ? L->act_src() : nullptr;
-    a.store = read_through ? L->store_dev : nullptr;
+    a.act_src = L->act_src();
+    a.store = L->store_dev;
+    a.read_through = read_through ? 1 : 0;
     a.counts = L->counts;
     a.x = x;
     a.y = y;
@@ -386,7 +387,7 @@ struct DecodePlan {
 
 std::mutex g_plan_mu;
 std::vector<std::unique_ptr<DecodePlan>> g_plans;  // most recently used last
-std::atomic<int> g_use_graphs{1};
+std::atomic<int> g_use_graphs{0};
 constexpr size_t kMaxPlans = 8;
 
 void drop_plans_with(const np_layer* L) {
@@ -705,9 +706,15 @@ np_status np_scatter_rows(np_layer* L, void* stream) {
 np_status np_sparse_ffn(np_layer* L, const float* x, float* y, void* stream) {
     if (!L) return fail(NP_EINVAL, "layer must not be NULL");
     if (!x || !y || !aligned16(x) || !aligned16(y)) return fail(NP_EINVAL, "x and y must be 16-byte aligned device pointers");
-    if (L->state != kScattered) return fail(NP_ESTATE, "np_sparse_ffn needs the last delta scattered");
+    if (L->state == kFresh) return fail(NP_ESTATE, "np_sparse_ffn needs a preceding np_delta_assign");
+    const bool read_through = L->state == kAssigned;
+    if (read_through && L->store_is_host)
+        return fail(NP_ESTATE, "the row store is host memory: call np_scatter_rows before np_sparse_ffn");
     DeviceGuard g(L->desc.device);
-    return enqueue_ffn(L, x, y, (hipStream_t)stream);
+    np_status st = enqueue_ffn(L, x, y, (hipStream_t)stream, nullptr, 0, read_through);
+    if (st != NP_OK) return st;
+    L->state = kScattered;
+    return NP_OK;
 }
 
 np_status np_decode_step(np_layer* const* layers, int32_t n_layers, const int32_t* cids, const float* x,

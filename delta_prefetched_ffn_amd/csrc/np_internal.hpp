@@ -91,10 +91,11 @@ struct FfnShape {
 struct FfnArgs {
     uint16_t* buf;          // [K][R][d]
     const int32_t* act;     // [K]
-    // Read-through (null: off): bundles of slots filled this step are read from the row
-    // store (act_src gives the neuron) and written into their slots by this launch.
-    const int32_t* act_src; // [K]
+    // Read-through (read_through != 0): bundles of slots filled this step are read from the
+    // row store (act_src gives the neuron) and written into their slots by this launch.
+    const int32_t* act_src; // [K] (always a valid array)
     const uint16_t* store;  // [M][R][d]
+    int32_t read_through;
     int32_t* counts;        // [4]
     const float* x;         // [d]
     float* y;               // [d]
@@ -108,6 +109,15 @@ struct FfnArgs {
     int32_t d, K, R, M;
     int32_t p1, q, tw, nwg;
 };
+
+// Device code: view a pointer read from memory as a global-memory pointer. Without it the
+// compiler must use flat accesses, which share a wait counter with LDS, so every LDS wait
+// would also wait for outstanding global loads and stores.
+#define NP_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ inline NP_GLOBAL T* gmem(T* p) {
+    return (NP_GLOBAL T*)p;
+}
 
 // Launchers (return hipError_t from the launch).
 hipError_t launch_delta_assign(const DeltaLaunch& a, hipStream_t s);

@@ -126,7 +126,12 @@ np_status np_scatter_rows(np_layer* layer, void* stream);
  * down * act(gate . x) * (up . x), bf16 weights, fp32 arithmetic and
  * accumulation, fixed-order (run-to-run identical) reduction.
  * x and y are device fp32 [d_model], 16-byte aligned, not overlapping.
- * Errors: NP_ESTATE unless the last assignment has been scattered. */
+ * Called right after np_delta_assign (no np_scatter_rows) with a row store in
+ * device memory, it does step 4 itself: the bundles of the slots filled by
+ * that assignment are read from the row store and written into their slots
+ * by the same launch (read-through), with the same y and buffer contents.
+ * Errors: NP_ESTATE before the first np_delta_assign, or after an
+ * unscattered assignment when the row store is host memory. */
 np_status np_sparse_ffn(np_layer* layer, const float* x, float* y, void* stream);
 
 /* One decode token over n_layers layers of one device with equal d_model
@@ -146,15 +151,17 @@ np_status np_sparse_ffn(np_layer* layer, const float* x, float* y, void* stream)
 np_status np_decode_step(np_layer* const* layers, int32_t n_layers, const int32_t* cids,
                          const float* x, float* y, void* compute_stream, void* copy_stream);
 
-/* Process-wide switch for np_decode_step. 1 (the default): the first call for a
- * given (layer set, compute stream, copy stream) captures the step's launches
- * into a HIP graph; every call then writes that token's centroid IDs, x and y
- * pointers into a small device parameter block with one kernel launch and
- * replays the graph on compute_stream, so a token costs two host calls instead
- * of several per layer. The graph is rebuilt when a layer is reset, reshaped or
- * destroyed. Streams must be non-NULL for the graph path (otherwise, and if
- * capture fails, the launches are issued one by one). 0: always issue the
- * launches one by one. Results are the same either way. */
+/* Process-wide switch for np_decode_step. 0 (the default): the launches are
+ * issued one by one. 1: the first call for a given (layer set, compute
+ * stream, copy stream) captures the step's launches into a HIP graph; every
+ * call then writes that token's centroid IDs, x and y pointers into a small
+ * device parameter block with one kernel launch and replays the graph on
+ * compute_stream, so a token costs two host calls instead of one per layer
+ * (for callers whose host thread is the bottleneck; on the GPU the extra
+ * parameter launch makes a step slightly longer). The graph is rebuilt when a
+ * layer is reset, reshaped or destroyed. Streams must be non-NULL for the
+ * graph path (otherwise, and if capture fails, the launches are issued one by
+ * one). Results are the same either way. */
 np_status np_decode_use_graphs(int32_t enable);
 
 /* Synchronizes the layer's device, then copies the current state to host

@@ -126,3 +126,35 @@ def test_reset_gives_a_cold_start(env):
     st = layer.read_state()
     assert st["slot_in"].tolist() == list(range(64))
     assert st["d_out"].size == 0
+
+
+def test_read_through_needs_a_device_store(env):
+    """np_sparse_ffn right after np_delta_assign reads the new bundles through only from a
+    device-memory row store; with a pinned-host store it refuses (NP_ESTATE) and the layer
+    still accepts np_scatter_rows."""
+    torch, B, layer, store, masks, dev = env
+    host = upload_store(store, "host")
+    hl = B.Layer(d_model=d, d_ff=M, k_max=K, n_rows=R, masks=masks, mask_mode=B.MASK_UNION,
+                 row_store=host.data_ptr(), keepalive=host)
+    s = torch.cuda.current_stream().cuda_stream
+    x = torch.ones(d, device="cuda")
+    y = torch.zeros(d, device="cuda")
+    hl.delta_assign(0, 0, s)
+    with pytest.raises(B.NPError) as e:
+        hl.sparse_ffn(x.data_ptr(), y.data_ptr(), s)
+    assert e.value.status == B.NP_ESTATE
+    hl.scatter_rows(s)
+    hl.sparse_ffn(x.data_ptr(), y.data_ptr(), s)
+    layer.delta_assign(0, 0, s)
+    layer.sparse_ffn(x.data_ptr(), y.data_ptr(), s)      # read-through
+    with pytest.raises(B.NPError) as e:
+        layer.scatter_rows(s)                              # already in the buffer
+    assert e.value.status == B.NP_ESTATE
+    torch.cuda.synchronize()
+    ol = O.OracleLayer(M, K, R, d)
+    res = ol.step(np.arange(64, dtype=np.int32))
+    ol.copy_bundles(store, res)
+    for L in (hl, layer):
+        compare_state(L.read_state(), ol, res, np.arange(64), "first")
+        assert np.array_equal(L.read_rows(), ol.buf)
+    hl.close()

@@ -62,7 +62,7 @@ SMALL = [
 
 
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: f"d{c.d}_M{c.M}_K{c.K}_{c.mode}_R{c.R}")
-@pytest.mark.parametrize("streams,graphs", [(1, True), (2, True), (2, False)])
+@pytest.mark.parametrize("streams,graphs", [(1, True), (1, False), (2, True), (2, False)])
 def test_small_shapes_decode_step(torch, cfg, streams, graphs):
     from delta_prefetched_ffn_amd import binding as B
     B.decode_use_graphs(graphs)
@@ -90,7 +90,7 @@ def test_small_shapes_decode_step(torch, cfg, streams, graphs):
             check_y(yh[t, l], O.sparse_ffn(stores[l], cfg.R, cfg.d, S, x_all[t, l]), f"t={t} l={l}")
     for layer in layers:
         layer.close()
-    B.decode_use_graphs(True)
+    B.decode_use_graphs(False)  # the library default
 
 
 def _dyadic_store(rng, M, R, d):
@@ -142,19 +142,21 @@ def test_decode_paths_agree_and_repeat_bitwise(torch):
     wl = Workload(cfg)
     x_all = wl.x_all()
     x = torch.from_numpy(x_all).cuda()
-    outs = []
-    for path in ["two", "one", "calls", "two-direct", "one-direct", "two-host", "two-host-direct", "two"]:
+    outs, bufs = [], []
+    for path in ["two", "one", "calls", "calls-rt", "two-direct", "one-direct", "two-host", "two-host-direct",
+                 "two"]:
         B.decode_use_graphs(not path.endswith("direct"))
         where = "host" if "host" in path else "device"
         layers = [make_layer(wl, l, where)[0] for l in range(cfg.L)]
         y = torch.zeros_like(x)
         cs, ps = torch.cuda.Stream(), torch.cuda.Stream()
         for t in range(cfg.T):
-            if path == "calls":
+            if path.startswith("calls"):
                 for l, layer in enumerate(layers):
                     g, u = (int(v) for v in wl.cids()[t, l])
                     layer.delta_assign(g, u, cs.cuda_stream)
-                    layer.scatter_rows(cs.cuda_stream)
+                    if path == "calls":  # else the FFN reads the new bundles through
+                        layer.scatter_rows(cs.cuda_stream)
                     layer.sparse_ffn(x[t, l].data_ptr(), y[t, l].data_ptr(), cs.cuda_stream)
             else:
                 B.decode_step(layers, wl.cids()[t], x[t].data_ptr(), y[t].data_ptr(), cs.cuda_stream,
@@ -162,11 +164,14 @@ def test_decode_paths_agree_and_repeat_bitwise(torch):
         torch.cuda.synchronize()
         assert all(L.read_state()["err"] == 0 for L in layers)
         outs.append(y.cpu().numpy())
+        bufs.append(layers[-1].read_rows())
         for layer in layers:
             layer.close()
-    B.decode_use_graphs(True)
+    B.decode_use_graphs(False)  # the library default
     for o in outs[1:]:
         assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
+    for b in bufs[1:]:  # slot buffers, stale rows included
+        assert np.array_equal(b, bufs[0])
 
 
 def test_edge_cases_empty_full_turnover_and_exact_capacity(torch):

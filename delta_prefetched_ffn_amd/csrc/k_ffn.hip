@@ -80,7 +80,11 @@ __device__ inline void axpy8(float* acc, const float h, const uint4 v) {
 // reads a fixed valid address (the start of the slot buffer) and its value is not used.
 // Every load is then an unconditional instruction, so the compiler can wait for exactly
 // the loads a computation needs.
-__device__ inline uint4 gload(const char* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ inline uint4 gload(const char* p) {
+    typedef uint32_t uv4 __attribute__((ext_vector_type(4)));
+    const uv4 t = __builtin_nontemporal_load((const NP_GLOBAL uv4*)p);
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
 // Read-through stores of new rows are streaming (non-temporal): nothing in this launch reads
 // them again, and they should not sit dirty in the L2 when the launch ends.
 __device__ inline void gstore(char* p, const uint4 v) {

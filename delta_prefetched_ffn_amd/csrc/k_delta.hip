@@ -17,36 +17,63 @@ namespace {
 constexpr int kNT = 256;
 constexpr int kWaves = kNT / 64;
 
-// Exclusive scan of one int per thread over the workgroup; *total gets the sum.
-__device__ int block_excl_scan(int v, int* total, int* s_tmp) {
+// Exclusive scans of two ints per thread over the workgroup in one pass; *ta and *tb get
+// the sums.
+__device__ inline void block_excl_scan2(int va, int vb, int* ea, int* eb, int* ta, int* tb, int* s_tmp) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int x = v;
+    int xa = va, xb = vb;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        int y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
-    if (lane == 63) s_tmp[wave] = x;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int acc = 0;
-        for (int w = 0; w < kWaves; ++w) {
-            int t = s_tmp[w];
-            s_tmp[w] = acc;
-            acc += t;
+        const int ya = __shfl_up(xa, off, 64), yb = __shfl_up(xb, off, 64);
+        if (lane >= off) {
+            xa += ya;
+            xb += yb;
         }
-        s_tmp[kWaves] = acc;
+    }
+    if (lane == 63) {
+        s_tmp[2 * wave] = xa;
+        s_tmp[2 * wave + 1] = xb;
     }
     __syncthreads();
-    const int res = s_tmp[wave] + x - v;
-    *total = s_tmp[kWaves];
-    __syncthreads();
-    return res;
+    int pa = 0, pb = 0, sa = 0, sb = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const int wa = s_tmp[2 * w], wb = s_tmp[2 * w + 1];
+        if (w < wave) {
+            pa += wa;
+            pb += wb;
+        }
+        sa += wa;
+        sb += wb;
+    }
+    *ea = pa + xa - va;
+    *eb = pb + xb - vb;
+    *ta = sa;
+    *tb = sb;
+    __syncthreads();  // s_tmp may be reused right away
 }
 
+// w with its r lowest set bits removed (r >= popcount(w) gives 0): finds the r-th set bit
+// (0-based) by halving the word six times, then clears everything below it.
 __device__ inline uint64_t drop_low_bits(uint64_t w, int r) {
-    for (int j = 0; j < r; ++j) w &= w - 1;
-    return w;
+    if (r <= 0) return w;
+    if (r >= __popcll(w)) return 0;
+    int pos = 0;
+    uint64_t x = w;
+#pragma unroll
+    for (int sh = 32; sh > 0; sh >>= 1) {
+        const int c = __popcll(x & ((1ull << sh) - 1));
+        if (r >= c) {
+            r -= c;
+            x >>= sh;
+            pos += sh;
+        }
+    }
+    return w & ~((1ull << pos) - 1);
+}
+
+__device__ inline uint64_t valid_bits(int v, int Kw, int K) {
+    return (v == Kw - 1 && (K & 63)) ? ((1ull << (K & 63)) - 1) : ~0ull;
 }
 
 constexpr int kOwnRegs = 32;  // owner entries per thread loaded with the masks (K <= 8192 in one pass)
@@ -59,7 +86,7 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
     __shared__ uint64_t s_F1[kMaxKWords];  // free slots after the assignment
     __shared__ int s_fpre[kMaxKWords];     // exclusive prefix of |F0| per word
     __shared__ int s_opre[kMaxKWords];     // exclusive prefix of occupied slots per word
-    __shared__ int s_tmp[kWaves + 1];
+    __shared__ int s_tmp[2 * kWaves];
     __shared__ int s_err;
 
     const LayerDev L = *a.layers[blockIdx.x];
@@ -73,48 +100,49 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
     auto* const res = gmem(L.res);
     auto* const freeb = gmem(L.freeb);
     auto* const counts = gmem(L.counts);
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int M = L.M, K = L.K, W = L.W, Kw = L.Kw;
     if (tid == 0) s_err = 0;
     const int32_t cg = a.prm ? gmem(a.prm)->cid[a.layer0 + blockIdx.x][0] : a.cid[blockIdx.x][0];
     const int32_t cu = a.prm ? gmem(a.prm)->cid[a.layer0 + blockIdx.x][1] : a.cid[blockIdx.x][1];
 
     // Step 1: active set S from the selected gate/up masks; R from the resident bits. The
     // owner table (slot -> neuron) is read in the same round trip: it drives the release.
-    const auto* ma = gmem(L.masks) + (size_t)cg * L.W;
-    const auto* mb = gmem(L.masks) + ((size_t)(L.n_tables - 1) * L.C + cu) * L.W;
+    const auto* ma = gmem(L.masks) + (size_t)cg * W;
+    const auto* mb = gmem(L.masks) + ((size_t)(L.n_tables - 1) * L.C + cu) * W;
     int own[kOwnRegs];
 #pragma unroll
-    for (int k = 0; k < kOwnRegs; ++k) {
-        const int sl = tid + k * kNT;
-        own[k] = sl < L.K ? owner[sl] : -1;
-    }
-    for (int w = tid; w < L.W; w += kNT) {
+    for (int k = 0; k < kOwnRegs; ++k) own[k] = owner[min(tid + k * kNT, K - 1)];
+    for (int w = tid; w < W; w += kNT) {
         const uint64_t ga = ma[w], gb = mb[w];
         s_S[w] = L.mode == 0 ? (ga | gb) : L.mode == 1 ? (ga & gb) : ga;
         s_R[w] = res[w];
     }
-    for (int v = tid; v < L.Kw; v += kNT) s_Fa[v] = s_F0[v] = freeb[v];
+    for (int v = tid; v < Kw; v += kNT) s_Fa[v] = s_F0[v] = freeb[v];
     __syncthreads();
 
-    // Step 2: |D_in| and |D_out| per contiguous word range, scanned for list offsets;
-    // D_out is written in ascending order.
-    const int wpt = (L.W + kNT - 1) / kNT;
-    const int w0 = min(tid * wpt, L.W), w1 = min(w0 + wpt, L.W);
+    // Step 2: D_in = S \ R and D_out = R \ S in ascending order. Each thread takes a
+    // contiguous range of words (sparse in practice), a workgroup scan gives list offsets.
+    const int wpt = (W + kNT - 1) / kNT;
+    const int w0 = min(tid * wpt, W), w1 = min(w0 + wpt, W);
     int c_in = 0, c_out = 0;
     for (int w = w0; w < w1; ++w) {
         c_in += __popcll(s_S[w] & ~s_R[w]);
         c_out += __popcll(s_R[w] & ~s_S[w]);
     }
-    int n_in, n_out;
-    const int base_in = block_excl_scan(c_in, &n_in, s_tmp);
-    const int base_out = block_excl_scan(c_out, &n_out, s_tmp);
+    int base_in, base_out, n_in, n_out;
+    block_excl_scan2(c_in, c_out, &base_in, &base_out, &n_in, &n_out, s_tmp);
     {
-        int k = base_out;
+        int ki = base_in, ko = base_out;
         for (int w = w0; w < w1; ++w) {
-            uint64_t bits = s_R[w] & ~s_S[w];
-            while (bits) {
-                d_out[k++] = w * 64 + (__ffsll((unsigned long long)bits) - 1);
-                bits &= bits - 1;
+            uint64_t bi = s_S[w] & ~s_R[w], bo = s_R[w] & ~s_S[w];
+            while (bi) {
+                d_in[ki++] = w * 64 + (__ffsll((unsigned long long)bi) - 1);
+                bi &= bi - 1;
+            }
+            while (bo) {
+                d_out[ko++] = w * 64 + (__ffsll((unsigned long long)bo) - 1);
+                bo &= bo - 1;
             }
         }
     }
@@ -122,118 +150,142 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
     // Step 3: release the slots whose owner leaves the active set (slot map -1, free bit;
     // the owner entry is cleared below unless the slot is taken again). Every slot is
     // looked at once, so the owners of D_out are found without a slot-map lookup each.
-    auto release = [&](int sl, int n) {
-        if (n < 0) return 0;
-        if (n >= L.M) {
+    // (An owner that is not a resident neuron would be released too; the released count is
+    // checked against |D_out| below.)
+    auto leaves = [&](int sl, int n) -> bool {
+        if (sl >= K || n < 0) return false;
+        if (n >= M) {
             atomicOr(&s_err, kErrBadList);
-            return 0;
+            return false;
         }
-        const uint64_t bit = 1ull << (n & 63);
-        if ((s_R[n >> 6] & bit) == 0) {  // an owned slot must belong to a resident neuron
-            atomicOr(&s_err, kErrBadList);
-            return 0;
-        }
-        if (s_S[n >> 6] & bit) return 0;  // stays resident
-        slot_map[n] = -1;
-        atomicOr((unsigned long long*)&s_F0[sl >> 6], 1ull << (sl & 63));
-        return 1;
+        return (s_S[n >> 6] & (1ull << (n & 63))) == 0;
     };
     int c_rel = 0;
-#pragma unroll
-    for (int k = 0; k < kOwnRegs; ++k) c_rel += release(tid + k * kNT, own[k]);
-    for (int sl = tid + kOwnRegs * kNT; sl < L.K; sl += kNT) c_rel += release(sl, owner[sl]);
-    int n_rel;
-    (void)block_excl_scan(c_rel, &n_rel, s_tmp);  // also orders the releases before what follows
-    if (tid == 0 && n_rel != n_out) atomicOr(&s_err, kErrBadList);
-
-    // Free slots after the release: per-word prefix counts (ascending slot order).
-    const int kpt = (L.Kw + kNT - 1) / kNT;
-    const int v0 = min(tid * kpt, L.Kw), v1 = min(v0 + kpt, L.Kw);
-    int c_free = 0;
-    for (int v = v0; v < v1; ++v) c_free += __popcll(s_F0[v]);
-    int n_free;
     {
-        int pre = block_excl_scan(c_free, &n_free, s_tmp);
-        for (int v = v0; v < v1; ++v) {
-            s_fpre[v] = pre;
-            pre += __popcll(s_F0[v]);
+        bool lv[kOwnRegs];
+#pragma unroll
+        for (int k = 0; k < kOwnRegs; ++k) lv[k] = leaves(tid + k * kNT, own[k]);
+#pragma unroll
+        for (int k = 0; k < kOwnRegs; ++k) {
+            if (!lv[k]) continue;
+            const int sl = tid + k * kNT;
+            slot_map[own[k]] = -1;
+            atomicOr((unsigned long long*)&s_F0[sl >> 6], 1ull << (sl & 63));
+            ++c_rel;
+        }
+        for (int sl = tid + kOwnRegs * kNT; sl < K; sl += kNT) {
+            const int n = owner[sl];
+            if (!leaves(sl, n)) continue;
+            slot_map[n] = -1;
+            atomicOr((unsigned long long*)&s_F0[sl >> 6], 1ull << (sl & 63));
+            ++c_rel;
         }
     }
+
+    // Free slots after the release: per-word prefix counts (ascending slot order); the
+    // released count is checked against |D_out|.
+    const int kpt = (Kw + kNT - 1) / kNT;
+    const int v0 = min(tid * kpt, Kw), v1 = min(v0 + kpt, Kw);
+    __syncthreads();  // the releases' free bits are in s_F0
+    int c_free = 0;
+    for (int v = v0; v < v1; ++v) c_free += __popcll(s_F0[v]);
+    int pre_free, pre_rel, n_free, n_rel;
+    block_excl_scan2(c_free, c_rel, &pre_free, &pre_rel, &n_free, &n_rel, s_tmp);
+    if (tid == 0 && n_rel != n_out) atomicOr(&s_err, kErrBadList);
+
     // Step 4 (set part): the n_in lowest free slots are taken; occupied slots per word.
     int c_occ = 0;
     for (int v = v0; v < v1; ++v) {
-        const int take = min(max(n_in - s_fpre[v], 0), __popcll(s_F0[v]));
+        s_fpre[v] = pre_free;
+        const int take = min(max(n_in - pre_free, 0), __popcll(s_F0[v]));
+        pre_free += __popcll(s_F0[v]);
         const uint64_t fw = drop_low_bits(s_F0[v], take);
         s_F1[v] = fw;
         freeb[v] = fw;
+        c_occ += __popcll(~fw & valid_bits(v, Kw, K));
         uint64_t gone = s_F0[v] & ~s_Fa[v] & fw;  // released and not taken again: no owner
         while (gone) {
             owner[v * 64 + __ffsll((unsigned long long)gone) - 1] = -1;
             gone &= gone - 1;
         }
-        const uint64_t valid = (v == L.Kw - 1 && (L.K & 63)) ? ((1ull << (L.K & 63)) - 1) : ~0ull;
-        c_occ += __popcll(~fw & valid);
     }
-    int n_act;
-    {
-        int pre = block_excl_scan(c_occ, &n_act, s_tmp);  // the barrier inside publishes s_fpre, s_F1
-        for (int v = v0; v < v1; ++v) {
-            s_opre[v] = pre;
-            const uint64_t valid = (v == L.Kw - 1 && (L.K & 63)) ? ((1ull << (L.K & 63)) - 1) : ~0ull;
-            pre += __popcll(~s_F1[v] & valid);
-        }
+    int pre_occ, unused_e, n_act, unused_t;
+    block_excl_scan2(c_occ, 0, &pre_occ, &unused_e, &n_act, &unused_t, s_tmp);  // publishes s_fpre, s_F1
+    for (int v = v0; v < v1; ++v) {
+        s_opre[v] = pre_occ;
+        pre_occ += __popcll(~s_F1[v] & valid_bits(v, Kw, K));
     }
     __syncthreads();
 
     // Step 4 (lists): the i-th incoming neuron (ascending) takes the i-th free slot
-    // (ascending). Its position in the ascending occupied-slot list gets the neuron ID in
-    // act_src, so that the FFN can read the new bundle where it still is (the row store).
+    // (ascending). A thread's incoming neurons have consecutive indexes, so after one
+    // search for the first slot it walks the free bits. The slot's position in the
+    // ascending occupied-slot list gets the neuron ID in act_src, so that the FFN can read
+    // the new bundle where it still is (the row store).
     {
-        int k = base_in;
+        int idx = base_in;
+        int lo = -1;
+        uint64_t fw = 0;
         for (int w = w0; w < w1; ++w) {
             uint64_t bits = s_S[w] & ~s_R[w];
             while (bits) {
                 const int n = w * 64 + (__ffsll((unsigned long long)bits) - 1);
                 bits &= bits - 1;
-                const int idx = k++;
                 if (idx >= n_free) {
                     atomicOr(&s_err, kErrFreeExhausted);
+                    ++idx;
                     continue;
                 }
-                int lo = 0, hi = L.Kw - 1;  // last word whose prefix is <= idx
-                while (lo < hi) {
-                    const int mid = (lo + hi + 1) >> 1;
-                    if (s_fpre[mid] <= idx) lo = mid; else hi = mid - 1;
+                if (lo < 0) {
+                    int l0 = 0, h0 = Kw - 1;  // last word whose prefix is <= idx
+                    while (l0 < h0) {
+                        const int mid = (l0 + h0 + 1) >> 1;
+                        if (s_fpre[mid] <= idx) l0 = mid; else h0 = mid - 1;
+                    }
+                    lo = l0;
+                    fw = drop_low_bits(s_F0[lo], idx - s_fpre[lo]);
                 }
-                const uint64_t fw = drop_low_bits(s_F0[lo], idx - s_fpre[lo]);
-                const int slot = lo * 64 + (__ffsll((unsigned long long)fw) - 1);
-                const uint64_t below = (1ull << (slot & 63)) - 1;
-                const int pos = s_opre[lo] + __popcll(~s_F1[lo] & below);
-                d_in[idx] = n;
+                while (fw == 0) fw = s_F0[++lo];  // idx < n_free: a free bit follows
+                const int b = __ffsll((unsigned long long)fw) - 1;
+                fw &= fw - 1;
+                const int slot = lo * 64 + b;
+                const int pos = s_opre[lo] + __popcll(~s_F1[lo] & ((1ull << b) - 1));
                 slot_in[idx] = slot;
                 slot_map[n] = slot;
                 owner[slot] = n;
                 act_src[pos] = n;
+                ++idx;
             }
         }
     }
-    // Occupied slots in ascending order; slots kept from the last step have act_src -1.
-    for (int v = v0; v < v1; ++v) {
-        const uint64_t valid = (v == L.Kw - 1 && (L.K & 63)) ? ((1ull << (L.K & 63)) - 1) : ~0ull;
-        const uint64_t taken = s_F0[v] & ~s_F1[v];
-        uint64_t occ = ~s_F1[v] & valid;
-        int o = s_opre[v];
-        while (occ) {
-            const int b = __ffsll((unsigned long long)occ) - 1;
-            occ &= occ - 1;
-            act[o] = v * 64 + b;
-            if (!((taken >> b) & 1)) act_src[o] = -1;
-            ++o;
+    // Occupied slots in ascending order, one word per wave and one slot per lane; slots
+    // kept from the last step have act_src -1.
+    {
+        constexpr int kU = 4;  // words per wave per round, their LDS reads issued together
+        const uint64_t bit = 1ull << lane;
+        for (int v0w = wave * kU; v0w < Kw; v0w += kWaves * kU) {
+            uint64_t occ[kU], taken[kU];
+            int o0[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int v = min(v0w + u, Kw - 1);
+                occ[u] = v0w + u < Kw ? ~s_F1[v] & valid_bits(v, Kw, K) : 0;
+                taken[u] = s_F0[v] & ~s_F1[v];
+                o0[u] = s_opre[v];
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                if (occ[u] & bit) {
+                    const int o = o0[u] + __popcll(occ[u] & (bit - 1));
+                    act[o] = (v0w + u) * 64 + lane;
+                    if (!(taken[u] & bit)) act_src[o] = -1;
+                }
+            }
         }
     }
 
     // Step 5: R = S.
-    for (int w = tid; w < L.W; w += kNT) res[w] = s_S[w];
+    for (int w = tid; w < W; w += kNT) res[w] = s_S[w];
     __syncthreads();
     if (tid == 0) {
         counts[0] = n_in;

@@ -39,8 +39,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--ffn-steps", type=int, default=40,
                    help="tokens in each of the two per-kernel FFN timing passes")
-    p.add_argument("--direct", action="store_true",
-                   help="issue each decode step's launches one by one instead of replaying a captured graph")
+    p.add_argument("--graphs", action="store_true",
+                   help="replay each decode step as a captured HIP graph instead of launching one by one")
     p.add_argument("--pcie-steps", type=int, default=40, help="timed tokens with the store in pinned host memory")
     p.add_argument("--no-pcie", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -125,7 +125,7 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    B.decode_use_graphs(not args.direct)
+    B.decode_use_graphs(args.graphs)
     wl = Workload(CONFIGS[WORKLOAD])
     c = wl.cfg
     t0 = time.time()
@@ -314,7 +314,7 @@ def main():
         "mean_delta_per_layer": in_bundles / (args.steps * c.L),
         "cold_start_ms": cold_ms,
         "host_enqueue_ms_per_step": enqueued * 1e3 / args.steps,
-        "decode_launches": "one by one" if args.direct else "captured graph replay",
+        "decode_launches": "captured graph replay" if args.graphs else "one by one",
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": "k_sparse_ffn", "bytes_per_launch": ffn_bytes_per_launch,

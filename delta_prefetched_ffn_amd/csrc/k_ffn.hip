@@ -341,7 +341,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
                 err |= kErrSpin;
                 break;
             }
-            __builtin_amdgcn_s_sleep(2);
+            __builtin_amdgcn_s_sleep(1);
 #pragma unroll
             for (int k = 0; k < kStage; ++k)
                 if (tid + k * NT < n_other && pair_seq(hp[k]) != seq) hp[k] = ld_pair(&a.hpair[plo + tid + k * NT]);
@@ -412,7 +412,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
                         err |= kErrSpin;
                         break;
                     }
-                    __builtin_amdgcn_s_sleep(4);
+                    __builtin_amdgcn_s_sleep(1);
 #pragma unroll
                     for (int k = 0; k < kB; ++k)
                         if (pair_seq(pp[k]) != seq)

@@ -30,14 +30,17 @@
  *   6. If |A_t| > K_max the step is refused and the state is unchanged.
  *
  * The FFN (section 3.4: row i of gate, up and down^T for each active
- * neuron i) is y = sum_{i in A_t} down_i * relu(gate_i . x) * (up_i . x)
- * for the gated bundle, and y = sum_{i in A_t} down_i * relu(up_i . x)
- * for the [up|down^T] bundle of a non-gated ReLU FFN (LLM in a flash,
- * section 3.2 and 3.3). The oracle evaluates it straight from the row
+ * neuron i) is y = sum_{i in A_t} down_i * act(gate_i . x) * (up_i . x)
+ * for the gated bundle, and y = sum_{i in A_t} down_i * act(up_i . x)
+ * for the [up|down^T] bundle of a non-gated FFN (LLM in a flash, sections
+ * 3.2 and 3.3). act is ReLU (the benchmark's gated-ReLU models) or SiLU,
+ * silu(g) = g / (1 + exp(-g)), the gate of the SwiGLU MLPs the paper runs
+ * (section 3.4). The oracle evaluates it straight from the row
  * store in fp64, over neuron IDs in the order given (callers pass them
  * ascending), without looking at the slot machinery. bf16 -> fp64 and
  * fp32 -> fp64 are exact, and so is each bf16 x fp32 product in fp64.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -151,16 +154,25 @@ static double npo_bf16_to_f64(uint16_t h) {
     return (double)v.f;
 }
 
+enum { NPO_ACT_RELU = 0, NPO_ACT_SILU = 1 };
+
+/* The activation on the gate (or, non-gated, the up) dot product. */
+static double npo_act(double g, int32_t act) {
+    if (act == NPO_ACT_SILU) return g / (1.0 + exp(-g));
+    return g > 0.0 ? g : 0.0;
+}
+
 /*
  * Sparse FFN in fp64. ids[k] (k < n) indexes the bundles in `store`
  * (bundle = n_rows rows of d bf16 values). n_rows = 3: [gate|up|down^T],
- * h = relu(gate.x) * (up.x); n_rows = 2: [up|down^T], h = relu(up.x).
+ * h = act(gate.x) * (up.x); n_rows = 2: [up|down^T], h = act(up.x).
  * y[d] = sum_k h_k * down_{ids[k]}, accumulated in the order given.
- * Returns NPO_EINVAL for an unsupported n_rows.
+ * Returns NPO_EINVAL for an unsupported n_rows or activation.
  */
-int32_t npo_sparse_ffn(const uint16_t* store, int32_t n_rows, int32_t d, const int32_t* ids,
-                       int32_t n, const float* x, double* y) {
+int32_t npo_sparse_ffn_act(const uint16_t* store, int32_t n_rows, int32_t d, const int32_t* ids,
+                           int32_t n, const float* x, int32_t act, double* y) {
     if (n_rows != 2 && n_rows != 3) return NPO_EINVAL;
+    if (act != NPO_ACT_RELU && act != NPO_ACT_SILU) return NPO_EINVAL;
     for (int32_t j = 0; j < d; ++j) y[j] = 0.0;
     for (int32_t k = 0; k < n; ++k) {
         const uint16_t* bundle = store + (int64_t)ids[k] * n_rows * d;
@@ -174,14 +186,20 @@ int32_t npo_sparse_ffn(const uint16_t* store, int32_t n_rows, int32_t d, const i
                 g += npo_bf16_to_f64(gate[j]) * (double)x[j];
                 u += npo_bf16_to_f64(up[j]) * (double)x[j];
             }
-            h = (g > 0.0 ? g : 0.0) * u;
+            h = npo_act(g, act) * u;
         } else {
             const uint16_t* up = bundle;
             double u = 0.0;
             for (int32_t j = 0; j < d; ++j) u += npo_bf16_to_f64(up[j]) * (double)x[j];
-            h = u > 0.0 ? u : 0.0;
+            h = npo_act(u, act);
         }
         for (int32_t j = 0; j < d; ++j) y[j] += h * npo_bf16_to_f64(down[j]);
     }
     return NPO_OK;
+}
+
+/* The ReLU FFN (the benchmark's models). */
+int32_t npo_sparse_ffn(const uint16_t* store, int32_t n_rows, int32_t d, const int32_t* ids,
+                       int32_t n, const float* x, double* y) {
+    return npo_sparse_ffn_act(store, n_rows, d, ids, n, x, NPO_ACT_RELU, y);
 }

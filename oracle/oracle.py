@@ -21,6 +21,8 @@ import numpy as np
 
 UNION, INTERSECT, SINGLE = 0, 1, 2
 MODES = {"union": UNION, "intersect": INTERSECT, "single": SINGLE}
+RELU, SILU = 0, 1
+ACTS = {"relu": RELU, "silu": SILU}
 _OK, _EINVAL, _ECAPACITY = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -32,7 +34,7 @@ def build_lib(force: bool = False) -> str:
     src = os.path.join(_HERE, "oracle.c")
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src):
         tmp = _LIB_PATH + f".tmp{os.getpid()}"
-        cmd = f"gcc -O2 -std=c11 -fPIC -shared -ffp-contract=off -o {tmp} {src}"
+        cmd = f"gcc -O2 -std=c11 -fPIC -shared -ffp-contract=off -o {tmp} {src} -lm"
         if os.system(cmd) != 0:
             raise RuntimeError(f"failed: {cmd}")
         os.replace(tmp, _LIB_PATH)
@@ -55,6 +57,8 @@ def _lib():
     lib.npo_copy_bundles.restype = None
     lib.npo_sparse_ffn.argtypes = [vp, i32, i32, vp, i32, vp, vp]
     lib.npo_sparse_ffn.restype = i32
+    lib.npo_sparse_ffn_act.argtypes = [vp, i32, i32, vp, i32, vp, i32, vp]
+    lib.npo_sparse_ffn_act.restype = i32
     return lib
 
 
@@ -139,8 +143,9 @@ class OracleLayer:
         return out[:n].copy()
 
 
-def sparse_ffn(store: np.ndarray, R: int, d: int, ids: np.ndarray, x: np.ndarray) -> np.ndarray:
-    """fp64 y[d] = sum over ids (in the order given) of down_i * h_i; store is uint16 [*][R][d]."""
+def sparse_ffn(store: np.ndarray, R: int, d: int, ids: np.ndarray, x: np.ndarray, act: str = "relu") -> np.ndarray:
+    """fp64 y[d] = sum over ids (in the order given) of down_i * h_i; store is uint16 [*][R][d].
+    h_i = act(gate_i . x) * (up_i . x) (R = 3) or act(up_i . x) (R = 2), act "relu" or "silu"."""
     st = store.reshape(-1)
     assert st.dtype == np.uint16 and st.flags.c_contiguous
     ids = _c(ids, np.int32)
@@ -149,8 +154,8 @@ def sparse_ffn(store: np.ndarray, R: int, d: int, ids: np.ndarray, x: np.ndarray
     x = _c(x, np.float32)
     assert x.size == d
     y = np.empty(d, dtype=np.float64)
-    rc = _lib().npo_sparse_ffn(st.ctypes.data, R, d, ids.ctypes.data, ids.size, x.ctypes.data,
-                               y.ctypes.data)
+    rc = _lib().npo_sparse_ffn_act(st.ctypes.data, R, d, ids.ctypes.data, ids.size, x.ctypes.data,
+                                   ACTS[act], y.ctypes.data)
     if rc != _OK:
-        raise ValueError(f"unsupported bundle rows {R}")
+        raise ValueError(f"unsupported bundle rows {R} or activation {act}")
     return y

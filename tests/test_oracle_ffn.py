@@ -168,3 +168,69 @@ def test_relu_zero_boundary():
     store = to_bf16_bits(np.array([[[1.0, -1.0], [3.0, 3.0], [1.0, 1.0]]], dtype=np.float32))
     y = O.sparse_ffn(store, 3, 2, np.array([0]), np.array([1.0, 1.0], dtype=np.float32))
     assert y.tolist() == [0.0, 0.0]
+
+
+# ---- SiLU (the gate of the paper's SwiGLU MLPs, NeuroPrefetcher section 3.4) ----
+# silu(g) = g * sigmoid(g). The pins use facts of the logistic function that do not restate
+# the formula: sigmoid(ln a) = a / (1 + a) for a > 0, sigmoid(-g) = 1 - sigmoid(g) (so that
+# silu(g) - silu(-g) = g), and the limits silu(g) -> g for large g, -> 0 for very negative g.
+
+def _one_neuron(gate, up, down, R):
+    rows = [gate, up, down] if R == 3 else [up, down]
+    return to_bf16_bits(np.array([[[r] for r in rows]], dtype=np.float32))
+
+
+@pytest.mark.parametrize("a", [3.0, 2.0, 0.5, 9.0])
+def test_silu_at_log_points(a):
+    # gated, d = 1, gate = up = down = 1: y = silu(x) * x with x = fp32(ln a); sigmoid(ln a)
+    # = a / (1 + a), and fp32 rounding of ln a moves it by at most 1e-7 relative
+    x = np.float32(np.log(a))
+    y = O.sparse_ffn(_one_neuron(1.0, 1.0, 1.0, 3), 3, 1, np.array([0]), np.array([x]), "silu")[0]
+    want = (a / (1.0 + a)) * float(x) * float(x)
+    assert abs(y - want) <= 1e-7 * abs(want)
+
+
+def test_silu_odd_part_is_identity():
+    # non-gated, up = down = 1: y(x) = silu(x); silu(x) - silu(-x) = x exactly in real arithmetic
+    rng = np.random.default_rng(5)
+    st = _one_neuron(0.0, 1.0, 1.0, 2)
+    for x in rng.standard_normal(50).astype(np.float32) * 4:
+        yp = O.sparse_ffn(st, 2, 1, np.array([0]), np.array([x]), "silu")[0]
+        ym = O.sparse_ffn(st, 2, 1, np.array([0]), np.array([-x]), "silu")[0]
+        assert abs((yp - ym) - float(x)) <= 1e-14 * max(1.0, abs(float(x)))
+        assert (yp > 0) == (x > 0) or x == 0                  # silu keeps the sign
+        assert ym >= -0.2785                                    # its minimum is about -0.2785
+
+
+def test_silu_limits_and_zero():
+    st = _one_neuron(0.0, 1.0, 1.0, 2)
+    y = lambda x: O.sparse_ffn(st, 2, 1, np.array([0]), np.array([x], dtype=np.float32), "silu")[0]
+    assert y(0.0) == 0.0
+    assert abs(y(40.0) - 40.0) <= 40.0 * 1e-15
+    assert abs(y(-40.0)) <= 1e-15
+
+
+def test_silu_gated_equals_dense_masked():
+    # the sparse sum over S equals the dense SwiGLU FFN with inactive neurons masked (dense
+    # side: NumPy matmul; its activation from the log-point fact sigmoid(g) = e^g / (1 + e^g))
+    rng = np.random.default_rng(11)
+    M, d = 64, 48
+    store = (rng.standard_normal((M, 3, d)).astype(np.float32) * 0.25)
+    store = ((store.view(np.uint32) + 0x8000) >> 16).astype(np.uint16)   # round to bf16 bits
+    x = rng.standard_normal(d).astype(np.float32)
+    active = np.sort(rng.choice(M, 20, replace=False)).astype(np.int32)
+    W = bf16_to_f64(store)
+    g = W[:, 0, :] @ x.astype(np.float64)
+    u = W[:, 1, :] @ x.astype(np.float64)
+    eg = np.exp(g)
+    m = np.zeros(M)
+    m[active] = 1.0
+    want = W[:, 2, :].T @ (m * g * (eg / (1.0 + eg)) * u)
+    y = O.sparse_ffn(store, 3, d, active, x, "silu")
+    assert np.abs(y - want).max() <= 1e-12 * np.abs(want).max()
+
+
+def test_unknown_activation_is_refused():
+    st = _one_neuron(1.0, 1.0, 1.0, 3)
+    with pytest.raises(KeyError):
+        O.sparse_ffn(st, 3, 1, np.array([0]), np.array([1.0], dtype=np.float32), "gelu")

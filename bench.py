@@ -1,11 +1,17 @@
 """Benchmark: sparse-FFN decode at batch 1 on the Llama-2-7B-shaped workload.
 
-One step = one decode token through all 31 sparse layers: active-set decode,
-set difference, slot assignment (one launch for all layers), per-layer row
-scatter on a copy stream, and per-layer fused sparse FFN on the compute
-stream (np_decode_step). Inputs (centroid IDs, x, the backing row store) are
+One step = one decode token through all 31 sparse layers (np_decode_step):
+active-set decode, set difference and slot assignment for all layers in one
+launch, then the fused sparse FFN of each layer in layer order, each reading
+its new bundles from the row store and writing them into their slots
+(read-through scatter). Inputs (centroid IDs, x, the backing row store) are
 resident in HBM before the timed region; the PCIe-inclusive rate with the
-row store in pinned host memory is reported beside it under "pcie_inclusive".
+row store in pinned host memory (per-layer scatter over the host link on a
+copy stream) is reported beside it under "pcie_inclusive".
+
+--config N runs another built-in workload the same way (6-8: the paper's
+Mistral-7B shape with SwiGLU and intersected masks); the default, 2, is the
+headline workload.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -25,7 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E peak, GB/s
-WORKLOAD = 2             # Llama-2-7B-shaped: 31 layers, d 4096, M 11008, K_max 4096
+DEFAULT_WORKLOAD = 2     # Llama-2-7B-shaped: 31 layers, d 4096, M 11008, K_max 4096
 
 
 def log(msg: str) -> None:
@@ -35,6 +41,7 @@ def log(msg: str) -> None:
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--config", type=int, default=DEFAULT_WORKLOAD, help="built-in workload number")
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--ffn-steps", type=int, default=40,
@@ -48,6 +55,19 @@ def parse():
     p.add_argument("--slots-per-wg", type=int, default=0)
     p.add_argument("--tile-cols", type=int, default=0)
     return p.parse_args()
+
+
+def workload_text(c, mean_active: float) -> str:
+    shape = {2: "Llama-2-7B-shaped", 3: "Llama-2-13B-shaped", 4: "OPT-6.7B-shaped", 5: "d7168 d_ff 28672",
+             6: "Mistral-7B-shaped", 7: "Mistral-7B-shaped", 8: "Mistral-7B-shaped"}.get(c.num, c.name)
+    ffn = ("SwiGLU (SiLU gate)" if c.act == "silu" else "gated ReLU") if c.R == 3 else "non-gated ReLU"
+    rows = "[gate|up|down^T]" if c.R == 3 else "[up|down^T]"
+    pers = f"{c.p_lo:.2f}-{c.p_hi:.2f}" if c.recipe == "trajectory" else "~0.84"
+    masks = {"union": "union of gate and up centroid masks", "intersect": "intersection of gate and up centroid masks",
+             "single": "one centroid mask"}[c.mode]
+    return (f"{shape} sparse FFN decode: {c.L} layers, d_model {c.d}, d_ff {c.M}, K_max {c.K}, {ffn}, "
+            f"bf16 {rows} bundles, {masks}, ~{100 * mean_active / c.M:.0f}% active, {pers} token-to-token "
+            f"persistence, batch 1")
 
 
 def token_ids(first: int, count: int, T: int) -> list[int]:
@@ -89,7 +109,7 @@ def cpu_baseline(wl, stores, seconds: float):
         S = O.active_set(tabs[l][0][g], tabs[l][-1][u], c.M, mode)
         res = layers[l].step(S)
         layers[l].copy_bundles(stores[l], res)
-        O.sparse_ffn(stores[l], c.R, c.d, S, x_all[t, l])
+        O.sparse_ffn(stores[l], c.R, c.d, S, x_all[t, l], c.act)
         return S.size, res.d_in.size
 
     with ThreadPoolExecutor(threads) as ex:
@@ -126,7 +146,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     B.decode_use_graphs(args.graphs)
-    wl = Workload(CONFIGS[WORKLOAD])
+    wl = Workload(CONFIGS[args.config])
     c = wl.cfg
     t0 = time.time()
     stores = [wl.store(l) for l in range(c.L)]
@@ -146,7 +166,7 @@ def main():
                 dev = torch.empty(t.numel(), dtype=torch.int16, pin_memory=True)
                 dev.copy_(t)
             L = B.Layer(d_model=c.d, d_ff=c.M, k_max=c.K, n_rows=c.R, masks=wl.masks(l),
-                        mask_mode=B.MODES[c.mode], row_store=dev.data_ptr(), keepalive=dev)
+                        mask_mode=B.MODES[c.mode], act=B.ACTS[c.act], row_store=dev.data_ptr(), keepalive=dev)
             if args.slots_per_wg or args.tile_cols:
                 L.set_ffn_shape(args.slots_per_wg, args.tile_cols)
             out.append(L)
@@ -303,9 +323,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "Llama-2-7B-shaped sparse FFN decode: 31 layers, d_model 4096, d_ff 11008, "
-                               "K_max 4096, gated ReLU, bf16 [gate|up|down^T] bundles, ~12% active, "
-                               "~0.84 token-to-token persistence, batch 1",
+        "config": {"workload": workload_text(c, act_bundles / (args.steps * c.L)),
                    "global_batch": 1, "layers": c.L, "d_model": c.d, "d_ff": c.M, "k_max": c.K,
                    "weights": "bf16", "backing_store": "HBM", "parallelism": "single GPU"},
         "effective_gbps": eff_gbps,
@@ -321,7 +339,7 @@ def main():
                      "active_row_bytes_per_launch": act_bytes_per_launch,
                      "active_row_gbps": act_bytes_per_launch / (avg_burst_us * 1e-6) / 1e9,
                      "avg_launch_us": avg_burst_us, "avg_launch_us_own_events": avg_event_us,
-                     "timing": "HIP events on the launch stream around back-to-back launches of the 31 layers, "
+                     "timing": f"HIP events on the launch stream around back-to-back launches of the {c.L} layers, "
                                "each right after its layer's delta assignment (read-through of the new bundles)",
                      "traffic_note": traffic_note},
         "hbm_read_probe_gbps": probe_gbps,

@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(_PKG, "libnp.so")
 NP_OK, NP_EINVAL, NP_ECAPACITY, NP_ENOMEM, NP_EHIP, NP_ESTATE, NP_EDEVICE = range(7)
 MASK_UNION, MASK_INTERSECT, MASK_SINGLE = 0, 1, 2
 MODES = {"union": MASK_UNION, "intersect": MASK_INTERSECT, "single": MASK_SINGLE}
-ACT_RELU = 0
+ACT_RELU, ACT_SILU = 0, 1
+ACTS = {"relu": ACT_RELU, "silu": ACT_SILU}
 _NAMES = {0: "NP_OK", 1: "NP_EINVAL", 2: "NP_ECAPACITY", 3: "NP_ENOMEM", 4: "NP_EHIP",
           5: "NP_ESTATE", 6: "NP_EDEVICE"}
 

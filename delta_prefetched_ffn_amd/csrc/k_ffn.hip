@@ -1,7 +1,7 @@
 // Fused gather-GEMV sparse FFN for gfx950 (batch 1, bf16 rows, fp32 math).
 //
-// Computes y = sum over the resident slots s of down_s * relu(gate_s . x) * (up_s . x)
-// (gated bundle [gate|up|down^T]) or y = sum_s down_s * relu(up_s . x) (bundle
+// Computes y = sum over the resident slots s of down_s * act(gate_s . x) * (up_s . x)
+// (gated bundle [gate|up|down^T]) or y = sum_s down_s * act(up_s . x) (bundle
 // [up|down^T]); NeuroPrefetcher, section 3.4: each active neuron i uses row i of
 // gate, up and down^T; the slot map locates the rows, whose order in the buffer
 // does not matter.
@@ -63,6 +63,15 @@ __device__ inline float dot8(const uint4 v, const fv4 lo, const fv4 hi) {
     a = fmaf(bf_lo(v.w), hi.z, a);
     a = fmaf(bf_hi(v.w), hi.w, a);
     return a;
+}
+
+// h of one neuron from its gate (g) and up (u) dot products: act(g) * u gated, act(u) not.
+// act 1 is SiLU, g / (1 + exp(-g)) (for very negative g, exp overflows to +inf and the
+// quotient is -0); act 0 is ReLU.
+__device__ inline float neuron_h(float g, float u, bool gated, int act) {
+    const float v = gated ? g : u;
+    const float a = act == 1 ? v / (1.f + expf(-v)) : fmaxf(v, 0.f);
+    return gated ? a * u : a;
 }
 
 __device__ inline void axpy8(float* acc, const float h, const uint4 v) {
@@ -272,7 +281,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
                         for (int k = 0; k < CL / 64; ++k) sm += s_red1[(rl * (CL / 64) + k) * V + cl * NR1 + r];
                         g[r] = sm;
                     }
-                    const float h = GATED ? fmaxf(g[0], 0.f) * g[1] : fmaxf(g[0], 0.f);
+                    const float h = neuron_h(g[0], g[NR1 - 1], GATED, a.activation);
                     st_pair(&a.hpair[pos], seq, h);
                     s_h[pos - plo] = h;
                 }
@@ -287,7 +296,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
                 for (int i = 0; i < SB; ++i) {
                     const int pos = b0 + rl + RL * i;
                     if (pos < c1) {
-                        const float h = GATED ? fmaxf(v[i * NR1], 0.f) * v[i * NR1 + NR1 - 1] : fmaxf(v[i], 0.f);
+                        const float h = neuron_h(v[i * NR1], v[i * NR1 + NR1 - 1], GATED, a.activation);
                         st_pair(&a.hpair[pos], seq, h);
                         s_h[pos - plo] = h;
                     }

@@ -271,6 +271,7 @@ np_status enqueue_ffn(np_layer* L, const float* x, float* y, hipStream_t s, cons
     a.K = L->desc.k_max;
     a.R = L->desc.n_rows;
     a.M = L->desc.d_ff;
+    a.activation = L->desc.act;
     a.p1 = sh.p1;
     a.q = sh.q;
     a.tw = sh.tw;
@@ -479,7 +480,7 @@ np_status np_layer_create(const np_layer_desc* desc, np_layer** out) {
         return fail(NP_EINVAL, "n_centroids=%d must be in [1, %d]", D.n_centroids, kMaxCentroids);
     if (D.mask_mode < NP_MASK_UNION || D.mask_mode > NP_MASK_SINGLE)
         return fail(NP_EINVAL, "unknown mask_mode %d", D.mask_mode);
-    if (D.act != NP_ACT_RELU) return fail(NP_EINVAL, "unsupported activation %d", D.act);
+    if (D.act != NP_ACT_RELU && D.act != NP_ACT_SILU) return fail(NP_EINVAL, "unsupported activation %d", D.act);
     if (!D.masks || !D.row_store) return fail(NP_EINVAL, "masks and row_store must not be NULL");
     if ((uint64_t)D.k_max * D.n_rows * D.d_model * 2 > kMaxBufBytes)
         return fail(NP_EINVAL, "slot buffer k_max * n_rows * d_model * 2 bytes must stay below 4 GiB");

@@ -108,6 +108,7 @@ struct FfnArgs {
     uint32_t buf_bytes;     // size of buf (below 4 GiB)
     int32_t d, K, R, M;
     int32_t p1, q, tw, nwg;
+    int32_t activation;     // 0 ReLU, 1 SiLU
 };
 
 // Device code: view a pointer read from memory as a global-memory pointer. Without it the

@@ -68,7 +68,10 @@ typedef enum {
  * uses one table for a non-gated FFN). */
 typedef enum { NP_MASK_UNION = 0, NP_MASK_INTERSECT = 1, NP_MASK_SINGLE = 2 } np_mask_mode;
 
-typedef enum { NP_ACT_RELU = 0 } np_act;
+/* Activation on the gate (gated) or up (non-gated) dot product: ReLU (the
+ * benchmark's gated-ReLU models; relu(0) = 0) or SiLU, g / (1 + exp(-g)), the
+ * gate of the SwiGLU MLPs of section 3.4. Computed in fp32 on the GPU. */
+typedef enum { NP_ACT_RELU = 0, NP_ACT_SILU = 1 } np_act;
 
 typedef struct np_layer np_layer; /* opaque: one sparse FFN layer */
 

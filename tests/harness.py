@@ -47,7 +47,7 @@ def make_layer(wl: Workload, l: int, where: str = "device", store: np.ndarray | 
         store = wl.store(l)
     dev_store = upload_store(store, where)
     layer = B.Layer(d_model=c.d, d_ff=c.M, k_max=c.K, n_rows=c.R, masks=wl.masks(l),
-                    mask_mode=B.MODES[c.mode], row_store=dev_store.data_ptr(), keepalive=dev_store)
+                    mask_mode=B.MODES[c.mode], act=B.ACTS[c.act], row_store=dev_store.data_ptr(), keepalive=dev_store)
     return layer, store
 
 

@@ -68,7 +68,7 @@ def run_full(num: int, where: str = "device", steps: int | None = None, ffn_samp
     picks = {(0, 0), (T - 1, c.L - 1)} | {(int(rng.integers(T)), int(rng.integers(c.L))) for _ in range(ffn_samples)}
     for t, l in sorted(picks):
         S = orc.active(t, l)
-        ref = O.sparse_ffn(wl.bundles(l, S), c.R, c.d, np.arange(S.size, dtype=np.int32), x_all[t, l])
+        ref = O.sparse_ffn(wl.bundles(l, S), c.R, c.d, np.arange(S.size, dtype=np.int32), x_all[t, l], c.act)
         check_y(yh[t, l], ref, f"cfg{num} t={t} l={l}")
     _log(f"config {num}: {T} steps, {len(picks)} FFN samples ok in {time.time() - t0:.1f}s")
     for layer in layers:
@@ -78,7 +78,7 @@ def run_full(num: int, where: str = "device", steps: int | None = None, ffn_samp
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("num", [2, 3, 4, 5])
+@pytest.mark.parametrize("num", [2, 3, 4, 5, 6, 7, 8])
 def test_full_config_device_store(num):
     run_full(num, "device")
 

@@ -46,7 +46,7 @@ def test_config1_single_layer_calls(torch, where):
         S, res = orc.step(t, 0, store)
         compare_state(st, orc.layers[0], res, S, f"t={t}")
         assert np.array_equal(layer.read_rows(), orc.layers[0].buf), f"t={t}: buffer differs"
-        check_y(y[t, 0].cpu().numpy(), O.sparse_ffn(store, c.R, c.d, S, x_all[t, 0]), f"t={t}")
+        check_y(y[t, 0].cpu().numpy(), O.sparse_ffn(store, c.R, c.d, S, x_all[t, 0], c.act), f"t={t}")
     layer.close()
 
 
@@ -58,10 +58,14 @@ SMALL = [
     small_config(905, L=2, d=5120, M=640, K=256, C=4, mode="union", m=100, swap=20, T=6),
     small_config(906, L=2, d=7168, M=1100, K=700, C=4, mode="union", m=300, swap=50, T=6),
     small_config(907, L=1, d=8, M=64, K=64, C=3, mode="union", m=20, swap=4, T=6),
+    # SwiGLU (SiLU gate) with intersected masks, as in the paper's models; and SiLU non-gated
+    small_config(908, L=2, d=4096, M=1400, K=600, C=5, mode="intersect", m=600, swap=50, T=8, act="silu"),
+    small_config(909, L=2, d=1000, M=500, K=200, C=4, mode="union", m=90, swap=12, T=6, act="silu"),
+    small_config(910, L=2, d=512, M=300, K=120, C=4, mode="single", R=2, m=100, swap=10, T=6, act="silu"),
 ]
 
 
-@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: f"d{c.d}_M{c.M}_K{c.K}_{c.mode}_R{c.R}")
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: f"d{c.d}_M{c.M}_K{c.K}_{c.mode}_R{c.R}_{c.act}")
 @pytest.mark.parametrize("streams,graphs", [(1, True), (1, False), (2, True), (2, False)])
 def test_small_shapes_decode_step(torch, cfg, streams, graphs):
     from delta_prefetched_ffn_amd import binding as B
@@ -87,7 +91,7 @@ def test_small_shapes_decode_step(torch, cfg, streams, graphs):
     for t in range(cfg.T):
         for l in range(cfg.L):
             S = orc2.active(t, l)
-            check_y(yh[t, l], O.sparse_ffn(stores[l], cfg.R, cfg.d, S, x_all[t, l]), f"t={t} l={l}")
+            check_y(yh[t, l], O.sparse_ffn(stores[l], cfg.R, cfg.d, S, x_all[t, l], cfg.act), f"t={t} l={l}")
     for layer in layers:
         layer.close()
     B.decode_use_graphs(False)  # the library default
@@ -238,7 +242,7 @@ def test_ffn_launch_shapes(torch, shape):
         layer.sparse_ffn(x[t, 0].data_ptr(), y[t, 0].data_ptr(), s)
         assert layer.read_state()["err"] == 0
         S = orc.active(t, 0)
-        check_y(y[t, 0].cpu().numpy(), O.sparse_ffn(store, cfg.R, cfg.d, S, x_all[t, 0]), f"{shape} t={t}")
+        check_y(y[t, 0].cpu().numpy(), O.sparse_ffn(store, cfg.R, cfg.d, S, x_all[t, 0], cfg.act), f"{shape} t={t}")
     layer.close()
     # exact arithmetic in the same shape
     rng = np.random.default_rng(77)

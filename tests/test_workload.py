@@ -57,12 +57,13 @@ def test_reproducible_and_sliceable():
 
 
 def test_mask_sizes_bound_capacity():
-    for num in (1, 2, 3, 4):
+    for num in (1, 2, 3, 4, 6, 7, 8):
         c = CONFIGS[num]
         tabs = Workload(c).masks(0)
         sizes = np.unpackbits(tabs.view(np.uint8), axis=-1).sum(axis=-1)
         assert (sizes == c.m).all()
-        assert c.n_proj * c.m <= c.K
+        # union: |S| <= |G| + |U|; intersection: |S| <= |G|
+        assert (c.m if c.mode == "intersect" else c.n_proj * c.m) <= c.K
 
 
 def test_config1_statistics():
@@ -73,7 +74,8 @@ def test_config1_statistics():
     assert 0.65 <= p <= 0.85
 
 
-@pytest.mark.parametrize("num,frac_lo,frac_hi", [(2, 0.10, 0.15), (3, 0.10, 0.14), (4, 0.05, 0.08)])
+@pytest.mark.parametrize("num,frac_lo,frac_hi", [(2, 0.10, 0.15), (3, 0.10, 0.14), (4, 0.05, 0.08),
+                                                 (6, 0.30, 0.35), (7, 0.40, 0.45), (8, 0.56, 0.61)])
 def test_model_shaped_statistics(num, frac_lo, frac_hi):
     c = CONFIGS[num]
     wl = Workload(c)

@@ -132,6 +132,7 @@ class Config:
     p_lo: float = 0.0     # trajectory recipe: persistence range
     p_hi: float = 0.0
     w_std: float = 0.02
+    act: str = "relu"     # activation of the model's FFN: "relu" | "silu" (SwiGLU gate)
 
     @property
     def W(self) -> int:
@@ -161,13 +162,24 @@ CONFIGS = {
               mode="single", T=256, m=1065, swap=88),
     5: Config(5, "large d7168 M28672 low-overlap", L=47, d=7168, M=28672, R=3, K=6144, C=128,
               mode="union", T=128, recipe="trajectory", active=2867, p_lo=0.70, p_hi=0.90),
+    # The paper's own model shape (Mistral-7B: d 4096, d_ff 14336, SwiGLU), its active set the
+    # intersection of the gate and up masks, at its three K_max budgets (62 / 50 / 31%
+    # sparsity). Each mask keeps K_max - s members of a base set of K_max neurons; the
+    # intersection then has about K_max (1 - s/K_max)^2 neurons and consecutive tokens share
+    # about (1 - s/K_max)^2 of them (0.84 at s/K_max = 0.0835).
+    6: Config(6, "Mistral-7B-shaped SwiGLU FFN, K_max 5500", L=31, d=4096, M=14336, R=3, K=5500,
+              C=512, mode="intersect", T=256, m=5500, swap=459, act="silu"),
+    7: Config(7, "Mistral-7B-shaped SwiGLU FFN, K_max 7168", L=31, d=4096, M=14336, R=3, K=7168,
+              C=512, mode="intersect", T=256, m=7168, swap=599, act="silu"),
+    8: Config(8, "Mistral-7B-shaped SwiGLU FFN, K_max 9865", L=31, d=4096, M=14336, R=3, K=9865,
+              C=512, mode="intersect", T=256, m=9865, swap=824, act="silu"),
 }
 
 
 def small_config(num: int, *, L=2, d=64, M=200, R=3, K=96, C=8, mode="union", T=6, m=40,
-                 swap=6, name="test shape") -> Config:
+                 swap=6, name="test shape", act="relu") -> Config:
     """A reduced shape for fast tests (same recipe, own seeds via `num`)."""
-    return Config(num, name, L=L, d=d, M=M, R=R, K=K, C=C, mode=mode, T=T, m=m, swap=swap)
+    return Config(num, name, L=L, d=d, M=M, R=R, K=K, C=C, mode=mode, T=T, m=m, swap=swap, act=act)
 
 
 class Workload:

@@ -128,6 +128,46 @@ int32_t npo_delta_step(int32_t M, int32_t K, int32_t* slot_map, int32_t* owner, 
     return NPO_OK;
 }
 
+/*
+ * Residency window (LLM in a flash, section 3.1 "Windowing": weights of neurons that
+ * were active for recent tokens stay resident, and only missing ones are loaded).
+ * Computes the resident set R_t that the delta step then moves to (D_in = R_t \ R_{t-1},
+ * D_out = R_{t-1} \ R_t), for token t, window k >= 1 and capacity K:
+ *   R_t = S_t plus every resident neuron last active at token t - j, 1 <= j < k,
+ *   taken from the most recent (j = 1) to the oldest and, within one j, by ascending ID,
+ *   as long as |R_t| <= K. Neurons that left the buffer are never loaded back here.
+ * k = 1 gives R_t = S_t (the exact rule of NeuroPrefetcher section 3.4).
+ * last_t[i] is the last token at which neuron i was active (anything below t - k + 1 for
+ * never). slot_map[i] >= 0 marks residency. Writes R_t ascending to R (capacity M) and
+ * returns |R_t|; -2 when n > K (refused), -1 for invalid arguments.
+ */
+int32_t npo_window_target(int32_t M, int32_t K, int32_t k, int32_t t, const int32_t* last_t,
+                          const int32_t* slot_map, const int32_t* S, int32_t n, int32_t* R) {
+    if (M <= 0 || K <= 0 || k < 1 || n < 0) return -1;
+    if (n > K) return -2;
+    char* in_r = (char*)calloc((size_t)M, 1);
+    if (!in_r) return -1;
+    for (int32_t q = 0; q < n; ++q) {
+        if (S[q] < 0 || S[q] >= M) { free(in_r); return -1; }
+        in_r[S[q]] = 1;
+    }
+    int32_t room = K - n;
+    for (int32_t j = 1; j < k && room > 0; ++j) {
+        for (int32_t i = 0; i < M && room > 0; ++i) {
+            if (in_r[i] || slot_map[i] < 0) continue;
+            if (t - last_t[i] == j) {
+                in_r[i] = 1;
+                --room;
+            }
+        }
+    }
+    int32_t m = 0;
+    for (int32_t i = 0; i < M; ++i)
+        if (in_r[i]) R[m++] = i;
+    free(in_r);
+    return m;
+}
+
 /* Ascending occupied slots (the slots whose rows the FFN reads); returns the count. */
 int32_t npo_occupied_slots(int32_t K, const int32_t* owner, int32_t* slots) {
     int32_t n = 0;

@@ -59,6 +59,8 @@ def _lib():
     lib.npo_sparse_ffn.restype = i32
     lib.npo_sparse_ffn_act.argtypes = [vp, i32, i32, vp, i32, vp, i32, vp]
     lib.npo_sparse_ffn_act.restype = i32
+    lib.npo_window_target.argtypes = [i32, i32, i32, i32, vp, vp, vp, i32, vp]
+    lib.npo_window_target.restype = i32
     return lib
 
 
@@ -89,22 +91,61 @@ class StepResult:
     d_out: np.ndarray     # ascending outgoing neuron IDs
 
 
-class OracleLayer:
-    """Slot map, owner table and (optionally) the K_max-row buffer of one sparse layer."""
+_NEVER = -(1 << 30)
 
-    def __init__(self, M: int, K: int, R: int, d: int, keep_buffer: bool = True):
-        self.M, self.K, self.R, self.d = M, K, R, d
+
+class OracleLayer:
+    """Slot map, owner table and (optionally) the K_max-row buffer of one sparse layer.
+
+    window = 1: the buffer holds exactly the active set (NeuroPrefetcher section 3.4).
+    window = k > 1: it also keeps neurons active in the last k - 1 tokens, capacity
+    permitting (LLM in a flash, section 3.1; see npo_window_target)."""
+
+    def __init__(self, M: int, K: int, R: int, d: int, keep_buffer: bool = True, window: int = 1):
+        assert window >= 1
+        self.M, self.K, self.R, self.d, self.window = M, K, R, d, window
         self.slot_map = np.full(M, -1, dtype=np.int32)
         self.owner = np.full(K, -1, dtype=np.int32)
+        self.last_t = np.full(M, _NEVER, dtype=np.int32)
+        self.t = 0
         self.buf = np.zeros((K, R, d), dtype=np.uint16) if keep_buffer else None
 
     def reset(self) -> None:
         self.slot_map.fill(-1)
         self.owner.fill(-1)
+        self.last_t.fill(_NEVER)
+        self.t = 0
         if self.buf is not None:
             self.buf.fill(0)
 
+    def target(self, S: np.ndarray) -> np.ndarray:
+        """The resident set this token moves to (S itself for window 1)."""
+        S = _c(S, np.int32)
+        if self.window == 1:
+            if S.size > self.K:
+                raise CapacityError(f"|S|={S.size} > K_max={self.K}")
+            return S
+        R = np.empty(self.M, dtype=np.int32)
+        m = _lib().npo_window_target(self.M, self.K, self.window, self.t, self.last_t.ctypes.data,
+                                     self.slot_map.ctypes.data, S.ctypes.data, S.size, R.ctypes.data)
+        if m == -2:
+            raise CapacityError(f"|S|={S.size} > K_max={self.K}")
+        if m < 0:
+            raise ValueError("invalid active set")
+        return R[:m].copy()
+
+    def active_slots(self, S: np.ndarray) -> np.ndarray:
+        """Ascending slots of the active neurons (the rows the FFN reads)."""
+        return np.sort(self.slot_map[_c(S, np.int32)])
+
     def step(self, S: np.ndarray) -> StepResult:
+        S = _c(S, np.int32)
+        res = self._move_to(self.target(S))
+        self.last_t[S] = self.t
+        self.t += 1
+        return res
+
+    def _move_to(self, S: np.ndarray) -> StepResult:
         S = _c(S, np.int32)
         d_in = np.empty(self.K, dtype=np.int32)
         slot_in = np.empty(self.K, dtype=np.int32)

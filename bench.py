@@ -42,6 +42,8 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--config", type=int, default=DEFAULT_WORKLOAD, help="built-in workload number")
+    p.add_argument("--window", type=int, default=1,
+                   help="residency window in tokens (1: the buffer holds exactly the active set)")
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--ffn-steps", type=int, default=40,
@@ -169,6 +171,8 @@ def main():
                         mask_mode=B.MODES[c.mode], act=B.ACTS[c.act], row_store=dev.data_ptr(), keepalive=dev)
             if args.slots_per_wg or args.tile_cols:
                 L.set_ffn_shape(args.slots_per_wg, args.tile_cols)
+            if args.window != 1:
+                L.set_window(args.window)
             out.append(L)
         return out
 
@@ -325,7 +329,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload_text(c, act_bundles / (args.steps * c.L)),
                    "global_batch": 1, "layers": c.L, "d_model": c.d, "d_ff": c.M, "k_max": c.K,
-                   "weights": "bf16", "backing_store": "HBM", "parallelism": "single GPU"},
+                   "weights": "bf16", "backing_store": "HBM", "parallelism": "single GPU",
+                   "residency_window": args.window},
         "effective_gbps": eff_gbps,
         "effective_frac_of_hbm_peak": eff_gbps / HBM_PEAK_GBPS,
         "mean_active_per_layer": act_bundles / (args.steps * c.L),

@@ -30,7 +30,7 @@ _NAMES = {0: "NP_OK", 1: "NP_EINVAL", 2: "NP_ECAPACITY", 3: "NP_ENOMEM", 4: "NP_
 EXPORTS = ["np_layer_create", "np_layer_destroy", "np_layer_reset", "np_delta_assign",
            "np_scatter_rows", "np_sparse_ffn", "np_decode_step", "np_layer_read_state",
            "np_layer_read_rows", "np_layer_info", "np_layer_counters", "np_layer_set_ffn_shape", "np_last_error",
-           "np_probe_read", "np_probe_copy", "np_decode_use_graphs"]
+           "np_probe_read", "np_probe_copy", "np_decode_use_graphs", "np_layer_set_window"]
 
 
 class NPError(RuntimeError):
@@ -69,6 +69,7 @@ def lib() -> ctypes.CDLL:
         "np_probe_read": [vp, i64, vp, vp],
         "np_probe_copy": [vp, vp, i64, vp],
         "np_decode_use_graphs": [i32],
+        "np_layer_set_window": [vp, i32],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -132,6 +133,10 @@ class Layer:
 
     def set_ffn_shape(self, slots_per_wg: int = 0, tile_cols: int = 0, threads: int = 0) -> None:
         _check(lib().np_layer_set_ffn_shape(self.h, slots_per_wg, tile_cols, threads))
+
+    def set_window(self, window: int) -> None:
+        """Residency window in tokens (1 = the buffer holds exactly the active set)."""
+        _check(lib().np_layer_set_window(self.h, window))
 
     def info(self) -> dict:
         out = np.zeros(6, dtype=np.int32)

@@ -85,7 +85,11 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
     __shared__ uint64_t s_F0[kMaxKWords];  // free slots after the release
     __shared__ uint64_t s_F1[kMaxKWords];  // free slots after the assignment
     __shared__ int s_fpre[kMaxKWords];     // exclusive prefix of |F0| per word
-    __shared__ int s_opre[kMaxKWords];     // exclusive prefix of occupied slots per word
+    __shared__ int s_opre[kMaxKWords];     // exclusive prefix of active slots per word
+    __shared__ uint64_t s_Rn[kMaxWords];   // the new resident set R_t
+    __shared__ uint64_t s_Ab[kMaxKWords];  // slots holding an active neuron (the FFN's list)
+    __shared__ int s_cnt[kMaxWindow];      // window: retained candidates per age
+    __shared__ int s_nS, s_jstar, s_allow;
     __shared__ int s_tmp[2 * kWaves];
     __shared__ int s_err;
 
@@ -102,7 +106,13 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
     auto* const counts = gmem(L.counts);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int M = L.M, K = L.K, W = L.W, Kw = L.Kw;
-    if (tid == 0) s_err = 0;
+    if (tid == 0) {
+        s_err = 0;
+        s_nS = 0;
+    }
+    if (tid < kMaxWindow) s_cnt[tid] = 0;
+    const int win = L.window;
+    const int tok = counts[4];  // tokens assigned before this one
     const int32_t cg = a.prm ? gmem(a.prm)->cid[a.layer0 + blockIdx.x][0] : a.cid[blockIdx.x][0];
     const int32_t cu = a.prm ? gmem(a.prm)->cid[a.layer0 + blockIdx.x][1] : a.cid[blockIdx.x][1];
 
@@ -118,24 +128,110 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
         s_S[w] = L.mode == 0 ? (ga | gb) : L.mode == 1 ? (ga & gb) : ga;
         s_R[w] = res[w];
     }
-    for (int v = tid; v < Kw; v += kNT) s_Fa[v] = s_F0[v] = freeb[v];
+    for (int v = tid; v < Kw; v += kNT) {
+        s_Fa[v] = s_F0[v] = freeb[v];
+        s_Ab[v] = 0;
+    }
     __syncthreads();
 
-    // Step 2: D_in = S \ R and D_out = R \ S in ascending order. Each thread takes a
-    // contiguous range of words (sparse in practice), a workgroup scan gives list offsets.
+    // Step 1b: the resident set R_t this token moves to. Exactly S (section 3.4), or with a
+    // window of k tokens (LLM in a flash, section 3.1) S plus the resident neurons last active
+    // j = 1 .. k-1 tokens ago, the most recent first and by ascending ID within one j, while
+    // |R_t| <= K. The active sets of the last k-1 tokens are kept as bit masks in a ring, so
+    // the age class of a neuron is the first earlier mask that holds it.
     const int wpt = (W + kNT - 1) / kNT;
     const int w0 = min(tid * wpt, W), w1 = min(w0 + wpt, W);
+    if (win > 1) {
+        const auto* ring = gmem(L.ring);
+        const int nj = min(win - 1, tok);  // earlier tokens that exist
+        auto ring_word = [&](int j, int w) { return ring[(size_t)((tok - j) % (win - 1)) * W + w]; };
+        int cnt[kMaxWindow];
+#pragma unroll
+        for (int j = 0; j < kMaxWindow; ++j) cnt[j] = 0;
+        int c_s = 0;
+        for (int w = w0; w < w1; ++w) {
+            const uint64_t base = s_R[w] & ~s_S[w];
+            uint64_t covered = 0;
+            c_s += __popcll(s_S[w]);
+#pragma unroll
+            for (int j = 1; j < kMaxWindow; ++j) {
+                if (j > nj) break;
+                const uint64_t A = ring_word(j, w);
+                cnt[j] += __popcll(A & base & ~covered);
+                covered |= A;
+            }
+        }
+        atomicAdd(&s_nS, c_s);
+#pragma unroll
+        for (int j = 1; j < kMaxWindow; ++j)
+            if (cnt[j]) atomicAdd(&s_cnt[j], cnt[j]);
+        __syncthreads();
+        if (tid == 0) {
+            int room = K - s_nS, js = kMaxWindow, allow = 0;
+            for (int j = 1; j <= nj; ++j) {
+                if (s_cnt[j] <= room) {
+                    room -= s_cnt[j];
+                } else {
+                    js = j;
+                    allow = room;
+                    break;
+                }
+            }
+            s_jstar = js;
+            s_allow = allow;
+        }
+        __syncthreads();
+        const int js = s_jstar, allow = s_allow;
+        // the cut age class keeps its lowest IDs: a workgroup scan of its per-thread counts
+        int c_cut = 0;
+        if (js <= nj)
+            for (int w = w0; w < w1; ++w) {
+                const uint64_t base = s_R[w] & ~s_S[w];
+                uint64_t covered = 0;
+                for (int j = 1; j <= js; ++j) {
+                    const uint64_t A = ring_word(j, w);
+                    if (j == js) c_cut += __popcll(A & base & ~covered);
+                    covered |= A;
+                }
+            }
+        int pre_cut, unused_e, unused_a, unused_b;
+        block_excl_scan2(c_cut, 0, &pre_cut, &unused_e, &unused_a, &unused_b, s_tmp);
+        for (int w = w0; w < w1; ++w) {
+            const uint64_t base = s_R[w] & ~s_S[w];
+            uint64_t covered = 0, kept = 0;
+            for (int j = 1; j <= min(js, nj); ++j) {
+                const uint64_t A = ring_word(j, w);
+                const uint64_t E = A & base & ~covered;
+                covered |= A;
+                if (j < js) {
+                    kept |= E;
+                } else {
+                    const int take = min(max(allow - pre_cut, 0), __popcll(E));
+                    kept |= E ^ drop_low_bits(E, take);  // the take lowest bits of E
+                    pre_cut += __popcll(E);
+                }
+            }
+            s_Rn[w] = s_S[w] | kept;
+        }
+    } else {
+        for (int w = w0; w < w1; ++w) s_Rn[w] = s_S[w];
+    }
+    __syncthreads();
+
+    // Step 2: D_in = S \ R and D_out = R \ R_t in ascending order (R_t = S without a
+    // window). Each thread takes a contiguous range of words (sparse in practice), a
+    // workgroup scan gives list offsets.
     int c_in = 0, c_out = 0;
     for (int w = w0; w < w1; ++w) {
         c_in += __popcll(s_S[w] & ~s_R[w]);
-        c_out += __popcll(s_R[w] & ~s_S[w]);
+        c_out += __popcll(s_R[w] & ~s_Rn[w]);
     }
     int base_in, base_out, n_in, n_out;
     block_excl_scan2(c_in, c_out, &base_in, &base_out, &n_in, &n_out, s_tmp);
     {
         int ki = base_in, ko = base_out;
         for (int w = w0; w < w1; ++w) {
-            uint64_t bi = s_S[w] & ~s_R[w], bo = s_R[w] & ~s_S[w];
+            uint64_t bi = s_S[w] & ~s_R[w], bo = s_R[w] & ~s_Rn[w];
             while (bi) {
                 d_in[ki++] = w * 64 + (__ffsll((unsigned long long)bi) - 1);
                 bi &= bi - 1;
@@ -147,35 +243,42 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
         }
     }
 
-    // Step 3: release the slots whose owner leaves the active set (slot map -1, free bit;
+    // Step 3: release the slots whose owner leaves the resident set (slot map -1, free bit;
     // the owner entry is cleared below unless the slot is taken again). Every slot is
     // looked at once, so the owners of D_out are found without a slot-map lookup each.
     // (An owner that is not a resident neuron would be released too; the released count is
     // checked against |D_out| below.)
-    auto leaves = [&](int sl, int n) -> bool {
-        if (sl >= K || n < 0) return false;
+    // A slot whose owner stays and is active this token is marked in s_Ab (the FFN's list).
+    // 0: slot free or owner stays inactive, 1: owner leaves, 2: owner stays and is active.
+    auto fate = [&](int sl, int n) -> int {
+        if (sl >= K || n < 0) return 0;
         if (n >= M) {
             atomicOr(&s_err, kErrBadList);
-            return false;
+            return 0;
         }
-        return (s_S[n >> 6] & (1ull << (n & 63))) == 0;
+        const uint64_t bit = 1ull << (n & 63);
+        if ((s_Rn[n >> 6] & bit) == 0) return 1;
+        return (s_S[n >> 6] & bit) ? 2 : 0;
     };
     int c_rel = 0;
     {
-        bool lv[kOwnRegs];
+        int fv[kOwnRegs];
 #pragma unroll
-        for (int k = 0; k < kOwnRegs; ++k) lv[k] = leaves(tid + k * kNT, own[k]);
+        for (int k = 0; k < kOwnRegs; ++k) fv[k] = fate(tid + k * kNT, own[k]);
 #pragma unroll
         for (int k = 0; k < kOwnRegs; ++k) {
-            if (!lv[k]) continue;
             const int sl = tid + k * kNT;
+            if (fv[k] == 2) atomicOr((unsigned long long*)&s_Ab[sl >> 6], 1ull << (sl & 63));
+            if (fv[k] != 1) continue;
             slot_map[own[k]] = -1;
             atomicOr((unsigned long long*)&s_F0[sl >> 6], 1ull << (sl & 63));
             ++c_rel;
         }
         for (int sl = tid + kOwnRegs * kNT; sl < K; sl += kNT) {
             const int n = owner[sl];
-            if (!leaves(sl, n)) continue;
+            const int f = fate(sl, n);
+            if (f == 2) atomicOr((unsigned long long*)&s_Ab[sl >> 6], 1ull << (sl & 63));
+            if (f != 1) continue;
             slot_map[n] = -1;
             atomicOr((unsigned long long*)&s_F0[sl >> 6], 1ull << (sl & 63));
             ++c_rel;
@@ -186,14 +289,15 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
     // released count is checked against |D_out|.
     const int kpt = (Kw + kNT - 1) / kNT;
     const int v0 = min(tid * kpt, Kw), v1 = min(v0 + kpt, Kw);
-    __syncthreads();  // the releases' free bits are in s_F0
+    __syncthreads();  // the releases' free bits are in s_F0, the kept active slots in s_Ab
     int c_free = 0;
     for (int v = v0; v < v1; ++v) c_free += __popcll(s_F0[v]);
     int pre_free, pre_rel, n_free, n_rel;
     block_excl_scan2(c_free, c_rel, &pre_free, &pre_rel, &n_free, &n_rel, s_tmp);
     if (tid == 0 && n_rel != n_out) atomicOr(&s_err, kErrBadList);
 
-    // Step 4 (set part): the n_in lowest free slots are taken; occupied slots per word.
+    // Step 4 (set part): the n_in lowest free slots are taken (they join the active slots);
+    // active slots per word.
     int c_occ = 0;
     for (int v = v0; v < v1; ++v) {
         s_fpre[v] = pre_free;
@@ -202,7 +306,8 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
         const uint64_t fw = drop_low_bits(s_F0[v], take);
         s_F1[v] = fw;
         freeb[v] = fw;
-        c_occ += __popcll(~fw & valid_bits(v, Kw, K));
+        s_Ab[v] |= s_F0[v] & ~fw;
+        c_occ += __popcll(s_Ab[v]);
         uint64_t gone = s_F0[v] & ~s_Fa[v] & fw;  // released and not taken again: no owner
         while (gone) {
             owner[v * 64 + __ffsll((unsigned long long)gone) - 1] = -1;
@@ -210,17 +315,17 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
         }
     }
     int pre_occ, unused_e, n_act, unused_t;
-    block_excl_scan2(c_occ, 0, &pre_occ, &unused_e, &n_act, &unused_t, s_tmp);  // publishes s_fpre, s_F1
+    block_excl_scan2(c_occ, 0, &pre_occ, &unused_e, &n_act, &unused_t, s_tmp);  // publishes s_fpre, s_F1, s_Ab
     for (int v = v0; v < v1; ++v) {
         s_opre[v] = pre_occ;
-        pre_occ += __popcll(~s_F1[v] & valid_bits(v, Kw, K));
+        pre_occ += __popcll(s_Ab[v]);
     }
     __syncthreads();
 
     // Step 4 (lists): the i-th incoming neuron (ascending) takes the i-th free slot
     // (ascending). A thread's incoming neurons have consecutive indexes, so after one
     // search for the first slot it walks the free bits. The slot's position in the
-    // ascending occupied-slot list gets the neuron ID in act_src, so that the FFN can read
+    // ascending active-slot list gets the neuron ID in act_src, so that the FFN can read
     // the new bundle where it still is (the row store).
     {
         int idx = base_in;
@@ -249,7 +354,7 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
                 const int b = __ffsll((unsigned long long)fw) - 1;
                 fw &= fw - 1;
                 const int slot = lo * 64 + b;
-                const int pos = s_opre[lo] + __popcll(~s_F1[lo] & ((1ull << b) - 1));
+                const int pos = s_opre[lo] + __popcll(s_Ab[lo] & ((1ull << b) - 1));
                 slot_in[idx] = slot;
                 slot_map[n] = slot;
                 owner[slot] = n;
@@ -258,8 +363,8 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
             }
         }
     }
-    // Occupied slots in ascending order, one word per wave and one slot per lane; slots
-    // kept from the last step have act_src -1.
+    // Active slots in ascending order (without a window: every occupied slot), one word per
+    // wave and one slot per lane; slots kept from the last step have act_src -1.
     {
         constexpr int kU = 4;  // words per wave per round, their LDS reads issued together
         const uint64_t bit = 1ull << lane;
@@ -269,7 +374,7 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
                 const int v = min(v0w + u, Kw - 1);
-                occ[u] = v0w + u < Kw ? ~s_F1[v] & valid_bits(v, Kw, K) : 0;
+                occ[u] = v0w + u < Kw ? s_Ab[v] : 0;
                 taken[u] = s_F0[v] & ~s_F1[v];
                 o0[u] = s_opre[v];
             }
@@ -284,14 +389,21 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
         }
     }
 
-    // Step 5: R = S.
-    for (int w = tid; w < W; w += kNT) res[w] = s_S[w];
+    // Step 5: R = R_t; with a window, S joins the ring of recent active sets.
+    for (int w = tid; w < W; w += kNT) {
+        res[w] = s_Rn[w];
+        if (win > 1) gmem(L.ring)[(size_t)(tok % (win - 1)) * W + w] = s_S[w];
+    }
     __syncthreads();
     if (tid == 0) {
         counts[0] = n_in;
         counts[1] = n_out;
         counts[2] = n_act;
+        counts[4] = tok + 1;
         if (s_err) atomicOr(&L.counts[3], s_err);
+        auto* acc = gmem(L.acc);
+        acc[0] += (unsigned long long)n_act;
+        acc[1] += (unsigned long long)n_in;
     }
 }
 

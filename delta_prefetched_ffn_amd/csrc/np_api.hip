@@ -59,6 +59,7 @@ struct DeviceGuard {
 };
 
 enum LayerState { kFresh = 0, kAssigned = 1, kScattered = 2 };
+constexpr size_t kCountsBytes = 8 * 4 + 2 * 8;  // int32 counts[8] + 2 x uint64 running sums
 
 constexpr int kDefaultSlotsPerWg = 0;  // 0: one workgroup per compute unit
 constexpr int kDefaultTileCols = 256;
@@ -83,7 +84,10 @@ struct np_layer {
     uint64_t* res = nullptr;
     uint64_t* freeb = nullptr;
     int32_t* lists = nullptr;  // d_in | slot_in | d_out | act | act_src, K each
-    int32_t* counts = nullptr;
+    int32_t* counts = nullptr;  // int32 [8], then the two 64-bit running sums (LayerDev::acc)
+    uint64_t* ring = nullptr;   // window > 1: [window - 1][W] recent active sets
+    int window = 1;
+    LayerDev ldh{};             // host copy of *ldev
     uint64_t* hpair = nullptr;
     uint64_t* ppair = nullptr;
     uint32_t ffn_seq = 0;
@@ -174,7 +178,7 @@ np_status alloc_ffn_scratch(np_layer* L) {
 
 void free_layer(np_layer* L) {
     void* ptrs[] = {L->d_masks, L->buf, L->slot_map, L->owner, L->res, L->freeb, L->lists,
-                    L->counts, L->hpair, L->ppair, L->ldev};
+                    L->counts, L->ring, L->hpair, L->ppair, L->ldev};
     for (void* p : ptrs)
         if (p) (void)hipFree(p);
     if (L->ev_scatter) (void)hipEventDestroy(L->ev_scatter);
@@ -192,7 +196,8 @@ np_status init_state(np_layer* L) {
     if (K & 63) fb[L->Kw - 1] = (1ull << (K & 63)) - 1;
     NP_HIP(hipMemcpy(L->freeb, fb.data(), (size_t)L->Kw * 8, hipMemcpyHostToDevice));
     NP_HIP(hipMemset(L->lists, 0, (size_t)5 * K * 4));
-    NP_HIP(hipMemset(L->counts, 0, 4 * 4));
+    NP_HIP(hipMemset(L->counts, 0, kCountsBytes));
+    if (L->ring) NP_HIP(hipMemset(L->ring, 0, (size_t)(L->window - 1) * L->W * 8));
     NP_HIP(hipDeviceSynchronize());
     std::fill(L->h_res.begin(), L->h_res.end(), 0ull);
     L->n_active = 0;
@@ -281,7 +286,7 @@ np_status enqueue_ffn(np_layer* L, const float* x, float* y, hipStream_t s, cons
 }
 
 np_status enqueue_scatter(np_layer* L, hipStream_t s, bool fixed_grid = false) {
-    const int grid = fixed_grid ? std::max(1, std::min(L->desc.k_max, 1024)) : scatter_grid(L->n_in);
+    const int grid = fixed_grid || L->n_in < 0 ? std::max(1, std::min(L->desc.k_max, 1024)) : scatter_grid(L->n_in);
     NP_HIP(launch_scatter(L->counts, L->d_in(), L->slot_in(), L->store_dev, L->buf, L->desc.d_ff,
                           L->desc.k_max, (int32_t)L->bundle_elems(), grid, s));
     return NP_OK;
@@ -560,7 +565,7 @@ np_status np_layer_create(const np_layer_desc* desc, np_layer** out) {
     bool ok = dmalloc((void**)&L->d_masks, mask_words * 8) && dmalloc((void**)&L->buf, buf_bytes) &&
               dmalloc((void**)&L->slot_map, (size_t)M * 4) && dmalloc((void**)&L->owner, (size_t)K * 4) &&
               dmalloc((void**)&L->res, (size_t)L->W * 8) && dmalloc((void**)&L->freeb, (size_t)L->Kw * 8) &&
-              dmalloc((void**)&L->lists, (size_t)5 * K * 4) && dmalloc((void**)&L->counts, 4 * 4) &&
+              dmalloc((void**)&L->lists, (size_t)5 * K * 4) && dmalloc((void**)&L->counts, kCountsBytes) &&
               dmalloc((void**)&L->hpair, (size_t)K * 8) &&
               dmalloc((void**)&L->ldev, sizeof(LayerDev));
     if (!ok) {
@@ -584,6 +589,9 @@ np_status np_layer_create(const np_layer_desc* desc, np_layer** out) {
     ld.act = L->act();
     ld.act_src = L->act_src();
     ld.counts = L->counts;
+    ld.acc = reinterpret_cast<unsigned long long*>(L->counts + 8);
+    ld.ring = nullptr;
+    ld.window = 1;
     ld.W = L->W;
     ld.Kw = L->Kw;
     ld.M = M;
@@ -595,7 +603,7 @@ np_status np_layer_create(const np_layer_desc* desc, np_layer** out) {
     ld.store = L->store_dev;
     ld.buf = L->buf;
     ld.bundle16 = (int32_t)(L->bundle_elems() / 8);
-    ld.pad2 = 0;
+    L->ldh = ld;
     hipError_t e = hipMemcpy(L->ldev, &ld, sizeof ld, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy(L->d_masks, L->h_masks.data(), mask_words * 8, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemset(L->hpair, 0, (size_t)K * 8);
@@ -676,8 +684,11 @@ np_status np_delta_assign(np_layer* L, int32_t gate_cid, int32_t up_cid, void* s
     const int n = combine_host(L, gate_cid, u, S.data());
     if (n > L->desc.k_max)
         return fail(NP_ECAPACITY, "|S| = %d exceeds k_max = %d", n, L->desc.k_max);
-    int n_in = 0;
-    for (int w = 0; w < L->W; ++w) n_in += __builtin_popcountll(S[w] & ~L->h_res[w]);
+    int n_in = -1;  // with a window the resident set is decided on the device
+    if (L->window == 1) {
+        n_in = 0;
+        for (int w = 0; w < L->W; ++w) n_in += __builtin_popcountll(S[w] & ~L->h_res[w]);
+    }
     DeviceGuard g(L->desc.device);
     DeltaLaunch a{};
     a.layers[0] = L->ldev;
@@ -689,7 +700,7 @@ np_status np_delta_assign(np_layer* L, int32_t gate_cid, int32_t up_cid, void* s
     L->n_active = n;
     L->n_in = n_in;
     L->total_active += n;
-    L->total_in += n_in;
+    L->total_in += std::max(n_in, 0);
     L->state = kAssigned;
     return NP_OK;
 }
@@ -743,8 +754,11 @@ np_status np_decode_step(np_layer* const* layers, int32_t n_layers, const int32_
         n_act[l] = combine_host(L, cids[2 * l], u, S[l].data());
         if (n_act[l] > L->desc.k_max)
             return fail(NP_ECAPACITY, "layer %d: |S| = %d exceeds k_max = %d", l, n_act[l], L->desc.k_max);
-        int ni = 0;
-        for (int w = 0; w < L->W; ++w) ni += __builtin_popcountll(S[l][w] & ~L->h_res[w]);
+        int ni = -1;  // with a window the resident set is decided on the device
+        if (L->window == 1) {
+            ni = 0;
+            for (int w = 0; w < L->W; ++w) ni += __builtin_popcountll(S[l][w] & ~L->h_res[w]);
+        }
         n_in[l] = ni;
     }
     DeviceGuard g(dev);
@@ -756,7 +770,7 @@ np_status np_decode_step(np_layer* const* layers, int32_t n_layers, const int32_
             L->n_active = n_act[l];
             L->n_in = n_in[l];
             L->total_active += n_act[l];
-            L->total_in += n_in[l];
+            L->total_in += std::max(n_in[l], 0);
             L->state = kAssigned;
         }
     };
@@ -863,6 +877,11 @@ np_status np_layer_info(const np_layer* L, int32_t* out6) {
     out6[3] = L->desc.n_rows;
     out6[4] = L->n_active;
     out6[5] = L->n_in;
+    if (L->window > 1 && L->state != kFresh) {  // |D_in| is decided on the device
+        DeviceGuard g(L->desc.device);
+        NP_HIP(hipDeviceSynchronize());
+        NP_HIP(hipMemcpy(&out6[5], L->counts, 4, hipMemcpyDeviceToHost));
+    }
     return NP_OK;
 }
 
@@ -870,6 +889,47 @@ np_status np_layer_counters(const np_layer* L, int64_t* out2) {
     if (!L || !out2) return fail(NP_EINVAL, "layer and out must not be NULL");
     out2[0] = L->total_active;
     out2[1] = L->total_in;
+    if (L->window > 1) {  // |D_in| is decided on the device: its running sum lives there
+        DeviceGuard g(L->desc.device);
+        NP_HIP(hipDeviceSynchronize());
+        unsigned long long acc[2];
+        NP_HIP(hipMemcpy(acc, L->counts + 8, sizeof acc, hipMemcpyDeviceToHost));
+        out2[1] = (int64_t)acc[1];
+    }
+    return NP_OK;
+}
+
+np_status np_layer_set_window(np_layer* L, int32_t window) {
+    if (!L) return fail(NP_EINVAL, "layer must not be NULL");
+    if (window < 1 || window > kMaxWindow) return fail(NP_EINVAL, "window=%d must be in [1, %d]", window, kMaxWindow);
+    if (L->state != kFresh) return fail(NP_ESTATE, "set the window before the first np_delta_assign (or after np_layer_reset)");
+    DeviceGuard g(L->desc.device);
+    NP_HIP(hipDeviceSynchronize());
+    uint64_t* ring = nullptr;
+    if (window > 1) {
+        const size_t bytes = (size_t)(window - 1) * L->W * 8;
+        if (hipMalloc(&ring, bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(NP_ENOMEM, "cannot allocate the %zu-byte window ring", bytes);
+        }
+        if (hipMemset(ring, 0, bytes) != hipSuccess) {
+            (void)hipFree(ring);
+            return fail(NP_EHIP, "window ring clear failed");
+        }
+    }
+    LayerDev ld = L->ldh;
+    ld.ring = ring;
+    ld.window = window;
+    if (hipMemcpy(L->ldev, &ld, sizeof ld, hipMemcpyHostToDevice) != hipSuccess) {
+        if (ring) (void)hipFree(ring);
+        return fail(NP_EHIP, "layer descriptor update failed");
+    }
+    if (L->ring) (void)hipFree(L->ring);
+    L->ring = ring;
+    L->window = window;
+    L->ldh = ld;
+    NP_HIP(hipMemset(L->counts, 0, kCountsBytes));  // token count and running sums restart
+    ++L->version;
     return NP_OK;
 }
 

@@ -14,6 +14,7 @@ constexpr int kMaxCentroids = 65536;
 constexpr int kMaxWords = kMaxDff / 64;  // mask words per set
 constexpr int kMaxKWords = kMaxKmax / 64;
 constexpr int kMaxLayersPerLaunch = 64;
+constexpr int kMaxWindow = 16;             // residency window, tokens
 constexpr uint64_t kMaxBufBytes = (1ull << 32) - 4096;  // slot buffer addressed by 32-bit offsets
 
 // Device error bits (counts[3]).
@@ -35,13 +36,15 @@ struct LayerDev {
     int32_t* d_out;          // [K]
     int32_t* act;            // [K] ascending occupied slots
     int32_t* act_src;        // [K] per act position: the neuron if its slot was filled this step, else -1
-    int32_t* counts;         // [4] n_in, n_out, n_active, error bits
+    int32_t* counts;         // [8] n_in, n_out, n_active, error bits, tokens assigned
+    unsigned long long* acc; // [2] running sums of n_active and n_in
+    uint64_t* ring;          // [window - 1][W] active sets of the last tokens (window > 1)
     int32_t W, Kw, M, K;
     int32_t mode, n_tables, C, pad;
     const uint16_t* store;   // backing row store (device address; may be mapped host memory)
     uint16_t* buf;           // [K][R][d] slot buffer
     int32_t bundle16;        // 16-byte chunks per bundle
-    int32_t pad2;
+    int32_t window;          // residency window in tokens (1: the buffer holds exactly S)
 };
 
 // One launch scattering the deltas of many layers (blockIdx.y = layer).

@@ -112,10 +112,12 @@ np_status np_layer_reset(np_layer* layer);
 
 /* Steps 1-3 for one layer (section 3.4). Builds S from mask gate_cid of the
  * gate table and up_cid of the up table (up_cid is ignored for SINGLE),
- * computes D_in = S \ R and D_out = R \ S in ascending neuron order,
- * releases the slots of D_out, gives the i-th neuron of D_in the i-th free
- * slot in ascending slot order, updates the slot map and owner table, and
- * lists the occupied slots in ascending order. Then R = S.
+ * picks the new resident set R' (R' = S, or with a residency window see
+ * np_layer_set_window), computes D_in = S \ R and D_out = R \ R' in
+ * ascending neuron order, releases the slots of D_out, gives the i-th neuron
+ * of D_in the i-th free slot in ascending slot order, updates the slot map
+ * and owner table, and lists the slots of S in ascending slot order (the rows
+ * the FFN reads). Then R = R'.
  * Errors: NP_EINVAL (cid out of range), NP_ECAPACITY (|S| > k_max; state
  * unchanged), NP_ESTATE (the previous assignment has not been scattered). */
 np_status np_delta_assign(np_layer* layer, int32_t gate_cid, int32_t up_cid, void* stream);
@@ -170,7 +172,8 @@ np_status np_decode_use_graphs(int32_t enable);
 /* Synchronizes the layer's device, then copies the current state to host
  * buffers (any pointer may be NULL): slot_map int32 [d_ff], owner int32
  * [k_max], d_in / slot_in / d_out int32 [k_max] (lists of the last
- * assignment), act_slots int32 [k_max] (ascending occupied slots), counts
+ * assignment), act_slots int32 [k_max] (ascending slots of S; with window 1
+ * these are all occupied slots), counts
  * int32 [4] = {n_in, n_out, n_active, device error bits}.
  * Returns NP_EDEVICE if a kernel of this layer reported an inconsistency
  * (nonzero error bits; the data is still copied). */
@@ -187,10 +190,24 @@ np_status np_layer_read_rows(const np_layer* layer, const int32_t* slots, int32_
  * last accepted assignment, n_in of the last accepted assignment}. */
 np_status np_layer_info(const np_layer* layer, int32_t* out6);
 
-/* Host-side running totals since create/reset: out2[0] = sum of |S| and
- * out2[1] = sum of |D_in| over every accepted assignment (bundles read by the
- * FFN and bundles written by the scatter, in units of one bundle). */
+/* Running totals since create/reset: out2[0] = sum of |S| and out2[1] = sum
+ * of |D_in| over every accepted assignment (bundles read by the FFN and
+ * bundles written by the scatter, in units of one bundle). Host-side and
+ * non-blocking with window 1; with a window, |D_in| is known on the device
+ * only and the call synchronizes the layer's device. */
 np_status np_layer_counters(const np_layer* layer, int64_t* out2);
+
+/* Residency window (LLM in a flash, section 3.1 "Windowing"): besides S, the
+ * buffer keeps the resident neurons that were active in the last window - 1
+ * tokens, the most recently active first and by ascending neuron ID within
+ * one token, as long as at most k_max neurons are resident. Kept neurons
+ * cost no transfer when they become active again; a neuron that left is only
+ * loaded again when it is active. window = 1 (the default) is the exact rule
+ * of section 3.4: the buffer holds S. 1 <= window <= 16. Only before the
+ * first np_delta_assign after create or reset (NP_ESTATE otherwise).
+ * Synchronizes the layer's device. With window > 1, np_layer_info's n_in and
+ * np_layer_counters' |D_in| are read back from the device. */
+np_status np_layer_set_window(np_layer* layer, int32_t window);
 
 /* FFN launch shape of this layer: about slots_per_wg active slots per
  * workgroup for the gate/up phase (1..16; the default, -1, sizes the grid to

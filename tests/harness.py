@@ -54,10 +54,11 @@ def make_layer(wl: Workload, l: int, where: str = "device", store: np.ndarray | 
 class OracleRun:
     """The oracle's state for every layer of a workload."""
 
-    def __init__(self, wl: Workload, keep_buffer: bool = True):
+    def __init__(self, wl: Workload, keep_buffer: bool = True, window: int = 1):
         c = wl.cfg
         self.wl = wl
-        self.layers = [O.OracleLayer(c.M, c.K, c.R, c.d, keep_buffer=keep_buffer) for _ in range(c.L)]
+        self.layers = [O.OracleLayer(c.M, c.K, c.R, c.d, keep_buffer=keep_buffer, window=window)
+                       for _ in range(c.L)]
         self.mode = O.MODES[c.mode]
 
     def active(self, t: int, l: int) -> np.ndarray:
@@ -80,5 +81,7 @@ def compare_state(st: dict, ol: O.OracleLayer, res: O.StepResult, S: np.ndarray,
     assert np.array_equal(st["d_out"], res.d_out), f"{what}: d_out differs"
     assert np.array_equal(st["slot_map"], ol.slot_map), f"{what}: slot_map differs"
     assert np.array_equal(st["owner"], ol.owner), f"{what}: owner differs"
-    assert np.array_equal(st["act"], ol.occupied_slots()), f"{what}: active slot list differs"
+    assert np.array_equal(st["act"], ol.active_slots(S)), f"{what}: active slot list differs"
+    if ol.window == 1:
+        assert np.array_equal(st["act"], ol.occupied_slots()), f"{what}: occupied slots differ"
     assert st["act"].size == S.size

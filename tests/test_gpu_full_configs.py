@@ -23,7 +23,7 @@ def _log(msg):
     print(f"[full-config] {msg}", flush=True)
 
 
-def run_full(num: int, where: str = "device", steps: int | None = None, ffn_samples: int = 10):
+def run_full(num: int, where: str = "device", steps: int | None = None, ffn_samples: int = 10, window: int = 1):
     from delta_prefetched_ffn_amd import binding as B
     torch = torch_mod()
     assert torch.cuda.is_available()
@@ -34,8 +34,10 @@ def run_full(num: int, where: str = "device", steps: int | None = None, ffn_samp
     layers = []
     for l in range(c.L):
         layers.append(make_layer(wl, l, where)[0])
+        if window > 1:
+            layers[-1].set_window(window)
     _log(f"config {num}: {c.L} layers built ({where} store) in {time.time() - t0:.1f}s")
-    orc = OracleRun(wl, keep_buffer=False)
+    orc = OracleRun(wl, keep_buffer=False, window=window)
     x_all = wl.x_all()[:T]
     x = torch.from_numpy(np.ascontiguousarray(x_all)).cuda()
     y = torch.zeros_like(x)
@@ -81,6 +83,13 @@ def run_full(num: int, where: str = "device", steps: int | None = None, ffn_samp
 @pytest.mark.parametrize("num", [2, 3, 4, 5, 6, 7, 8])
 def test_full_config_device_store(num):
     run_full(num, "device")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("num,window", [(2, 4), (9, 1), (9, 4)])
+def test_full_config_residency_window(num, window):
+    """Config 9 is the low-overlap stress case (persistence 0.40-0.50)."""
+    run_full(num, "device", window=window)
 
 
 @pytest.mark.timeout(600)

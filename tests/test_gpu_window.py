@@ -1,0 +1,113 @@
+"""GPU parity of the residency window (LLM in a flash section 3.1; the oracle's
+npo_window_target): delta lists, slot map, owner table, the FFN's slot list and the
+buffer bit-exact, y within max-abs 2e-2 / relative L2 5e-3, under capacity pressure,
+through np_decode_step (direct launches and graph replay) and the per-layer calls."""
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from tests.harness import OracleRun, check_y, compare_state, make_layer, torch_mod
+from workload.gen import Workload, small_config
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [
+    # |S| up to about 0.8 K_max: the window has to be trimmed on most tokens
+    small_config(920, L=2, d=512, M=600, K=150, C=6, mode="union", m=60, swap=10, T=12),
+    small_config(921, L=2, d=4096, M=1500, K=500, C=5, mode="union", m=200, swap=30, T=10),
+    small_config(922, L=1, d=1000, M=900, K=400, C=4, mode="intersect", m=380, swap=40, T=10, act="silu"),
+]
+
+
+@pytest.fixture(scope="module")
+def torch():
+    t = torch_mod()
+    assert t.cuda.is_available()
+    return t
+
+
+@pytest.mark.parametrize("window", [2, 4, 16])
+@pytest.mark.parametrize("path", ["direct", "graph", "calls"])
+@pytest.mark.parametrize("cfg", SHAPES, ids=lambda c: f"d{c.d}_M{c.M}_K{c.K}_{c.mode}")
+def test_window_parity(torch, cfg, path, window):
+    from delta_prefetched_ffn_amd import binding as B
+    B.decode_use_graphs(path == "graph")
+    wl = Workload(cfg)
+    layers, stores = zip(*[make_layer(wl, l) for l in range(cfg.L)])
+    for layer in layers:
+        layer.set_window(window)
+    orc = OracleRun(wl, window=window)
+    x_all = wl.x_all()
+    x = torch.from_numpy(x_all).cuda()
+    y = torch.zeros_like(x)
+    cs = torch.cuda.Stream()
+    loads = 0
+    for t in range(cfg.T):
+        if path == "calls":
+            for l, layer in enumerate(layers):
+                g, u = (int(v) for v in wl.cids()[t, l])
+                layer.delta_assign(g, u, cs.cuda_stream)
+                layer.sparse_ffn(x[t, l].data_ptr(), y[t, l].data_ptr(), cs.cuda_stream)  # read-through
+        else:
+            B.decode_step(layers, wl.cids()[t], x[t].data_ptr(), y[t].data_ptr(), cs.cuda_stream, cs.cuda_stream)
+        for l, layer in enumerate(layers):
+            st = layer.read_state()
+            S, res = orc.step(t, l, stores[l])
+            compare_state(st, orc.layers[l], res, S, f"w={window} t={t} l={l}")
+            assert np.array_equal(layer.read_rows(), orc.layers[l].buf), f"w={window} t={t} l={l}: buffer"
+            assert layer.info()["n_in"] == res.d_in.size
+            loads += res.d_in.size
+    torch.cuda.synchronize()
+    assert sum(layer.counters()[1] for layer in layers) == loads
+    yh = y.cpu().numpy()
+    for t in range(cfg.T):
+        for l in range(cfg.L):
+            S = orc.active(t, l)
+            check_y(yh[t, l], O.sparse_ffn(stores[l], cfg.R, cfg.d, S, x_all[t, l], cfg.act), f"t={t} l={l}")
+    for layer in layers:
+        layer.close()
+    B.decode_use_graphs(False)
+
+
+def test_window_reduces_loads_and_one_is_the_exact_rule(torch):
+    from delta_prefetched_ffn_amd import binding as B
+    cfg = SHAPES[0]
+    wl = Workload(cfg)
+    x = torch.from_numpy(wl.x_all()).cuda()
+    totals, outs = {}, {}
+    for window in (None, 1, 3):
+        layers = [make_layer(wl, l)[0] for l in range(cfg.L)]
+        if window is not None:
+            for layer in layers:
+                layer.set_window(window)
+        y = torch.zeros_like(x)
+        for t in range(cfg.T):
+            B.decode_step(layers, wl.cids()[t], x[t].data_ptr(), y[t].data_ptr(), 0, 0)
+        torch.cuda.synchronize()
+        totals[window] = sum(layer.counters()[1] for layer in layers)
+        outs[window] = y.cpu().numpy()
+        for layer in layers:
+            layer.close()
+    assert totals[None] == totals[1] and totals[3] < totals[1]
+    assert np.array_equal(outs[None].view(np.uint32), outs[1].view(np.uint32))
+
+
+def test_set_window_checks(torch):
+    from delta_prefetched_ffn_amd import binding as B
+    wl = Workload(SHAPES[0])
+    layer = make_layer(wl, 0)[0]
+    for bad in (0, 17, -1):
+        with pytest.raises(B.NPError) as e:
+            layer.set_window(bad)
+        assert e.value.status == B.NP_EINVAL
+    layer.set_window(4)
+    g, u = (int(v) for v in wl.cids()[0, 0])
+    layer.delta_assign(g, u, 0)
+    with pytest.raises(B.NPError) as e:
+        layer.set_window(2)                     # not before the first assignment
+    assert e.value.status == B.NP_ESTATE
+    layer.scatter_rows(0)
+    torch.cuda.synchronize()
+    layer.reset()
+    layer.set_window(2)                         # fine again after a reset
+    layer.close()

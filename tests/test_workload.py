@@ -84,8 +84,9 @@ def test_model_shaped_statistics(num, frac_lo, frac_hi):
     assert 0.82 <= p <= 0.85
 
 
-def test_trajectory_statistics():
-    c = CONFIGS[5]
+@pytest.mark.parametrize("num", [5, 9])
+def test_trajectory_statistics(num):
+    c = CONFIGS[num]
     wl = Workload(c)
     seqs = active_sets(wl, [0], c.T)
     sizes = {S.size for S in seqs[0]}
@@ -95,7 +96,7 @@ def test_trajectory_statistics():
         prev, S = seqs[0][t - 1], seqs[0][t]
         got = np.intersect1d(prev, S).size / prev.size
         assert abs(got - pt[t]) <= 1.0 / c.active
-        assert 0.70 - 1e-3 <= got <= 0.90 + 1e-3
+        assert c.p_lo - 1e-3 <= got <= c.p_hi + 1e-3
 
 
 def test_small_config_shapes():

@@ -162,6 +162,10 @@ CONFIGS = {
               mode="single", T=256, m=1065, swap=88),
     5: Config(5, "large d7168 M28672 low-overlap", L=47, d=7168, M=28672, R=3, K=6144, C=128,
               mode="union", T=128, recipe="trajectory", active=2867, p_lo=0.70, p_hi=0.90),
+    # The low-overlap stress case of DynamicInfer (adjacent-token Jaccard distance 0.70-0.75,
+    # i.e. about 45% persistence) at the Llama-2-7B shape.
+    9: Config(9, "Llama-2-7B-shaped low-overlap stress", L=31, d=4096, M=11008, R=3, K=4096, C=128,
+              mode="union", T=128, recipe="trajectory", active=1324, p_lo=0.40, p_hi=0.50),
     # The paper's own model shape (Mistral-7B: d 4096, d_ff 14336, SwiGLU), its active set the
     # intersection of the gate and up masks, at its three K_max budgets (62 / 50 / 31%
     # sparsity). Each mask keeps K_max - s members of a base set of K_max neurons; the

@@ -95,12 +95,12 @@ def stored_traffic(ffn_bytes_per_launch: float):
     return rec.get("traffic_bytes_per_launch"), rec.get("note", "")
 
 
-def cpu_baseline(wl, stores, seconds: float):
+def cpu_baseline(wl, stores, seconds: float, window: int = 1):
     """The CPU oracle, untouched, on a bounded sample of the same workload."""
     from oracle import oracle as O
     c = wl.cfg
     threads = max(1, min(16, os.cpu_count() or 1))
-    layers = [O.OracleLayer(c.M, c.K, c.R, c.d) for _ in range(c.L)]
+    layers = [O.OracleLayer(c.M, c.K, c.R, c.d, window=window) for _ in range(c.L)]
     mode = O.MODES[c.mode]
     cids = wl.cids()
     tabs = [wl.masks(l) for l in range(c.L)]
@@ -311,7 +311,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        cpu = cpu_baseline(wl, stores, args.cpu_seconds)
+        cpu = cpu_baseline(wl, stores, args.cpu_seconds, args.window)
         log(f"cpu baseline: {cpu['value']:.3f} tok/s on {cpu['cores']} threads")
 
     out = {

@@ -78,9 +78,15 @@ def token_ids(first: int, count: int, T: int) -> list[int]:
 
 
 def kernel_source_hash() -> str:
+    """Hash of what the sparse-FFN kernel is built from: k_ffn.hip and the launch structs
+    (FfnShape, FfnArgs) of np_internal.hpp."""
+    csrc = os.path.join(ROOT, "delta_prefetched_ffn_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("k_ffn.hip", "np_internal.hpp"):
-        h.update(open(os.path.join(ROOT, "delta_prefetched_ffn_amd", "csrc", f), "rb").read())
+    h.update(open(os.path.join(csrc, "k_ffn.hip"), "rb").read())
+    hdr = open(os.path.join(csrc, "np_internal.hpp")).read()
+    i = hdr.index("struct FfnShape")
+    j = hdr.index("};", hdr.index("struct FfnArgs")) + 2
+    h.update(hdr[i:j].encode())
     return h.hexdigest()[:16]
 
 

@@ -42,6 +42,8 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--config", type=int, default=DEFAULT_WORKLOAD, help="built-in workload number")
+    p.add_argument("--reduce", choices=["atomic", "ordered"], default="atomic",
+                   help="FFN partial-sum reduction: fp32 atomics (default) or fixed order (bit-reproducible)")
     p.add_argument("--window", type=int, default=1,
                    help="residency window in tokens (1: the buffer holds exactly the active set)")
     p.add_argument("--steps", type=int, default=200)
@@ -179,6 +181,7 @@ def main():
                 L.set_ffn_shape(args.slots_per_wg, args.tile_cols)
             if args.window != 1:
                 L.set_window(args.window)
+            L.set_ffn_reduce(args.reduce)
             out.append(L)
         return out
 
@@ -219,7 +222,9 @@ def main():
     # As in the decode step, each FFN follows its layer's delta assignment directly and reads
     # the new bundles through from the row store (writing them into their slots). Even tokens:
     # all 31 launches back to back between two events; odd tokens: each launch between its own
-    # events. Algorithmic bytes of a launch: active bundles read + new bundles written + x + y.
+    # events. y is cleared before the launches (a decode step clears it inside its assign
+    # launch) and each launch adds into it, as in a decode step. Algorithmic bytes of a launch:
+    # active bundles read + new bundles written + x + y.
     ffn_toks = token_ids(1 + args.warmup + args.steps, 2 * args.ffn_steps, c.T)
     s = cs
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(c.L)]
@@ -233,9 +238,11 @@ def main():
             info = L.info()
             ns.append((info["n_active"], info["n_in"]))
         if i % 2 == 0:
+            with torch.cuda.stream(s):
+                y[t].zero_()  # as a decode step's assign launch does, outside the timed launches
             burst[0].record(s)
             for l, L in enumerate(layers):
-                L.sparse_ffn(x[t, l].data_ptr(), y[t, l].data_ptr(), s.cuda_stream)
+                L.sparse_ffn_acc(x[t, l].data_ptr(), y[t, l].data_ptr(), s.cuda_stream)
             burst[1].record(s)
             s.synchronize()
             burst_ms += burst[0].elapsed_time(burst[1])
@@ -243,9 +250,11 @@ def main():
             burst_act_bytes += sum(na * c.bundle_bytes for na, _ in ns)
             burst_n += c.L
         else:
+            with torch.cuda.stream(s):
+                y[t].zero_()
             for l, L in enumerate(layers):
                 ev[l][0].record(s)
-                L.sparse_ffn(x[t, l].data_ptr(), y[t, l].data_ptr(), s.cuda_stream)
+                L.sparse_ffn_acc(x[t, l].data_ptr(), y[t, l].data_ptr(), s.cuda_stream)
                 ev[l][1].record(s)
             s.synchronize()
             event_ms += sum(a.elapsed_time(b) for a, b in ev)
@@ -336,7 +345,7 @@ def main():
         "config": {"workload": workload_text(c, act_bundles / (args.steps * c.L)),
                    "global_batch": 1, "layers": c.L, "d_model": c.d, "d_ff": c.M, "k_max": c.K,
                    "weights": "bf16", "backing_store": "HBM", "parallelism": "single GPU",
-                   "residency_window": args.window},
+                   "residency_window": args.window, "ffn_reduce": args.reduce},
         "effective_gbps": eff_gbps,
         "effective_frac_of_hbm_peak": eff_gbps / HBM_PEAK_GBPS,
         "mean_active_per_layer": act_bundles / (args.steps * c.L),

@@ -22,6 +22,8 @@ NP_OK, NP_EINVAL, NP_ECAPACITY, NP_ENOMEM, NP_EHIP, NP_ESTATE, NP_EDEVICE = rang
 MASK_UNION, MASK_INTERSECT, MASK_SINGLE = 0, 1, 2
 MODES = {"union": MASK_UNION, "intersect": MASK_INTERSECT, "single": MASK_SINGLE}
 ACT_RELU, ACT_SILU = 0, 1
+REDUCE_ATOMIC, REDUCE_ORDERED = 0, 1
+REDUCES = {"atomic": REDUCE_ATOMIC, "ordered": REDUCE_ORDERED}
 ACTS = {"relu": ACT_RELU, "silu": ACT_SILU}
 _NAMES = {0: "NP_OK", 1: "NP_EINVAL", 2: "NP_ECAPACITY", 3: "NP_ENOMEM", 4: "NP_EHIP",
           5: "NP_ESTATE", 6: "NP_EDEVICE"}
@@ -30,7 +32,8 @@ _NAMES = {0: "NP_OK", 1: "NP_EINVAL", 2: "NP_ECAPACITY", 3: "NP_ENOMEM", 4: "NP_
 EXPORTS = ["np_layer_create", "np_layer_destroy", "np_layer_reset", "np_delta_assign",
            "np_scatter_rows", "np_sparse_ffn", "np_decode_step", "np_layer_read_state",
            "np_layer_read_rows", "np_layer_info", "np_layer_counters", "np_layer_set_ffn_shape", "np_last_error",
-           "np_probe_read", "np_probe_copy", "np_decode_use_graphs", "np_layer_set_window"]
+           "np_probe_read", "np_probe_copy", "np_decode_use_graphs", "np_layer_set_window",
+           "np_sparse_ffn_acc", "np_layer_set_ffn_reduce"]
 
 
 class NPError(RuntimeError):
@@ -70,6 +73,8 @@ def lib() -> ctypes.CDLL:
         "np_probe_copy": [vp, vp, i64, vp],
         "np_decode_use_graphs": [i32],
         "np_layer_set_window": [vp, i32],
+        "np_sparse_ffn_acc": [vp, vp, vp, vp],
+        "np_layer_set_ffn_reduce": [vp, i32],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -133,6 +138,14 @@ class Layer:
 
     def set_ffn_shape(self, slots_per_wg: int = 0, tile_cols: int = 0, threads: int = 0) -> None:
         _check(lib().np_layer_set_ffn_shape(self.h, slots_per_wg, tile_cols, threads))
+
+    def sparse_ffn_acc(self, x_ptr: int, y_ptr: int, stream: int = 0) -> None:
+        """y += FFN(x)."""
+        _check(lib().np_sparse_ffn_acc(self.h, x_ptr, y_ptr, stream or None))
+
+    def set_ffn_reduce(self, mode: str) -> None:
+        """"atomic" (default; fp32 atomics, order free) or "ordered" (fixed order, bit-reproducible)."""
+        _check(lib().np_layer_set_ffn_reduce(self.h, REDUCES[mode]))
 
     def set_window(self, window: int) -> None:
         """Residency window in tokens (1 = the buffer holds exactly the active set)."""

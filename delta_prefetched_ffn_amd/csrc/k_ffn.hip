@@ -21,9 +21,11 @@
 //     [w - Q + 1, w] (phase 2). Its down-row loads are issued before phase 1,
 //     so they overlap the gate/up traffic.
 //   * Over the contributors of a tile (w = t, t + Q, ...) the windows cover
-//     every chunk exactly once. The highest contributor of a tile sums the
-//     tile's partials in ascending contributor order (fixed order: results are
-//     identical run to run) and writes y.
+//     every chunk exactly once. Ordered reduction: the highest contributor of a
+//     tile sums the tile's partials in ascending contributor order (fixed
+//     order: results are identical run to run) and writes y. Atomic reduction:
+//     every contributor adds its partial into y with float atomics, which saves
+//     the second exchange but leaves the order of the additions free.
 //
 // Read-through: in a decode step whose row store is device memory, a slot filled this
 // step is read from the row store (where its bundle already is) instead of from the slot
@@ -388,11 +390,19 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     __syncthreads();
 
     const int ncontrib = (a.nwg - 1 - t) / a.q + 1;
-    const bool reducer = w == t + a.q * (ncontrib - 1);
+    const bool reducer = !a.atomic_y && w == t + a.q * (ncontrib - 1);
     float own = 0.f;                          // this workgroup's partial of column tid (tid < tcols)
     if (tid < tcols) {
         for (int r = 0; r < RL2; ++r) own += s_red2[r * a.tw + tid];
-        if (!reducer) st_pair(&a.ppair[(size_t)w * a.tw + tid], seq, own);
+        if (a.atomic_y) {
+            // Atomic reduction: every contributor adds its partial into y (cleared before the
+            // launch or holding the value to add to). No exchange, no reducer; the order of
+            // the additions, and so the last bits of y, may differ from run to run.
+            float* yp = a.prm ? a.prm->y + (size_t)a.layer * a.d : a.y;
+            unsafeAtomicAdd(yp + col0 + tid, own);
+        } else if (!reducer) {
+            st_pair(&a.ppair[(size_t)w * a.tw + tid], seq, own);
+        }
     }
     if (reducer) {
         // The tile's highest contributor sums the other contributors' partials: G groups of
@@ -438,7 +448,8 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
             float yv = 0.f;
             for (int gg = 0; gg < G; ++gg) yv += s_red2[gg * a.tw + tid];
             auto* yg = gmem(a.prm ? a.prm->y + (size_t)a.layer * a.d : a.y);
-            yg[col0 + tid] = yv + own;
+            const float y0 = a.accumulate ? yg[col0 + tid] : 0.f;
+            yg[col0 + tid] = a.accumulate ? y0 + (yv + own) : yv + own;
         }
     }
     if (!a.prm && n_dev != n) err |= kErrCount;

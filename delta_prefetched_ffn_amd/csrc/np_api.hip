@@ -87,6 +87,7 @@ struct np_layer {
     int32_t* counts = nullptr;  // int32 [8], then the two 64-bit running sums (LayerDev::acc)
     uint64_t* ring = nullptr;   // window > 1: [window - 1][W] recent active sets
     int window = 1;
+    int reduce = NP_REDUCE_ATOMIC;  // how the FFN combines the partial sums of its workgroups
     LayerDev ldh{};             // host copy of *ldev
     uint64_t* hpair = nullptr;
     uint64_t* ppair = nullptr;
@@ -244,8 +245,11 @@ int scatter_grid(int n_in) { return std::max(1, std::min(n_in, 4096)); }
 // prm != nullptr: a launch captured into a decode graph (per-token values from prm).
 // read_through: the slots filled by the last assignment are read from the (device) row
 // store and written into the slot buffer by the FFN itself, in place of a scatter.
+// y_holds_base: y already holds the value to add the FFN output to (zeros in a decode step,
+// whose assign launch clears y, or the caller's value for np_sparse_ffn_acc); otherwise the
+// FFN output replaces y.
 np_status enqueue_ffn(np_layer* L, const float* x, float* y, hipStream_t s, const DecodeParams* prm = nullptr,
-                      int layer = 0, bool read_through = false) {
+                      int layer = 0, bool read_through = false, bool y_holds_base = false) {
     FfnShape sh{};
     if (!ffn_shape(L, L->n_active, &sh, prm != nullptr))
         return fail(NP_EINVAL, "no FFN launch shape for d_model=%d n=%d tile=%d", L->desc.d_model,
@@ -277,6 +281,10 @@ np_status enqueue_ffn(np_layer* L, const float* x, float* y, hipStream_t s, cons
     a.R = L->desc.n_rows;
     a.M = L->desc.d_ff;
     a.activation = L->desc.act;
+    a.atomic_y = L->reduce == NP_REDUCE_ATOMIC ? 1 : 0;
+    a.accumulate = y_holds_base ? 1 : 0;
+    if (a.atomic_y && !y_holds_base)  // the atomic reduction adds into y: start from zero
+        NP_HIP(hipMemsetAsync(y, 0, (size_t)L->desc.d_model * sizeof(float), s));
     a.p1 = sh.p1;
     a.q = sh.q;
     a.tw = sh.tw;
@@ -314,6 +322,9 @@ constexpr int kScatterWgsPerLayer = 64;
 np_status enqueue_token(np_layer* const* layers, int n, const int32_t* cid, const float* x, float* y,
                         hipStream_t cs, hipStream_t ps, const DecodeParams* prm, const hipEvent_t* ev) {
     const int d = layers[0]->desc.d_model;
+    // the assign launch clears every layer's y, so the FFN launches add into zeros
+    bool any_atomic = false;
+    for (int l = 0; l < n; ++l) any_atomic |= layers[l]->reduce == NP_REDUCE_ATOMIC;
     for (int l0 = 0; l0 < n; l0 += kMaxLayersPerLaunch) {
         DeltaLaunch a{};
         a.n_layers = std::min(kMaxLayersPerLaunch, n - l0);
@@ -324,6 +335,9 @@ np_status enqueue_token(np_layer* const* layers, int n, const int32_t* cid, cons
         }
         a.prm = prm;
         a.layer0 = l0;
+        a.zero_y = any_atomic ? 1 : 0;
+        a.y = prm ? nullptr : y;
+        a.d = d;
         NP_HIP(launch_delta_assign(a, cs));
     }
     if (one_queue(layers, n, cs, ps)) {
@@ -341,7 +355,7 @@ np_status enqueue_token(np_layer* const* layers, int n, const int32_t* cid, cons
         if (sa.n_layers > 0) NP_HIP(launch_scatter_all(sa, kScatterWgsPerLayer, cs));
         for (int l = 0; l < n; ++l) {
             np_status st = enqueue_ffn(layers[l], prm ? nullptr : x + (size_t)l * d, prm ? nullptr : y + (size_t)l * d,
-                                       cs, prm, l, !layers[l]->store_is_host);
+                                       cs, prm, l, !layers[l]->store_is_host, any_atomic);
             if (st != NP_OK) return st;
         }
         return NP_OK;
@@ -353,7 +367,8 @@ np_status enqueue_token(np_layer* const* layers, int n, const int32_t* cid, cons
         if (st != NP_OK) return st;
         NP_HIP(hipEventRecord(ev[2 + l], ps));
         NP_HIP(hipStreamWaitEvent(cs, ev[2 + l], 0));
-        st = enqueue_ffn(layers[l], prm ? nullptr : x + (size_t)l * d, prm ? nullptr : y + (size_t)l * d, cs, prm, l);
+        st = enqueue_ffn(layers[l], prm ? nullptr : x + (size_t)l * d, prm ? nullptr : y + (size_t)l * d, cs, prm, l,
+                         false, any_atomic);
         if (st != NP_OK) return st;
     }
     NP_HIP(hipEventRecord(ev[1], ps));  // join the copy stream back to the compute stream
@@ -715,7 +730,8 @@ np_status np_scatter_rows(np_layer* L, void* stream) {
     return NP_OK;
 }
 
-np_status np_sparse_ffn(np_layer* L, const float* x, float* y, void* stream) {
+namespace {
+np_status sparse_ffn_call(np_layer* L, const float* x, float* y, void* stream, bool acc) {
     if (!L) return fail(NP_EINVAL, "layer must not be NULL");
     if (!x || !y || !aligned16(x) || !aligned16(y)) return fail(NP_EINVAL, "x and y must be 16-byte aligned device pointers");
     if (L->state == kFresh) return fail(NP_ESTATE, "np_sparse_ffn needs a preceding np_delta_assign");
@@ -723,9 +739,28 @@ np_status np_sparse_ffn(np_layer* L, const float* x, float* y, void* stream) {
     if (read_through && L->store_is_host)
         return fail(NP_ESTATE, "the row store is host memory: call np_scatter_rows before np_sparse_ffn");
     DeviceGuard g(L->desc.device);
-    np_status st = enqueue_ffn(L, x, y, (hipStream_t)stream, nullptr, 0, read_through);
+    np_status st = enqueue_ffn(L, x, y, (hipStream_t)stream, nullptr, 0, read_through, acc);
     if (st != NP_OK) return st;
     L->state = kScattered;
+    return NP_OK;
+}
+}  // namespace
+
+np_status np_sparse_ffn(np_layer* L, const float* x, float* y, void* stream) {
+    return sparse_ffn_call(L, x, y, stream, false);
+}
+
+np_status np_sparse_ffn_acc(np_layer* L, const float* x, float* y, void* stream) {
+    return sparse_ffn_call(L, x, y, stream, true);
+}
+
+np_status np_layer_set_ffn_reduce(np_layer* L, int32_t mode) {
+    if (!L) return fail(NP_EINVAL, "layer must not be NULL");
+    if (mode != NP_REDUCE_ATOMIC && mode != NP_REDUCE_ORDERED) return fail(NP_EINVAL, "unknown reduce mode %d", mode);
+    DeviceGuard g(L->desc.device);
+    NP_HIP(hipDeviceSynchronize());
+    L->reduce = mode;
+    ++L->version;  // captured decode graphs carry the mode
     return NP_OK;
 }
 

@@ -78,6 +78,10 @@ struct DeltaLaunch {
     int32_t n_layers;
     const DecodeParams* prm;  // if set, centroid IDs come from prm->cid[layer0 + i]
     int32_t layer0;
+    // zero_y != 0: each workgroup also clears y[layer0 + i][0..d) (y from prm when set),
+    // for FFN launches that add their partial sums into y.
+    float* y;
+    int32_t zero_y, d;
 };
 
 // FFN launch shape (chosen on the host from the host-known |S|).
@@ -112,6 +116,8 @@ struct FfnArgs {
     int32_t d, K, R, M;
     int32_t p1, q, tw, nwg;
     int32_t activation;     // 0 ReLU, 1 SiLU
+    int32_t atomic_y;       // 1: every workgroup adds its tile partials into y with float atomics
+    int32_t accumulate;     // ordered reduction only: y = y + FFN instead of y = FFN
 };
 
 // Device code: view a pointer read from memory as a global-memory pointer. Without it the

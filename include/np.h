@@ -129,8 +129,9 @@ np_status np_scatter_rows(np_layer* layer, void* stream);
 
 /* Step 5: y[d_model] = sum over the resident (= active) slots of
  * down * act(gate . x) * (up . x), bf16 weights, fp32 arithmetic and
- * accumulation, fixed-order (run-to-run identical) reduction.
- * x and y are device fp32 [d_model], 16-byte aligned, not overlapping.
+ * accumulation; the cross-workgroup reduction is set by np_layer_set_ffn_reduce.
+ * x and y are device fp32 [d_model], 16-byte aligned, not overlapping. The
+ * result is run-to-run identical with NP_REDUCE_ORDERED (np_layer_set_ffn_reduce).
  * Called right after np_delta_assign (no np_scatter_rows) with a row store in
  * device memory, it does step 4 itself: the bundles of the slots filled by
  * that assignment are read from the row store and written into their slots
@@ -138,6 +139,21 @@ np_status np_scatter_rows(np_layer* layer, void* stream);
  * Errors: NP_ESTATE before the first np_delta_assign, or after an
  * unscattered assignment when the row store is host memory. */
 np_status np_sparse_ffn(np_layer* layer, const float* x, float* y, void* stream);
+
+/* As np_sparse_ffn, but y += FFN(x): the FFN output is added to what y holds
+ * (the residual stream of a transformer block). Same state rules. */
+np_status np_sparse_ffn_acc(np_layer* layer, const float* x, float* y, void* stream);
+
+/* How the FFN's workgroups combine the partial sums of y (section 3.4 fixes
+ * only the sum). NP_REDUCE_ATOMIC (the default): every workgroup adds its
+ * partial sums into y with fp32 atomics; the order of the additions, and so
+ * the last bits of y, can differ from run to run. np_sparse_ffn then clears y
+ * with one extra launch; np_decode_step clears it inside its assign launch.
+ * NP_REDUCE_ORDERED: the partial sums are exchanged and added in a fixed
+ * order by one workgroup per output tile, one more cross-workgroup hop per
+ * launch, bit-identical results run to run. Synchronizes the device. */
+typedef enum { NP_REDUCE_ATOMIC = 0, NP_REDUCE_ORDERED = 1 } np_reduce;
+np_status np_layer_set_ffn_reduce(np_layer* layer, int32_t mode);
 
 /* One decode token over n_layers layers of one device with equal d_model
  * (sections 3.1, 3.4, 3.5): validates every layer's cids on the host (a

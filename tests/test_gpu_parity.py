@@ -138,9 +138,9 @@ def test_exact_dyadic_inputs_bit_exact(torch, R):
 
 
 def test_decode_paths_agree_and_repeat_bitwise(torch):
-    """Graph replay and direct launches, one stream and two streams, device and pinned-host row
-    stores (the latter takes the per-layer two-stream structure), and per-layer calls give
-    bit-identical y; reruns too."""
+    """With the ordered reduction: graph replay and direct launches, one stream and two streams,
+    device and pinned-host row stores (the latter takes the per-layer two-stream structure), and
+    per-layer calls give bit-identical y; reruns too."""
     from delta_prefetched_ffn_amd import binding as B
     cfg = small_config(960, L=3, d=4096, M=3000, K=600, C=6, mode="union", m=250, swap=30, T=6)
     wl = Workload(cfg)
@@ -152,6 +152,8 @@ def test_decode_paths_agree_and_repeat_bitwise(torch):
         B.decode_use_graphs(not path.endswith("direct"))
         where = "host" if "host" in path else "device"
         layers = [make_layer(wl, l, where)[0] for l in range(cfg.L)]
+        for layer in layers:
+            layer.set_ffn_reduce("ordered")  # bit-identical results need the fixed-order reduction
         y = torch.zeros_like(x)
         cs, ps = torch.cuda.Stream(), torch.cuda.Stream()
         for t in range(cfg.T):
@@ -263,3 +265,38 @@ def test_ffn_launch_shapes(torch, shape):
         ref = O.sparse_ffn(dstore, 3, 4096, dorc.active(t, 0), x_np)
         assert np.array_equal(yd.cpu().numpy().astype(np.float64), ref), f"{shape} t={t}"
     dl.close()
+
+
+@pytest.mark.parametrize("mode", ["atomic", "ordered"])
+def test_accumulate_and_reduce_modes(torch, mode):
+    """np_sparse_ffn_acc adds the FFN output to y; np_sparse_ffn replaces y (also when y holds
+    NaN); both reductions match the oracle; the ordered one repeats bit for bit."""
+    from delta_prefetched_ffn_amd import binding as B
+    cfg = small_config(980, L=1, d=4096, M=1200, K=500, C=4, mode="union", m=200, swap=30, T=4, act="silu")
+    wl = Workload(cfg)
+    layer, store = make_layer(wl, 0)
+    layer.set_ffn_reduce(mode)
+    orc = OracleRun(wl)
+    x_all = wl.x_all()
+    rng = np.random.default_rng(1)
+    s = _stream(torch)
+    for t in range(cfg.T):
+        g, u = (int(v) for v in wl.cids()[t, 0])
+        layer.delta_assign(g, u, s)
+        S, res = orc.step(t, 0, store)
+        x = torch.from_numpy(x_all[t, 0]).cuda()
+        base = rng.standard_normal(cfg.d).astype(np.float32)
+        y_acc = torch.from_numpy(base).cuda()
+        y_new = torch.full((cfg.d,), float("nan"), device="cuda")
+        layer.sparse_ffn_acc(x.data_ptr(), y_acc.data_ptr(), s)   # read-through on the first call
+        layer.sparse_ffn(x.data_ptr(), y_new.data_ptr(), s)
+        y_rep = torch.full((cfg.d,), float("nan"), device="cuda")
+        layer.sparse_ffn(x.data_ptr(), y_rep.data_ptr(), s)
+        torch.cuda.synchronize()
+        ref = O.sparse_ffn(store, cfg.R, cfg.d, S, x_all[t, 0], cfg.act)
+        check_y(y_new.cpu().numpy(), ref, f"{mode} t={t} replace")
+        check_y(y_acc.cpu().numpy() - base, ref, f"{mode} t={t} accumulate")
+        if mode == "ordered":
+            assert np.array_equal(y_new.cpu().numpy().view(np.uint32), y_rep.cpu().numpy().view(np.uint32))
+        compare_state(layer.read_state(), orc.layers[0], res, S, f"{mode} t={t}")
+    layer.close()

@@ -116,12 +116,6 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
     const int32_t cg = a.prm ? gmem(a.prm)->cid[a.layer0 + blockIdx.x][0] : a.cid[blockIdx.x][0];
     const int32_t cu = a.prm ? gmem(a.prm)->cid[a.layer0 + blockIdx.x][1] : a.cid[blockIdx.x][1];
 
-    if (a.zero_y) {  // y of this layer for FFN launches that add into it
-        float* yb = a.prm ? gmem(a.prm)->y : a.y;
-        auto* yl = gmem(yb + (size_t)(a.layer0 + blockIdx.x) * a.d);
-        for (int i = tid; i < a.d; i += kNT) yl[i] = 0.f;
-    }
-
     // Step 1: active set S from the selected gate/up masks; R from the resident bits. The
     // owner table (slot -> neuron) is read in the same round trip: it drives the release.
     const auto* ma = gmem(L.masks) + (size_t)cg * W;
@@ -393,6 +387,14 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
                 }
             }
         }
+    }
+
+    // y of this layer for FFN launches that add into it (stored last: a store ahead of the
+    // loads above would make their waits wait for it too)
+    if (a.zero_y) {
+        float* yb = a.prm ? gmem(a.prm)->y : a.y;
+        auto* yl = gmem(yb + (size_t)(a.layer0 + blockIdx.x) * a.d);
+        for (int i = tid; i < a.d; i += kNT) yl[i] = 0.f;
     }
 
     // Step 5: R = R_t; with a window, S joins the ring of recent active sets.

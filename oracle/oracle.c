@@ -168,6 +168,47 @@ int32_t npo_window_target(int32_t M, int32_t K, int32_t k, int32_t t, const int3
     return m;
 }
 
+/*
+ * Frequency-weighted retention (DynamicInfer, key design 2, the hierarchical neuron cache: the
+ * importance of neuron i is v = a + lambda * f, a = 1 when i is predicted active and f its
+ * historical activation frequency, and the most important neurons are kept on the GPU,
+ * replaced greedily by importance). Here every active neuron must be resident, so a = 1 ranks
+ * first and the rest is ordered by f alone. f comes quantised: level[i] in [0, n_levels),
+ * higher = more frequent. Computes R_t for capacity K:
+ *   R_t = S_t plus resident neurons not in S_t, taken from the highest level down and, within
+ *   one level, by ascending ID, as long as |R_t| <= K.
+ * Neurons that are not resident are never loaded here (eviction only). With no room left
+ * (|S_t| = K) or n_levels = 0 this is R_t = S_t, the exact rule of NeuroPrefetcher section 3.4.
+ * Writes R_t ascending to R (capacity M) and returns |R_t|; -2 when n > K (refused), -1 for
+ * invalid arguments (a level outside [0, n_levels) included).
+ */
+int32_t npo_level_target(int32_t M, int32_t K, int32_t n_levels, const uint8_t* level,
+                         const int32_t* slot_map, const int32_t* S, int32_t n, int32_t* R) {
+    if (M <= 0 || K <= 0 || n_levels < 0 || n < 0) return -1;
+    for (int32_t i = 0; i < M && n_levels > 0; ++i)
+        if (level[i] >= n_levels) return -1;
+    if (n > K) return -2;
+    char* in_r = (char*)calloc((size_t)M, 1);
+    if (!in_r) return -1;
+    for (int32_t q = 0; q < n; ++q) {
+        if (S[q] < 0 || S[q] >= M) { free(in_r); return -1; }
+        in_r[S[q]] = 1;
+    }
+    int32_t room = K - n;
+    for (int32_t lv = n_levels - 1; lv >= 0 && room > 0; --lv) {
+        for (int32_t i = 0; i < M && room > 0; ++i) {
+            if (in_r[i] || slot_map[i] < 0 || level[i] != lv) continue;
+            in_r[i] = 1;
+            --room;
+        }
+    }
+    int32_t m = 0;
+    for (int32_t i = 0; i < M; ++i)
+        if (in_r[i]) R[m++] = i;
+    free(in_r);
+    return m;
+}
+
 /* Ascending occupied slots (the slots whose rows the FFN reads); returns the count. */
 int32_t npo_occupied_slots(int32_t K, const int32_t* owner, int32_t* slots) {
     int32_t n = 0;

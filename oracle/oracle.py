@@ -61,6 +61,8 @@ def _lib():
     lib.npo_sparse_ffn_act.restype = i32
     lib.npo_window_target.argtypes = [i32, i32, i32, i32, vp, vp, vp, i32, vp]
     lib.npo_window_target.restype = i32
+    lib.npo_level_target.argtypes = [i32, i32, i32, vp, vp, vp, i32, vp]
+    lib.npo_level_target.restype = i32
     return lib
 
 
@@ -99,11 +101,17 @@ class OracleLayer:
 
     window = 1: the buffer holds exactly the active set (NeuroPrefetcher section 3.4).
     window = k > 1: it also keeps neurons active in the last k - 1 tokens, capacity
-    permitting (LLM in a flash, section 3.1; see npo_window_target)."""
+    permitting (LLM in a flash, section 3.1; see npo_window_target).
+    levels (uint8 [M], values < n_levels): it keeps resident neurons by frequency level,
+    capacity permitting (DynamicInfer, key design 2; see npo_level_target)."""
 
-    def __init__(self, M: int, K: int, R: int, d: int, keep_buffer: bool = True, window: int = 1):
+    def __init__(self, M: int, K: int, R: int, d: int, keep_buffer: bool = True, window: int = 1,
+                 levels: np.ndarray | None = None, n_levels: int = 0):
         assert window >= 1
+        assert levels is None or (window == 1 and n_levels >= 1 and len(levels) == M)
         self.M, self.K, self.R, self.d, self.window = M, K, R, d, window
+        self.levels = None if levels is None else _c(levels, np.uint8)
+        self.n_levels = n_levels if levels is not None else 0
         self.slot_map = np.full(M, -1, dtype=np.int32)
         self.owner = np.full(K, -1, dtype=np.int32)
         self.last_t = np.full(M, _NEVER, dtype=np.int32)
@@ -121,6 +129,15 @@ class OracleLayer:
     def target(self, S: np.ndarray) -> np.ndarray:
         """The resident set this token moves to (S itself for window 1)."""
         S = _c(S, np.int32)
+        if self.levels is not None:
+            R = np.empty(self.M, dtype=np.int32)
+            m = _lib().npo_level_target(self.M, self.K, self.n_levels, self.levels.ctypes.data,
+                                        self.slot_map.ctypes.data, S.ctypes.data, S.size, R.ctypes.data)
+            if m == -2:
+                raise CapacityError(f"|S|={S.size} > K_max={self.K}")
+            if m < 0:
+                raise ValueError("invalid active set or levels")
+            return R[:m].copy()
         if self.window == 1:
             if S.size > self.K:
                 raise CapacityError(f"|S|={S.size} > K_max={self.K}")

@@ -33,7 +33,7 @@ EXPORTS = ["np_layer_create", "np_layer_destroy", "np_layer_reset", "np_delta_as
            "np_scatter_rows", "np_sparse_ffn", "np_decode_step", "np_layer_read_state",
            "np_layer_read_rows", "np_layer_info", "np_layer_counters", "np_layer_set_ffn_shape", "np_last_error",
            "np_probe_read", "np_probe_copy", "np_decode_use_graphs", "np_layer_set_window",
-           "np_sparse_ffn_acc", "np_layer_set_ffn_reduce"]
+           "np_sparse_ffn_acc", "np_layer_set_ffn_reduce", "np_layer_set_levels"]
 
 
 class NPError(RuntimeError):
@@ -75,6 +75,7 @@ def lib() -> ctypes.CDLL:
         "np_layer_set_window": [vp, i32],
         "np_sparse_ffn_acc": [vp, vp, vp, vp],
         "np_layer_set_ffn_reduce": [vp, i32],
+        "np_layer_set_levels": [vp, i32, vp],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -150,6 +151,15 @@ class Layer:
     def set_window(self, window: int) -> None:
         """Residency window in tokens (1 = the buffer holds exactly the active set)."""
         _check(lib().np_layer_set_window(self.h, window))
+
+    def set_levels(self, levels, n_levels: int) -> None:
+        """Retention by frequency level: levels uint8 [d_ff], each < n_levels (0 switches it off)."""
+        if n_levels == 0:
+            _check(lib().np_layer_set_levels(self.h, 0, None))
+            return
+        lv = np.ascontiguousarray(levels, dtype=np.uint8)
+        assert lv.shape == (self.d_ff,), lv.shape
+        _check(lib().np_layer_set_levels(self.h, n_levels, lv.ctypes.data))
 
     def info(self) -> dict:
         out = np.zeros(6, dtype=np.int32)

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
     __shared__ int s_opre[kMaxKWords];     // exclusive prefix of active slots per word
     __shared__ uint64_t s_Rn[kMaxWords];   // the new resident set R_t
     __shared__ uint64_t s_Ab[kMaxKWords];  // slots holding an active neuron (the FFN's list)
-    __shared__ int s_cnt[kMaxWindow];      // window: retained candidates per age
+    __shared__ int s_cnt[kMaxClasses + 1]; // retained candidates per class (age or level)
     __shared__ int s_nS, s_jstar, s_allow;
     __shared__ int s_tmp[2 * kWaves];
     __shared__ int s_err;
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
         s_err = 0;
         s_nS = 0;
     }
-    if (tid < kMaxWindow) s_cnt[tid] = 0;
+    if (tid <= kMaxClasses) s_cnt[tid] = 0;
     const int win = L.window;
     const int tok = counts[4];  // tokens assigned before this one
     const int32_t cg = a.prm ? gmem(a.prm)->cid[a.layer0 + blockIdx.x][0] : a.cid[blockIdx.x][0];
@@ -134,27 +134,34 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
     }
     __syncthreads();
 
-    // Step 1b: the resident set R_t this token moves to. Exactly S (section 3.4), or with a
-    // window of k tokens (LLM in a flash, section 3.1) S plus the resident neurons last active
-    // j = 1 .. k-1 tokens ago, the most recent first and by ascending ID within one j, while
-    // |R_t| <= K. The active sets of the last k-1 tokens are kept as bit masks in a ring, so
-    // the age class of a neuron is the first earlier mask that holds it.
+    // Step 1b: the resident set R_t this token moves to. Exactly S (section 3.4), or S plus
+    // resident neurons of retention classes j = 1, 2, ..., taken class by class and by
+    // ascending ID within a class while |R_t| <= K:
+    //   * window of k tokens (LLM in a flash, section 3.1): class j = last active j tokens ago
+    //     (1 <= j < k). The active sets of the last k-1 tokens are kept as bit masks in a
+    //     ring, so the class of a neuron is the first earlier mask that holds it;
+    //   * frequency levels (DynamicInfer, key design 2: importance a + lambda f, every active
+    //     neuron resident): class j = the j-th highest level, from static per-level masks.
     const int wpt = (W + kNT - 1) / kNT;
     const int w0 = min(tid * wpt, W), w1 = min(w0 + wpt, W);
-    if (win > 1) {
+    const bool by_level = L.n_levels > 0;
+    if (win > 1 || by_level) {
         const auto* ring = gmem(L.ring);
-        const int nj = min(win - 1, tok);  // earlier tokens that exist
-        auto ring_word = [&](int j, int w) { return ring[(size_t)((tok - j) % (win - 1)) * W + w]; };
-        int cnt[kMaxWindow];
+        const auto* lvl = gmem(L.levels);
+        const int nj = by_level ? L.n_levels : min(win - 1, tok);  // classes that exist
+        auto ring_word = [&](int j, int w) -> uint64_t {
+            return by_level ? lvl[(size_t)(j - 1) * W + w] : ring[(size_t)((tok - j) % (win - 1)) * W + w];
+        };
+        int cnt[kMaxClasses + 1];
 #pragma unroll
-        for (int j = 0; j < kMaxWindow; ++j) cnt[j] = 0;
+        for (int j = 0; j <= kMaxClasses; ++j) cnt[j] = 0;
         int c_s = 0;
         for (int w = w0; w < w1; ++w) {
             const uint64_t base = s_R[w] & ~s_S[w];
             uint64_t covered = 0;
             c_s += __popcll(s_S[w]);
 #pragma unroll
-            for (int j = 1; j < kMaxWindow; ++j) {
+            for (int j = 1; j <= kMaxClasses; ++j) {
                 if (j > nj) break;
                 const uint64_t A = ring_word(j, w);
                 cnt[j] += __popcll(A & base & ~covered);
@@ -163,11 +170,11 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
         }
         atomicAdd(&s_nS, c_s);
 #pragma unroll
-        for (int j = 1; j < kMaxWindow; ++j)
+        for (int j = 1; j <= kMaxClasses; ++j)
             if (cnt[j]) atomicAdd(&s_cnt[j], cnt[j]);
         __syncthreads();
         if (tid == 0) {
-            int room = K - s_nS, js = kMaxWindow, allow = 0;
+            int room = K - s_nS, js = kMaxClasses + 1, allow = 0;
             for (int j = 1; j <= nj; ++j) {
                 if (s_cnt[j] <= room) {
                     room -= s_cnt[j];

@@ -87,6 +87,8 @@ struct np_layer {
     int32_t* counts = nullptr;  // int32 [8], then the two 64-bit running sums (LayerDev::acc)
     uint64_t* ring = nullptr;   // window > 1: [window - 1][W] recent active sets
     int window = 1;
+    uint64_t* levels = nullptr; // n_levels > 0: [n_levels][W] neurons per frequency level
+    int n_levels = 0;
     int reduce = NP_REDUCE_ATOMIC;  // how the FFN combines the partial sums of its workgroups
     LayerDev ldh{};             // host copy of *ldev
     uint64_t* hpair = nullptr;
@@ -111,6 +113,10 @@ struct np_layer {
 };
 
 namespace {
+
+// A retention rule (window or frequency levels) decides the resident set, and so |D_in|, on
+// the device; without one the host knows |D_in| from its mirror of the resident set.
+bool device_decides(const np_layer* L) { return L->window > 1 || L->n_levels > 0; }
 
 int pow2_floor(int v) {
     int p = 1;
@@ -179,7 +185,7 @@ np_status alloc_ffn_scratch(np_layer* L) {
 
 void free_layer(np_layer* L) {
     void* ptrs[] = {L->d_masks, L->buf, L->slot_map, L->owner, L->res, L->freeb, L->lists,
-                    L->counts, L->ring, L->hpair, L->ppair, L->ldev};
+                    L->counts, L->ring, L->levels, L->hpair, L->ppair, L->ldev};
     for (void* p : ptrs)
         if (p) (void)hipFree(p);
     if (L->ev_scatter) (void)hipEventDestroy(L->ev_scatter);
@@ -607,6 +613,9 @@ np_status np_layer_create(const np_layer_desc* desc, np_layer** out) {
     ld.acc = reinterpret_cast<unsigned long long*>(L->counts + 8);
     ld.ring = nullptr;
     ld.window = 1;
+    ld.levels = nullptr;
+    ld.n_levels = 0;
+    ld.pad2 = 0;
     ld.W = L->W;
     ld.Kw = L->Kw;
     ld.M = M;
@@ -699,8 +708,8 @@ np_status np_delta_assign(np_layer* L, int32_t gate_cid, int32_t up_cid, void* s
     const int n = combine_host(L, gate_cid, u, S.data());
     if (n > L->desc.k_max)
         return fail(NP_ECAPACITY, "|S| = %d exceeds k_max = %d", n, L->desc.k_max);
-    int n_in = -1;  // with a window the resident set is decided on the device
-    if (L->window == 1) {
+    int n_in = -1;  // with a retention rule the resident set is decided on the device
+    if (!device_decides(L)) {
         n_in = 0;
         for (int w = 0; w < L->W; ++w) n_in += __builtin_popcountll(S[w] & ~L->h_res[w]);
     }
@@ -789,8 +798,8 @@ np_status np_decode_step(np_layer* const* layers, int32_t n_layers, const int32_
         n_act[l] = combine_host(L, cids[2 * l], u, S[l].data());
         if (n_act[l] > L->desc.k_max)
             return fail(NP_ECAPACITY, "layer %d: |S| = %d exceeds k_max = %d", l, n_act[l], L->desc.k_max);
-        int ni = -1;  // with a window the resident set is decided on the device
-        if (L->window == 1) {
+        int ni = -1;  // with a retention rule the resident set is decided on the device
+        if (!device_decides(L)) {
             ni = 0;
             for (int w = 0; w < L->W; ++w) ni += __builtin_popcountll(S[l][w] & ~L->h_res[w]);
         }
@@ -912,7 +921,7 @@ np_status np_layer_info(const np_layer* L, int32_t* out6) {
     out6[3] = L->desc.n_rows;
     out6[4] = L->n_active;
     out6[5] = L->n_in;
-    if (L->window > 1 && L->state != kFresh) {  // |D_in| is decided on the device
+    if (device_decides(L) && L->state != kFresh) {  // |D_in| is decided on the device
         DeviceGuard g(L->desc.device);
         NP_HIP(hipDeviceSynchronize());
         NP_HIP(hipMemcpy(&out6[5], L->counts, 4, hipMemcpyDeviceToHost));
@@ -924,7 +933,7 @@ np_status np_layer_counters(const np_layer* L, int64_t* out2) {
     if (!L || !out2) return fail(NP_EINVAL, "layer and out must not be NULL");
     out2[0] = L->total_active;
     out2[1] = L->total_in;
-    if (L->window > 1) {  // |D_in| is decided on the device: its running sum lives there
+    if (device_decides(L)) {  // |D_in| is decided on the device: its running sum lives there
         DeviceGuard g(L->desc.device);
         NP_HIP(hipDeviceSynchronize());
         unsigned long long acc[2];
@@ -937,6 +946,7 @@ np_status np_layer_counters(const np_layer* L, int64_t* out2) {
 np_status np_layer_set_window(np_layer* L, int32_t window) {
     if (!L) return fail(NP_EINVAL, "layer must not be NULL");
     if (window < 1 || window > kMaxWindow) return fail(NP_EINVAL, "window=%d must be in [1, %d]", window, kMaxWindow);
+    if (window > 1 && L->n_levels > 0) return fail(NP_EINVAL, "a window excludes frequency levels (set n_levels 0 first)");
     if (L->state != kFresh) return fail(NP_ESTATE, "set the window before the first np_delta_assign (or after np_layer_reset)");
     DeviceGuard g(L->desc.device);
     NP_HIP(hipDeviceSynchronize());
@@ -979,6 +989,49 @@ np_status np_probe_copy(void* dst, const void* src, int64_t bytes, void* stream)
     if (!src || !dst || bytes <= 0 || bytes % 16 || !aligned16(src) || !aligned16(dst))
         return fail(NP_EINVAL, "probe_copy needs 16-byte aligned pointers, bytes a multiple of 16");
     NP_HIP(launch_probe_copy(dst, src, bytes, (hipStream_t)stream));
+    return NP_OK;
+}
+
+np_status np_layer_set_levels(np_layer* L, int32_t n_levels, const uint8_t* level) {
+    if (!L) return fail(NP_EINVAL, "layer must not be NULL");
+    if (n_levels < 0 || n_levels > kMaxLevels) return fail(NP_EINVAL, "n_levels=%d must be in [0, %d]", n_levels, kMaxLevels);
+    if (n_levels > 0 && !level) return fail(NP_EINVAL, "level must not be NULL when n_levels > 0");
+    if (n_levels > 0 && L->window > 1) return fail(NP_EINVAL, "frequency levels exclude a window > 1 (set window 1 first)");
+    if (L->state != kFresh) return fail(NP_ESTATE, "set the levels before the first np_delta_assign (or after np_layer_reset)");
+    const int M = L->desc.d_ff, W = L->W;
+    std::vector<uint64_t> masks((size_t)n_levels * W, 0ull);
+    for (int i = 0; i < M && n_levels > 0; ++i) {
+        if (level[i] >= n_levels) return fail(NP_EINVAL, "level[%d] = %d is not below n_levels = %d", i, level[i], n_levels);
+        const int j = n_levels - 1 - level[i];  // class order: highest level first
+        masks[(size_t)j * W + (i >> 6)] |= 1ull << (i & 63);
+    }
+    DeviceGuard g(L->desc.device);
+    NP_HIP(hipDeviceSynchronize());
+    uint64_t* dm = nullptr;
+    if (n_levels > 0) {
+        const size_t bytes = masks.size() * 8;
+        if (hipMalloc(&dm, bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(NP_ENOMEM, "cannot allocate the %zu-byte level masks", bytes);
+        }
+        if (hipMemcpy(dm, masks.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
+            (void)hipFree(dm);
+            return fail(NP_EHIP, "level mask upload failed");
+        }
+    }
+    LayerDev ld = L->ldh;
+    ld.levels = dm;
+    ld.n_levels = n_levels;
+    if (hipMemcpy(L->ldev, &ld, sizeof ld, hipMemcpyHostToDevice) != hipSuccess) {
+        if (dm) (void)hipFree(dm);
+        return fail(NP_EHIP, "layer descriptor update failed");
+    }
+    if (L->levels) (void)hipFree(L->levels);
+    L->levels = dm;
+    L->n_levels = n_levels;
+    L->ldh = ld;
+    NP_HIP(hipMemset(L->counts, 0, kCountsBytes));  // token count and running sums restart
+    ++L->version;
     return NP_OK;
 }
 

@@ -15,6 +15,8 @@ constexpr int kMaxWords = kMaxDff / 64;  // mask words per set
 constexpr int kMaxKWords = kMaxKmax / 64;
 constexpr int kMaxLayersPerLaunch = 64;
 constexpr int kMaxWindow = 16;             // residency window, tokens
+constexpr int kMaxLevels = 16;             // frequency levels of the retention by frequency
+constexpr int kMaxClasses = 16;            // retention classes (window ages 1..15 or levels)
 constexpr uint64_t kMaxBufBytes = (1ull << 32) - 4096;  // slot buffer addressed by 32-bit offsets
 
 // Device error bits (counts[3]).
@@ -45,6 +47,10 @@ struct LayerDev {
     uint16_t* buf;           // [K][R][d] slot buffer
     int32_t bundle16;        // 16-byte chunks per bundle
     int32_t window;          // residency window in tokens (1: the buffer holds exactly S)
+    // Retention by frequency level (n_levels > 0, window 1): bit masks of the neurons of each
+    // level, highest level first ([n_levels][W]).
+    const uint64_t* levels;
+    int32_t n_levels, pad2;
 };
 
 // One launch scattering the deltas of many layers (blockIdx.y = layer).

@@ -112,8 +112,8 @@ np_status np_layer_reset(np_layer* layer);
 
 /* Steps 1-3 for one layer (section 3.4). Builds S from mask gate_cid of the
  * gate table and up_cid of the up table (up_cid is ignored for SINGLE),
- * picks the new resident set R' (R' = S, or with a residency window see
- * np_layer_set_window), computes D_in = S \ R and D_out = R \ R' in
+ * picks the new resident set R' (R' = S, or with a residency window or
+ * frequency levels see np_layer_set_window and np_layer_set_levels), computes D_in = S \ R and D_out = R \ R' in
  * ascending neuron order, releases the slots of D_out, gives the i-th neuron
  * of D_in the i-th free slot in ascending slot order, updates the slot map
  * and owner table, and lists the slots of S in ascending slot order (the rows
@@ -209,8 +209,8 @@ np_status np_layer_info(const np_layer* layer, int32_t* out6);
 /* Running totals since create/reset: out2[0] = sum of |S| and out2[1] = sum
  * of |D_in| over every accepted assignment (bundles read by the FFN and
  * bundles written by the scatter, in units of one bundle). Host-side and
- * non-blocking with window 1; with a window, |D_in| is known on the device
- * only and the call synchronizes the layer's device. */
+ * non-blocking with window 1 and no levels; otherwise |D_in| is known on the
+ * device only and the call synchronizes the layer's device. */
 np_status np_layer_counters(const np_layer* layer, int64_t* out2);
 
 /* Residency window (LLM in a flash, section 3.1 "Windowing"): besides S, the
@@ -221,9 +221,27 @@ np_status np_layer_counters(const np_layer* layer, int64_t* out2);
  * loaded again when it is active. window = 1 (the default) is the exact rule
  * of section 3.4: the buffer holds S. 1 <= window <= 16. Only before the
  * first np_delta_assign after create or reset (NP_ESTATE otherwise).
+ * Exclusive with frequency levels (np_layer_set_levels; NP_EINVAL).
  * Synchronizes the layer's device. With window > 1, np_layer_info's n_in and
  * np_layer_counters' |D_in| are read back from the device. */
 np_status np_layer_set_window(np_layer* layer, int32_t window);
+
+/* Retention by frequency level (DynamicInfer paper notes, key design 2, the
+ * hierarchical neuron cache: importance a + lambda * f, a = 1 for a
+ * predicted-active neuron, f its historical activation frequency). Every
+ * active neuron is resident, so only the neurons outside S are ranked, by
+ * f: besides S the buffer keeps resident neurons by descending level, then
+ * ascending neuron ID, as long as at most k_max neurons are resident; a
+ * neuron that left is only loaded again when it is active. level is host
+ * uint8 [d_ff], each value < n_levels (higher = more frequent), the
+ * caller's quantisation of offline activation frequencies; it is copied.
+ * n_levels = 0 switches the retention off (level may be NULL): the buffer
+ * holds exactly S again. 0 <= n_levels <= 16. Exclusive with a window > 1
+ * (NP_EINVAL). Only before the first np_delta_assign after create or reset
+ * (NP_ESTATE otherwise). Synchronizes the layer's device. With n_levels > 0,
+ * np_layer_info's n_in and np_layer_counters' |D_in| are read back from
+ * the device. */
+np_status np_layer_set_levels(np_layer* layer, int32_t n_levels, const uint8_t* level);
 
 /* FFN launch shape of this layer: about slots_per_wg active slots per
  * workgroup for the gate/up phase (1..16; the default, -1, sizes the grid to

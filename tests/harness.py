@@ -54,11 +54,13 @@ def make_layer(wl: Workload, l: int, where: str = "device", store: np.ndarray | 
 class OracleRun:
     """The oracle's state for every layer of a workload."""
 
-    def __init__(self, wl: Workload, keep_buffer: bool = True, window: int = 1):
+    def __init__(self, wl: Workload, keep_buffer: bool = True, window: int = 1, n_levels: int = 0):
         c = wl.cfg
         self.wl = wl
-        self.layers = [O.OracleLayer(c.M, c.K, c.R, c.d, keep_buffer=keep_buffer, window=window)
-                       for _ in range(c.L)]
+        self.layers = [O.OracleLayer(c.M, c.K, c.R, c.d, keep_buffer=keep_buffer, window=window,
+                                     levels=wl.frequency_levels(l, n_levels) if n_levels else None,
+                                     n_levels=n_levels)
+                       for l in range(c.L)]
         self.mode = O.MODES[c.mode]
 
     def active(self, t: int, l: int) -> np.ndarray:
@@ -82,6 +84,6 @@ def compare_state(st: dict, ol: O.OracleLayer, res: O.StepResult, S: np.ndarray,
     assert np.array_equal(st["slot_map"], ol.slot_map), f"{what}: slot_map differs"
     assert np.array_equal(st["owner"], ol.owner), f"{what}: owner differs"
     assert np.array_equal(st["act"], ol.active_slots(S)), f"{what}: active slot list differs"
-    if ol.window == 1:
+    if ol.window == 1 and ol.levels is None:
         assert np.array_equal(st["act"], ol.occupied_slots()), f"{what}: occupied slots differ"
     assert st["act"].size == S.size

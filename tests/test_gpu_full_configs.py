@@ -23,7 +23,8 @@ def _log(msg):
     print(f"[full-config] {msg}", flush=True)
 
 
-def run_full(num: int, where: str = "device", steps: int | None = None, ffn_samples: int = 10, window: int = 1):
+def run_full(num: int, where: str = "device", steps: int | None = None, ffn_samples: int = 10, window: int = 1,
+             n_levels: int = 0):
     from delta_prefetched_ffn_amd import binding as B
     torch = torch_mod()
     assert torch.cuda.is_available()
@@ -36,8 +37,10 @@ def run_full(num: int, where: str = "device", steps: int | None = None, ffn_samp
         layers.append(make_layer(wl, l, where)[0])
         if window > 1:
             layers[-1].set_window(window)
+        if n_levels:
+            layers[-1].set_levels(wl.frequency_levels(l, n_levels), n_levels)
     _log(f"config {num}: {c.L} layers built ({where} store) in {time.time() - t0:.1f}s")
-    orc = OracleRun(wl, keep_buffer=False, window=window)
+    orc = OracleRun(wl, keep_buffer=False, window=window, n_levels=n_levels)
     x_all = wl.x_all()[:T]
     x = torch.from_numpy(np.ascontiguousarray(x_all)).cuda()
     y = torch.zeros_like(x)
@@ -90,6 +93,12 @@ def test_full_config_device_store(num):
 def test_full_config_residency_window(num, window):
     """Config 9 is the low-overlap stress case (persistence 0.40-0.50)."""
     run_full(num, "device", window=window)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("num,n_levels", [(2, 8), (9, 8)])
+def test_full_config_frequency_levels(num, n_levels):
+    run_full(num, "device", n_levels=n_levels)
 
 
 @pytest.mark.timeout(600)

@@ -266,6 +266,17 @@ class Workload:
                 self._masks[l] = np.stack(tabs)
         return self._masks[l]
 
+    def frequency_levels(self, l: int, n_levels: int) -> np.ndarray:
+        """uint8 [M]: each neuron's activation frequency over layer l's centroid masks (the
+        fraction of the gate and up masks that hold it), quantised to n_levels equal-width
+        levels (0 = rarest). A stand-in for offline activation statistics."""
+        c = self.cfg
+        tabs = self.masks(l)
+        bits = np.unpackbits(tabs.view(np.uint8).reshape(tabs.shape[0], c.C, -1), axis=-1,
+                             bitorder="little")[:, :, : c.M]
+        f = bits.reshape(-1, c.M).mean(axis=0)
+        return np.minimum((f * n_levels).astype(np.int64), n_levels - 1).astype(np.uint8)
+
     # ----------------------------------------------------------------- cids
     def cids(self) -> np.ndarray:
         """int32 [T][L][2]: (gate cid, up cid) per step and layer; single mode repeats it.

@@ -46,6 +46,8 @@ def parse():
                    help="FFN partial-sum reduction: fp32 atomics (default) or fixed order (bit-reproducible)")
     p.add_argument("--window", type=int, default=1,
                    help="residency window in tokens (1: the buffer holds exactly the active set)")
+    p.add_argument("--levels", type=int, default=0,
+                   help="retention by frequency level: number of levels (0: off; exclusive with --window)")
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--ffn-steps", type=int, default=40,
@@ -103,12 +105,14 @@ def stored_traffic(ffn_bytes_per_launch: float):
     return rec.get("traffic_bytes_per_launch"), rec.get("note", "")
 
 
-def cpu_baseline(wl, stores, seconds: float, window: int = 1):
+def cpu_baseline(wl, stores, seconds: float, window: int = 1, n_levels: int = 0):
     """The CPU oracle, untouched, on a bounded sample of the same workload."""
     from oracle import oracle as O
     c = wl.cfg
     threads = max(1, min(16, os.cpu_count() or 1))
-    layers = [O.OracleLayer(c.M, c.K, c.R, c.d, window=window) for _ in range(c.L)]
+    layers = [O.OracleLayer(c.M, c.K, c.R, c.d, window=window,
+                            levels=wl.frequency_levels(l, n_levels) if n_levels else None, n_levels=n_levels)
+              for l in range(c.L)]
     mode = O.MODES[c.mode]
     cids = wl.cids()
     tabs = [wl.masks(l) for l in range(c.L)]
@@ -181,6 +185,8 @@ def main():
                 L.set_ffn_shape(args.slots_per_wg, args.tile_cols)
             if args.window != 1:
                 L.set_window(args.window)
+            if args.levels:
+                L.set_levels(wl.frequency_levels(l, args.levels), args.levels)
             L.set_ffn_reduce(args.reduce)
             out.append(L)
         return out
@@ -326,7 +332,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        cpu = cpu_baseline(wl, stores, args.cpu_seconds, args.window)
+        cpu = cpu_baseline(wl, stores, args.cpu_seconds, args.window, args.levels)
         log(f"cpu baseline: {cpu['value']:.3f} tok/s on {cpu['cores']} threads")
 
     out = {
@@ -345,7 +351,8 @@ def main():
         "config": {"workload": workload_text(c, act_bundles / (args.steps * c.L)),
                    "global_batch": 1, "layers": c.L, "d_model": c.d, "d_ff": c.M, "k_max": c.K,
                    "weights": "bf16", "backing_store": "HBM", "parallelism": "single GPU",
-                   "residency_window": args.window, "ffn_reduce": args.reduce},
+                   "residency_window": args.window, "frequency_levels": args.levels,
+                   "ffn_reduce": args.reduce},
         "effective_gbps": eff_gbps,
         "effective_frac_of_hbm_peak": eff_gbps / HBM_PEAK_GBPS,
         "mean_active_per_layer": act_bundles / (args.steps * c.L),

@@ -209,6 +209,89 @@ int32_t npo_level_target(int32_t M, int32_t K, int32_t n_levels, const uint8_t* 
     return m;
 }
 
+/*
+ * Compacted buffer (LLM in a flash, section 3.3 "Optimized Data Management in DRAM": the
+ * occupied rows always form the prefix 0 .. n-1 of the preallocated matrix; a removed neuron's
+ * row is replaced by a row from the end of the occupied region, and incoming rows are appended
+ * after it), with the set difference of NeuroPrefetcher section 3.4 deciding who leaves and
+ * who comes. State: pos_map[M] (position of neuron i, -1 if absent), owner[K] (neuron at a
+ * position, -1 past the end), *n_occ (rows in use). One step:
+ *   1. D_in = S \ R and D_out = R \ S, ascending (R = the neurons in the buffer).
+ *   2. Removal, one hole at a time in ascending position: rows at the end of the occupied
+ *      region whose neuron leaves are dropped (the region shrinks); then the lowest position
+ *      still held by a leaving neuron takes the last row of the region, which is recorded as a
+ *      move (mv_src -> mv_dst) and the region shrinks by one. A leaving row is never moved.
+ *   3. Appending: the k-th incoming neuron (ascending) goes to position n_keep + k, where
+ *      n_keep = |R| - |D_out| is the region left after step 2.
+ * Outputs (capacity K each): d_in / pos_in (n_in), d_out (n_out), mv_src / mv_dst (n_mv, in
+ * ascending mv_dst). NPO_ECAPACITY, state untouched, when n_active > K.
+ */
+int32_t npo_compact_step(int32_t M, int32_t K, int32_t* pos_map, int32_t* owner, int32_t* n_occ,
+                         const int32_t* S, int32_t n_active, int32_t* d_in, int32_t* pos_in,
+                         int32_t* n_in, int32_t* d_out, int32_t* n_out, int32_t* mv_src,
+                         int32_t* mv_dst, int32_t* n_mv) {
+    if (M <= 0 || K <= 0 || n_active < 0) return NPO_EINVAL;
+    if (n_active > K) return NPO_ECAPACITY;
+    char* in_s = (char*)calloc((size_t)M, 1);
+    char* leaving = (char*)calloc((size_t)M, 1);
+    if (!in_s || !leaving) { free(in_s); free(leaving); return NPO_EINVAL; }
+    for (int32_t k = 0; k < n_active; ++k) {
+        if (S[k] < 0 || S[k] >= M) { free(in_s); free(leaving); return NPO_EINVAL; }
+        in_s[S[k]] = 1;
+    }
+    /* Step 1 */
+    int32_t ni = 0, no = 0;
+    for (int32_t i = 0; i < M; ++i) {
+        const int present = pos_map[i] != -1;
+        if (in_s[i] && !present) d_in[ni++] = i;
+        if (!in_s[i] && present) { d_out[no++] = i; leaving[i] = 1; }
+    }
+    /* Step 2 */
+    int32_t n = *n_occ, nm = 0;
+    for (;;) {
+        while (n > 0 && leaving[owner[n - 1]]) {          /* drop leaving rows at the end */
+            pos_map[owner[n - 1]] = -1;
+            owner[n - 1] = -1;
+            --n;
+        }
+        int32_t hole = -1;
+        for (int32_t p = 0; p < n; ++p)
+            if (leaving[owner[p]]) { hole = p; break; }
+        if (hole < 0) break;
+        const int32_t gone = owner[hole], mover = owner[n - 1];
+        pos_map[gone] = -1;
+        owner[hole] = mover;
+        pos_map[mover] = hole;
+        owner[n - 1] = -1;
+        mv_src[nm] = n - 1;
+        mv_dst[nm] = hole;
+        ++nm;
+        --n;
+    }
+    /* Step 3 */
+    for (int32_t k = 0; k < ni; ++k) {
+        pos_in[k] = n + k;
+        owner[n + k] = d_in[k];
+        pos_map[d_in[k]] = n + k;
+    }
+    *n_occ = n + ni;
+    *n_in = ni;
+    *n_out = no;
+    *n_mv = nm;
+    free(in_s);
+    free(leaving);
+    return NPO_OK;
+}
+
+/* The moves of one compact step: buf[mv_dst[k]] = buf[mv_src[k]] (sources and destinations
+ * are disjoint, so the order does not matter). */
+void npo_move_bundles(uint16_t* buf, int64_t bundle_elems, const int32_t* mv_src,
+                      const int32_t* mv_dst, int32_t n_mv) {
+    for (int32_t k = 0; k < n_mv; ++k)
+        memcpy(buf + (int64_t)mv_dst[k] * bundle_elems, buf + (int64_t)mv_src[k] * bundle_elems,
+               (size_t)bundle_elems * sizeof(uint16_t));
+}
+
 /* Ascending occupied slots (the slots whose rows the FFN reads); returns the count. */
 int32_t npo_occupied_slots(int32_t K, const int32_t* owner, int32_t* slots) {
     int32_t n = 0;

@@ -14,7 +14,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from dataclasses import dataclass
+from dataclasses import dataclass, field
 from functools import lru_cache
 
 import numpy as np
@@ -63,6 +63,10 @@ def _lib():
     lib.npo_window_target.restype = i32
     lib.npo_level_target.argtypes = [i32, i32, i32, vp, vp, vp, i32, vp]
     lib.npo_level_target.restype = i32
+    lib.npo_compact_step.argtypes = [i32, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.npo_compact_step.restype = i32
+    lib.npo_move_bundles.argtypes = [vp, i64, vp, vp, i32]
+    lib.npo_move_bundles.restype = None
     return lib
 
 
@@ -89,8 +93,10 @@ def active_set(mask_g: np.ndarray, mask_u: np.ndarray | None, M: int, mode: int)
 @dataclass
 class StepResult:
     d_in: np.ndarray      # ascending incoming neuron IDs
-    slot_in: np.ndarray   # slot assigned to each incoming neuron
+    slot_in: np.ndarray   # slot (compact layout: position) assigned to each incoming neuron
     d_out: np.ndarray     # ascending outgoing neuron IDs
+    mv_src: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int32))  # compact layout:
+    mv_dst: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int32))  # rows moved src -> dst
 
 
 _NEVER = -(1 << 30)
@@ -103,11 +109,16 @@ class OracleLayer:
     window = k > 1: it also keeps neurons active in the last k - 1 tokens, capacity
     permitting (LLM in a flash, section 3.1; see npo_window_target).
     levels (uint8 [M], values < n_levels): it keeps resident neurons by frequency level,
-    capacity permitting (DynamicInfer, key design 2; see npo_level_target)."""
+    capacity permitting (DynamicInfer, key design 2; see npo_level_target).
+    layout "compact": the rows of the active set always fill positions 0 .. |S|-1 (LLM in a
+    flash, section 3.3; see npo_compact_step); slot_map then maps a neuron to its position."""
 
     def __init__(self, M: int, K: int, R: int, d: int, keep_buffer: bool = True, window: int = 1,
-                 levels: np.ndarray | None = None, n_levels: int = 0):
-        assert window >= 1
+                 levels: np.ndarray | None = None, n_levels: int = 0, layout: str = "slots"):
+        assert window >= 1 and layout in ("slots", "compact")
+        assert layout == "slots" or (window == 1 and levels is None)
+        self.layout = layout
+        self.n_occ = 0
         assert levels is None or (window == 1 and n_levels >= 1 and len(levels) == M)
         self.M, self.K, self.R, self.d, self.window = M, K, R, d, window
         self.levels = None if levels is None else _c(levels, np.uint8)
@@ -121,6 +132,7 @@ class OracleLayer:
     def reset(self) -> None:
         self.slot_map.fill(-1)
         self.owner.fill(-1)
+        self.n_occ = 0
         self.last_t.fill(_NEVER)
         self.t = 0
         if self.buf is not None:
@@ -157,6 +169,8 @@ class OracleLayer:
 
     def step(self, S: np.ndarray) -> StepResult:
         S = _c(S, np.int32)
+        if self.layout == "compact":
+            return self._compact_step(S)
         res = self._move_to(self.target(S))
         self.last_t[S] = self.t
         self.t += 1
@@ -179,9 +193,32 @@ class OracleLayer:
         return StepResult(d_in[: n_in.value].copy(), slot_in[: n_in.value].copy(),
                           d_out[: n_out.value].copy())
 
+    def _compact_step(self, S: np.ndarray) -> StepResult:
+        K = self.K
+        d_in, pos_in, d_out = (np.empty(K, dtype=np.int32) for _ in range(3))
+        mv_src, mv_dst = np.empty(K, dtype=np.int32), np.empty(K, dtype=np.int32)
+        n_occ, n_in, n_out, n_mv = (ctypes.c_int32(v) for v in (self.n_occ, 0, 0, 0))
+        rc = _lib().npo_compact_step(self.M, K, self.slot_map.ctypes.data, self.owner.ctypes.data,
+                                     ctypes.byref(n_occ), S.ctypes.data, S.size, d_in.ctypes.data,
+                                     pos_in.ctypes.data, ctypes.byref(n_in), d_out.ctypes.data,
+                                     ctypes.byref(n_out), mv_src.ctypes.data, mv_dst.ctypes.data,
+                                     ctypes.byref(n_mv))
+        if rc == _ECAPACITY:
+            raise CapacityError(f"|S|={S.size} > K_max={K}")
+        if rc != _OK:
+            raise ValueError("invalid active set")
+        self.n_occ = n_occ.value
+        self.t += 1
+        return StepResult(d_in[: n_in.value].copy(), pos_in[: n_in.value].copy(), d_out[: n_out.value].copy(),
+                          mv_src[: n_mv.value].copy(), mv_dst[: n_mv.value].copy())
+
     def copy_bundles(self, store: np.ndarray, res: StepResult) -> None:
-        """buf[slot_in[k]] = store[d_in[k]] (byte copy); store is uint16 [M][R][d]."""
+        """Moves of a compact step first (buf[mv_dst] = buf[mv_src]), then
+        buf[slot_in[k]] = store[d_in[k]] (byte copy); store is uint16 [M][R][d]."""
         assert self.buf is not None
+        if res.mv_src.size:
+            _lib().npo_move_bundles(self.buf.ctypes.data, self.R * self.d, res.mv_src.ctypes.data,
+                                    res.mv_dst.ctypes.data, res.mv_src.size)
         st = store.reshape(-1)
         assert st.dtype == np.uint16 and st.flags.c_contiguous and st.size >= self.M * self.R * self.d
         _lib().npo_copy_bundles(self.buf.ctypes.data, st.ctypes.data, self.R * self.d,
@@ -190,6 +227,9 @@ class OracleLayer:
     def copy_given_bundles(self, bundles: np.ndarray, res: StepResult) -> None:
         """Same as copy_bundles, with bundles[k] already holding neuron d_in[k]'s bundle."""
         assert self.buf is not None
+        if res.mv_src.size:
+            _lib().npo_move_bundles(self.buf.ctypes.data, self.R * self.d, res.mv_src.ctypes.data,
+                                    res.mv_dst.ctypes.data, res.mv_src.size)
         b = _c(bundles, np.uint16).reshape(-1)
         ids = np.arange(res.d_in.size, dtype=np.int32)
         _lib().npo_copy_bundles(self.buf.ctypes.data, b.ctypes.data, self.R * self.d,

@@ -24,6 +24,7 @@ MODES = {"union": MASK_UNION, "intersect": MASK_INTERSECT, "single": MASK_SINGLE
 ACT_RELU, ACT_SILU = 0, 1
 REDUCE_ATOMIC, REDUCE_ORDERED = 0, 1
 REDUCES = {"atomic": REDUCE_ATOMIC, "ordered": REDUCE_ORDERED}
+LAYOUTS = {"slots": 0, "compact": 1}
 ACTS = {"relu": ACT_RELU, "silu": ACT_SILU}
 _NAMES = {0: "NP_OK", 1: "NP_EINVAL", 2: "NP_ECAPACITY", 3: "NP_ENOMEM", 4: "NP_EHIP",
           5: "NP_ESTATE", 6: "NP_EDEVICE"}
@@ -33,7 +34,8 @@ EXPORTS = ["np_layer_create", "np_layer_destroy", "np_layer_reset", "np_delta_as
            "np_scatter_rows", "np_sparse_ffn", "np_decode_step", "np_layer_read_state",
            "np_layer_read_rows", "np_layer_info", "np_layer_counters", "np_layer_set_ffn_shape", "np_last_error",
            "np_probe_read", "np_probe_copy", "np_decode_use_graphs", "np_layer_set_window",
-           "np_sparse_ffn_acc", "np_layer_set_ffn_reduce", "np_layer_set_levels"]
+           "np_sparse_ffn_acc", "np_layer_set_ffn_reduce", "np_layer_set_levels",
+           "np_layer_set_layout", "np_layer_read_moves"]
 
 
 class NPError(RuntimeError):
@@ -76,6 +78,8 @@ def lib() -> ctypes.CDLL:
         "np_sparse_ffn_acc": [vp, vp, vp, vp],
         "np_layer_set_ffn_reduce": [vp, i32],
         "np_layer_set_levels": [vp, i32, vp],
+        "np_layer_set_layout": [vp, i32],
+        "np_layer_read_moves": [vp, vp, vp, vp],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -160,6 +164,18 @@ class Layer:
         lv = np.ascontiguousarray(levels, dtype=np.uint8)
         assert lv.shape == (self.d_ff,), lv.shape
         _check(lib().np_layer_set_levels(self.h, n_levels, lv.ctypes.data))
+
+    def set_layout(self, layout: str) -> None:
+        """"slots" (slot map, the default) or "compact" (active rows at positions 0 .. |S|-1)."""
+        _check(lib().np_layer_set_layout(self.h, LAYOUTS[layout]))
+
+    def read_moves(self) -> tuple[np.ndarray, np.ndarray]:
+        """(src, dst) positions of the rows the last assignment moved (compact layout)."""
+        src = np.empty(self.k_max, dtype=np.int32)
+        dst = np.empty(self.k_max, dtype=np.int32)
+        n = ctypes.c_int32(0)
+        _check(lib().np_layer_read_moves(self.h, src.ctypes.data, dst.ctypes.data, ctypes.byref(n)))
+        return src[: n.value].copy(), dst[: n.value].copy()
 
     def info(self) -> dict:
         out = np.zeros(6, dtype=np.int32)

@@ -78,6 +78,111 @@ __device__ inline uint64_t valid_bits(int v, int Kw, int K) {
 
 constexpr int kOwnRegs = 32;  // owner entries per thread loaded with the masks (K <= 8192 in one pass)
 
+// Bits of the positions below lim in word v.
+__device__ inline uint64_t below(int v, int lim) {
+    const int b = lim - v * 64;
+    return b <= 0 ? 0ull : (b >= 64 ? ~0ull : ((1ull << b) - 1));
+}
+
+// Steps 3-4 of the compacted layout (LLM in a flash, section 3.3: the occupied rows form the
+// prefix 0 .. n-1; a leaving row is replaced by a row from the end of the region; incoming
+// rows are appended). On entry the leaving neurons' slot-map entries are -1 and their
+// positions are set in s_F0 (s_Fa: the positions free before this step, i.e. n_occ and up).
+// With n_keep = n_occ - |D_out|, the holes (leaving positions below n_keep, ascending) take
+// the staying rows at n_keep and up in descending order (the move list, applied to the bytes
+// by a copy kernel before the FFN), and the k-th incoming neuron goes to n_keep + k.
+// Returns |S| (the rows 0 .. |S|-1 the FFN reads).
+__device__ int compact_assign(const LayerDev& L, int n_in, int n_out, int base_in, int w0, int w1, int v0, int v1,
+                              const uint64_t* s_S, const uint64_t* s_R, const uint64_t* s_Fa,
+                              const uint64_t* s_F0, int* s_mpre, int* s_tmp, int* s_err) {
+    const int tid = threadIdx.x, K = L.K, Kw = L.Kw;
+    auto* const owner = gmem(L.owner);
+    auto* const slot_map = gmem(L.slot_map);
+    int c_fa = 0;
+    for (int v = v0; v < v1; ++v) c_fa += __popcll(s_Fa[v]);
+    int e_a, e_b, n_free0, unused;
+    block_excl_scan2(c_fa, 0, &e_a, &e_b, &n_free0, &unused, s_tmp);
+    const int n_occ = K - n_free0, n_keep = n_occ - n_out;
+    auto holes = [&](int v) { return s_F0[v] & ~s_Fa[v] & below(v, n_keep); };
+    auto movers = [&](int v) { return ~s_F0[v] & below(v, n_occ) & ~below(v, n_keep); };
+    int c_h = 0, c_m = 0;
+    for (int v = v0; v < v1; ++v) {
+        c_h += __popcll(holes(v));
+        c_m += __popcll(movers(v));
+    }
+    int pre_h, pre_m, n_h, n_m;
+    block_excl_scan2(c_h, c_m, &pre_h, &pre_m, &n_h, &n_m, s_tmp);
+    if (tid == 0 && (n_h != n_m || n_keep < 0)) atomicOr(s_err, kErrBadList);
+    for (int v = v0; v < v1; ++v) {
+        s_mpre[v] = pre_m;
+        pre_m += __popcll(movers(v));
+    }
+    __syncthreads();
+    // hole of ascending rank i <- mover of ascending rank n_m - 1 - i
+    {
+        int i = pre_h;
+        for (int v = v0; v < v1; ++v) {
+            uint64_t H = holes(v);
+            while (H) {
+                const int h = v * 64 + __ffsll((unsigned long long)H) - 1;
+                H &= H - 1;
+                const int j = n_m - 1 - i;
+                if (j >= 0) {
+                    int l0 = 0, h0 = Kw - 1;  // last word whose mover prefix is <= j
+                    while (l0 < h0) {
+                        const int mid = (l0 + h0 + 1) >> 1;
+                        if (s_mpre[mid] <= j) l0 = mid; else h0 = mid - 1;
+                    }
+                    const uint64_t rest = drop_low_bits(movers(l0), j - s_mpre[l0]);
+                    if (rest == 0) {  // only with an inconsistent state
+                        atomicOr(s_err, kErrBadList);
+                        ++i;
+                        continue;
+                    }
+                    const int m = l0 * 64 + __ffsll((unsigned long long)rest) - 1;
+                    const int nm = owner[m];
+                    gmem(L.mv_src)[i] = m;
+                    gmem(L.mv_dst)[i] = h;
+                    owner[h] = nm;
+                    if ((unsigned)nm < (unsigned)L.M) slot_map[nm] = h;
+                    else atomicOr(s_err, kErrBadList);
+                }
+                ++i;
+            }
+        }
+    }
+    __syncthreads();  // every mover's owner entry has been read
+    const int n_act = min(max(n_keep + n_in, 0), K);
+    {
+        int idx = base_in;
+        for (int w = w0; w < w1; ++w) {
+            uint64_t bits = s_S[w] & ~s_R[w];
+            while (bits) {
+                const int n = w * 64 + (__ffsll((unsigned long long)bits) - 1);
+                bits &= bits - 1;
+                const int pos = n_keep + idx;
+                if (pos < 0 || pos >= K) {
+                    atomicOr(s_err, kErrFreeExhausted);
+                } else {
+                    gmem(L.slot_in)[idx] = pos;
+                    slot_map[n] = pos;
+                    owner[pos] = n;
+                    gmem(L.act_src)[pos] = n;
+                }
+                ++idx;
+            }
+        }
+    }
+    for (int p = max(n_act, 0) + tid; p < n_occ; p += kNT) owner[p] = -1;
+    for (int p = tid; p < n_act; p += kNT) {
+        gmem(L.act)[p] = p;
+        if (p < n_keep) gmem(L.act_src)[p] = -1;
+    }
+    for (int v = tid; v < Kw; v += kNT) gmem(L.freeb)[v] = valid_bits(v, Kw, K) & ~below(v, n_act);
+    if (tid == 0) gmem(L.counts)[5] = n_h;
+    return n_act;
+}
+
 __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
     __shared__ uint64_t s_S[kMaxWords];
     __shared__ uint64_t s_R[kMaxWords];
@@ -303,6 +408,10 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
     block_excl_scan2(c_free, c_rel, &pre_free, &pre_rel, &n_free, &n_rel, s_tmp);
     if (tid == 0 && n_rel != n_out) atomicOr(&s_err, kErrBadList);
 
+    int n_act = 0;
+    if (L.compact) {
+        n_act = compact_assign(L, n_in, n_out, base_in, w0, w1, v0, v1, s_S, s_R, s_Fa, s_F0, s_fpre, s_tmp, &s_err);
+    } else {
     // Step 4 (set part): the n_in lowest free slots are taken (they join the active slots);
     // active slots per word.
     int c_occ = 0;
@@ -321,7 +430,7 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
             gone &= gone - 1;
         }
     }
-    int pre_occ, unused_e, n_act, unused_t;
+    int pre_occ, unused_e, unused_t;
     block_excl_scan2(c_occ, 0, &pre_occ, &unused_e, &n_act, &unused_t, s_tmp);  // publishes s_fpre, s_F1, s_Ab
     for (int v = v0; v < v1; ++v) {
         s_opre[v] = pre_occ;
@@ -395,6 +504,7 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
             }
         }
     }
+    }  // slot layout
 
     // y of this layer for FFN launches that add into it (stored last: a store ahead of the
     // loads above would make their waits wait for it too)

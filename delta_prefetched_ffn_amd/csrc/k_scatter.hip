@@ -73,6 +73,37 @@ __global__ __launch_bounds__(kNT) void k_scatter_all(ScatterLaunch a) {
     }
 }
 
+// Compacted layout: the rows moved by the last assignment, buf[mv_dst[k]] = buf[mv_src[k]]
+// for k < counts[5], all layers at once (blockIdx.y = layer). Sources (the end of the old
+// region) and destinations (holes below it) are disjoint, so the copies are independent.
+__global__ __launch_bounds__(kNT) void k_move_all(ScatterLaunch a) {
+    const LayerDev* L = a.layers[blockIdx.y];
+    const int K = L->K, cb = L->bundle16;
+    const int n_mv = min(gmem(L->counts)[5], K);
+    auto* buf = gmem(reinterpret_cast<uint4*>(L->buf));
+    const auto* src_l = gmem(L->mv_src);
+    const auto* dst_l = gmem(L->mv_dst);
+    for (int i = blockIdx.x; i < n_mv; i += gridDim.x) {
+        const int sp = src_l[i], dp = dst_l[i];
+        if ((unsigned)sp >= (unsigned)K || (unsigned)dp >= (unsigned)K) {
+            if (threadIdx.x == 0) atomicOr(&L->counts[3], kErrBadList);
+            continue;
+        }
+        const auto* src = buf + (size_t)sp * cb;
+        auto* dst = buf + (size_t)dp * cb;
+        for (int c = threadIdx.x; c < cb; c += kNT * kU) {
+            typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+            u4 v[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                if (c + u * kNT < cb) v[u] = reinterpret_cast<const NP_GLOBAL u4*>(src)[c + u * kNT];
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                if (c + u * kNT < cb) reinterpret_cast<NP_GLOBAL u4*>(dst)[c + u * kNT] = v[u];
+        }
+    }
+}
+
 // Streaming read: every lane sums the low words of its 16-byte loads.
 __global__ __launch_bounds__(kNT) void k_probe_read(const uint4* __restrict__ src, int64_t n16, float* sink) {
     const int64_t stride = (int64_t)gridDim.x * kNT;
@@ -110,6 +141,11 @@ hipError_t launch_scatter(int32_t* counts, const int32_t* d_in, const int32_t* s
 
 hipError_t launch_scatter_all(const ScatterLaunch& a, int wgs_per_layer, hipStream_t s) {
     hipLaunchKernelGGL(k_scatter_all, dim3(wgs_per_layer, a.n_layers), dim3(kNT), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_move_all(const ScatterLaunch& a, int wgs_per_layer, hipStream_t s) {
+    hipLaunchKernelGGL(k_move_all, dim3(wgs_per_layer, a.n_layers), dim3(kNT), 0, s, a);
     return hipGetLastError();
 }
 

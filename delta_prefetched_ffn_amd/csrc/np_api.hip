@@ -60,6 +60,7 @@ struct DeviceGuard {
 
 enum LayerState { kFresh = 0, kAssigned = 1, kScattered = 2 };
 constexpr size_t kCountsBytes = 8 * 4 + 2 * 8;  // int32 counts[8] + 2 x uint64 running sums
+constexpr int kLists = 7;                        // K-entry lists per layer
 
 constexpr int kDefaultSlotsPerWg = 0;  // 0: one workgroup per compute unit
 constexpr int kDefaultTileCols = 256;
@@ -83,12 +84,13 @@ struct np_layer {
     int32_t* owner = nullptr;
     uint64_t* res = nullptr;
     uint64_t* freeb = nullptr;
-    int32_t* lists = nullptr;  // d_in | slot_in | d_out | act | act_src, K each
+    int32_t* lists = nullptr;  // d_in | slot_in | d_out | act | act_src | mv_src | mv_dst, K each
     int32_t* counts = nullptr;  // int32 [8], then the two 64-bit running sums (LayerDev::acc)
     uint64_t* ring = nullptr;   // window > 1: [window - 1][W] recent active sets
     int window = 1;
     uint64_t* levels = nullptr; // n_levels > 0: [n_levels][W] neurons per frequency level
     int n_levels = 0;
+    int layout = NP_LAYOUT_SLOTS;
     int reduce = NP_REDUCE_ATOMIC;  // how the FFN combines the partial sums of its workgroups
     LayerDev ldh{};             // host copy of *ldev
     uint64_t* hpair = nullptr;
@@ -109,6 +111,8 @@ struct np_layer {
     int32_t* d_out() const { return lists + 2 * (size_t)desc.k_max; }
     int32_t* act() const { return lists + 3 * (size_t)desc.k_max; }
     int32_t* act_src() const { return lists + 4 * (size_t)desc.k_max; }
+    int32_t* mv_src() const { return lists + 5 * (size_t)desc.k_max; }
+    int32_t* mv_dst() const { return lists + 6 * (size_t)desc.k_max; }
     size_t bundle_elems() const { return (size_t)desc.n_rows * desc.d_model; }
 };
 
@@ -202,7 +206,7 @@ np_status init_state(np_layer* L) {
     std::vector<uint64_t> fb(L->Kw, ~0ull);
     if (K & 63) fb[L->Kw - 1] = (1ull << (K & 63)) - 1;
     NP_HIP(hipMemcpy(L->freeb, fb.data(), (size_t)L->Kw * 8, hipMemcpyHostToDevice));
-    NP_HIP(hipMemset(L->lists, 0, (size_t)5 * K * 4));
+    NP_HIP(hipMemset(L->lists, 0, (size_t)kLists * K * 4));
     NP_HIP(hipMemset(L->counts, 0, kCountsBytes));
     if (L->ring) NP_HIP(hipMemset(L->ring, 0, (size_t)(L->window - 1) * L->W * 8));
     NP_HIP(hipDeviceSynchronize());
@@ -345,6 +349,19 @@ np_status enqueue_token(np_layer* const* layers, int n, const int32_t* cid, cons
         a.y = prm ? nullptr : y;
         a.d = d;
         NP_HIP(launch_delta_assign(a, cs));
+    }
+    // compacted layouts: the rows moved by the assignment, before anything writes new rows
+    {
+        ScatterLaunch ma{};
+        for (int l = 0; l < n; ++l) {
+            if (layers[l]->layout != NP_LAYOUT_COMPACT) continue;
+            ma.layers[ma.n_layers++] = layers[l]->ldev;
+            if (ma.n_layers == kMaxLayersPerLaunch) {
+                NP_HIP(launch_move_all(ma, kScatterWgsPerLayer, cs));
+                ma.n_layers = 0;
+            }
+        }
+        if (ma.n_layers > 0) NP_HIP(launch_move_all(ma, kScatterWgsPerLayer, cs));
     }
     if (one_queue(layers, n, cs, ps)) {
         // Device-memory row stores: each FFN reads its new bundles from the store and writes
@@ -586,7 +603,7 @@ np_status np_layer_create(const np_layer_desc* desc, np_layer** out) {
     bool ok = dmalloc((void**)&L->d_masks, mask_words * 8) && dmalloc((void**)&L->buf, buf_bytes) &&
               dmalloc((void**)&L->slot_map, (size_t)M * 4) && dmalloc((void**)&L->owner, (size_t)K * 4) &&
               dmalloc((void**)&L->res, (size_t)L->W * 8) && dmalloc((void**)&L->freeb, (size_t)L->Kw * 8) &&
-              dmalloc((void**)&L->lists, (size_t)5 * K * 4) && dmalloc((void**)&L->counts, kCountsBytes) &&
+              dmalloc((void**)&L->lists, (size_t)kLists * K * 4) && dmalloc((void**)&L->counts, kCountsBytes) &&
               dmalloc((void**)&L->hpair, (size_t)K * 8) &&
               dmalloc((void**)&L->ldev, sizeof(LayerDev));
     if (!ok) {
@@ -615,7 +632,9 @@ np_status np_layer_create(const np_layer_desc* desc, np_layer** out) {
     ld.window = 1;
     ld.levels = nullptr;
     ld.n_levels = 0;
-    ld.pad2 = 0;
+    ld.compact = 0;
+    ld.mv_src = L->mv_src();
+    ld.mv_dst = L->mv_dst();
     ld.W = L->W;
     ld.Kw = L->Kw;
     ld.M = M;
@@ -720,6 +739,12 @@ np_status np_delta_assign(np_layer* L, int32_t gate_cid, int32_t up_cid, void* s
     a.cid[0][1] = u;
     a.n_layers = 1;
     NP_HIP(launch_delta_assign(a, (hipStream_t)stream));
+    if (L->layout == NP_LAYOUT_COMPACT) {
+        ScatterLaunch ma{};
+        ma.layers[0] = L->ldev;
+        ma.n_layers = 1;
+        NP_HIP(launch_move_all(ma, kScatterWgsPerLayer, (hipStream_t)stream));
+    }
     L->h_res.swap(S);
     L->n_active = n;
     L->n_in = n_in;
@@ -947,6 +972,7 @@ np_status np_layer_set_window(np_layer* L, int32_t window) {
     if (!L) return fail(NP_EINVAL, "layer must not be NULL");
     if (window < 1 || window > kMaxWindow) return fail(NP_EINVAL, "window=%d must be in [1, %d]", window, kMaxWindow);
     if (window > 1 && L->n_levels > 0) return fail(NP_EINVAL, "a window excludes frequency levels (set n_levels 0 first)");
+    if (window > 1 && L->layout == NP_LAYOUT_COMPACT) return fail(NP_EINVAL, "a window needs the slot layout");
     if (L->state != kFresh) return fail(NP_ESTATE, "set the window before the first np_delta_assign (or after np_layer_reset)");
     DeviceGuard g(L->desc.device);
     NP_HIP(hipDeviceSynchronize());
@@ -997,6 +1023,7 @@ np_status np_layer_set_levels(np_layer* L, int32_t n_levels, const uint8_t* leve
     if (n_levels < 0 || n_levels > kMaxLevels) return fail(NP_EINVAL, "n_levels=%d must be in [0, %d]", n_levels, kMaxLevels);
     if (n_levels > 0 && !level) return fail(NP_EINVAL, "level must not be NULL when n_levels > 0");
     if (n_levels > 0 && L->window > 1) return fail(NP_EINVAL, "frequency levels exclude a window > 1 (set window 1 first)");
+    if (n_levels > 0 && L->layout == NP_LAYOUT_COMPACT) return fail(NP_EINVAL, "frequency levels need the slot layout");
     if (L->state != kFresh) return fail(NP_ESTATE, "set the levels before the first np_delta_assign (or after np_layer_reset)");
     const int M = L->desc.d_ff, W = L->W;
     std::vector<uint64_t> masks((size_t)n_levels * W, 0ull);
@@ -1032,6 +1059,37 @@ np_status np_layer_set_levels(np_layer* L, int32_t n_levels, const uint8_t* leve
     L->ldh = ld;
     NP_HIP(hipMemset(L->counts, 0, kCountsBytes));  // token count and running sums restart
     ++L->version;
+    return NP_OK;
+}
+
+np_status np_layer_set_layout(np_layer* L, int32_t layout) {
+    if (!L) return fail(NP_EINVAL, "layer must not be NULL");
+    if (layout != NP_LAYOUT_SLOTS && layout != NP_LAYOUT_COMPACT) return fail(NP_EINVAL, "unknown layout %d", layout);
+    if (layout == NP_LAYOUT_COMPACT && (L->window > 1 || L->n_levels > 0))
+        return fail(NP_EINVAL, "the compacted layout holds exactly S: no window or frequency levels");
+    if (L->state != kFresh) return fail(NP_ESTATE, "set the layout before the first np_delta_assign (or after np_layer_reset)");
+    DeviceGuard g(L->desc.device);
+    NP_HIP(hipDeviceSynchronize());
+    LayerDev ld = L->ldh;
+    ld.compact = layout == NP_LAYOUT_COMPACT ? 1 : 0;
+    NP_HIP(hipMemcpy(L->ldev, &ld, sizeof ld, hipMemcpyHostToDevice));
+    L->ldh = ld;
+    L->layout = layout;
+    ++L->version;
+    return NP_OK;
+}
+
+np_status np_layer_read_moves(const np_layer* L, int32_t* src, int32_t* dst, int32_t* n_moves) {
+    if (!L || !n_moves) return fail(NP_EINVAL, "layer and n_moves must not be NULL");
+    DeviceGuard g(L->desc.device);
+    NP_HIP(hipDeviceSynchronize());
+    int32_t n = 0;
+    if (L->layout == NP_LAYOUT_COMPACT && L->state != kFresh)
+        NP_HIP(hipMemcpy(&n, L->counts + 5, 4, hipMemcpyDeviceToHost));
+    n = std::max(0, std::min(n, L->desc.k_max));
+    if (n && src) NP_HIP(hipMemcpy(src, L->mv_src(), (size_t)n * 4, hipMemcpyDeviceToHost));
+    if (n && dst) NP_HIP(hipMemcpy(dst, L->mv_dst(), (size_t)n * 4, hipMemcpyDeviceToHost));
+    *n_moves = n;
     return NP_OK;
 }
 

@@ -38,7 +38,7 @@ struct LayerDev {
     int32_t* d_out;          // [K]
     int32_t* act;            // [K] ascending occupied slots
     int32_t* act_src;        // [K] per act position: the neuron if its slot was filled this step, else -1
-    int32_t* counts;         // [8] n_in, n_out, n_active, error bits, tokens assigned
+    int32_t* counts;         // [8] n_in, n_out, n_active, error bits, tokens assigned, moves
     unsigned long long* acc; // [2] running sums of n_active and n_in
     uint64_t* ring;          // [window - 1][W] active sets of the last tokens (window > 1)
     int32_t W, Kw, M, K;
@@ -50,7 +50,12 @@ struct LayerDev {
     // Retention by frequency level (n_levels > 0, window 1): bit masks of the neurons of each
     // level, highest level first ([n_levels][W]).
     const uint64_t* levels;
-    int32_t n_levels, pad2;
+    int32_t n_levels;
+    // Compacted layout (compact != 0): the active rows are positions 0 .. |S|-1; the rows
+    // moved this step are mv_src[k] -> mv_dst[k], k < counts[5].
+    int32_t compact;
+    int32_t* mv_src;         // [K]
+    int32_t* mv_dst;         // [K]
 };
 
 // One launch scattering the deltas of many layers (blockIdx.y = layer).
@@ -142,6 +147,7 @@ hipError_t launch_scatter(int32_t* counts, const int32_t* d_in, const int32_t* s
                           const uint16_t* store, uint16_t* buf, int32_t M, int32_t K,
                           int32_t bundle_elems, int grid, hipStream_t s);
 hipError_t launch_scatter_all(const ScatterLaunch& a, int wgs_per_layer, hipStream_t s);
+hipError_t launch_move_all(const ScatterLaunch& a, int wgs_per_layer, hipStream_t s);
 hipError_t launch_sparse_ffn(const FfnArgs& a, const FfnShape& sh, bool gated, hipStream_t s);
 hipError_t launch_probe_read(const void* src, int64_t bytes, float* sink, hipStream_t s);
 hipError_t launch_probe_copy(void* dst, const void* src, int64_t bytes, hipStream_t s);

@@ -152,6 +152,7 @@ np_status np_sparse_ffn_acc(np_layer* layer, const float* x, float* y, void* str
  * NP_REDUCE_ORDERED: the partial sums are exchanged and added in a fixed
  * order by one workgroup per output tile, one more cross-workgroup hop per
  * launch, bit-identical results run to run. Synchronizes the device. */
+typedef enum { NP_LAYOUT_SLOTS = 0, NP_LAYOUT_COMPACT = 1 } np_layout;
 typedef enum { NP_REDUCE_ATOMIC = 0, NP_REDUCE_ORDERED = 1 } np_reduce;
 np_status np_layer_set_ffn_reduce(np_layer* layer, int32_t mode);
 
@@ -242,6 +243,26 @@ np_status np_layer_set_window(np_layer* layer, int32_t window);
  * np_layer_info's n_in and np_layer_counters' |D_in| are read back from
  * the device. */
 np_status np_layer_set_levels(np_layer* layer, int32_t n_levels, const uint8_t* level);
+
+/* Buffer layout. NP_LAYOUT_SLOTS (the default; NeuroPrefetcher section 3.4):
+ * the slot map, incoming neurons take the lowest free slots, no compaction.
+ * NP_LAYOUT_COMPACT (LLM in a flash, section 3.3 "Optimized Data Management
+ * in DRAM"): the rows of S always occupy positions 0 .. |S|-1; with
+ * n_keep = |R| - |D_out|, each leaving row below n_keep (ascending) is
+ * replaced by the last staying row of the region (a move, copied on the
+ * device right after the assignment, before any new row is written), and
+ * the k-th incoming neuron (ascending) is appended at n_keep + k. The slot
+ * map, owner table and slot_in of np_layer_read_state then hold positions.
+ * Needs window 1 and no frequency levels (NP_EINVAL). Only before the first
+ * np_delta_assign after create or reset (NP_ESTATE). Synchronizes the
+ * layer's device. */
+np_status np_layer_set_layout(np_layer* layer, int32_t layout);
+
+/* The moves of the last assignment of a compacted layer: src[k] -> dst[k]
+ * (positions, ascending dst), *n_moves of them (capacity k_max each; 0 for
+ * the slot layout; src or dst may be NULL). Synchronizes the layer's
+ * device. */
+np_status np_layer_read_moves(const np_layer* layer, int32_t* src, int32_t* dst, int32_t* n_moves);
 
 /* FFN launch shape of this layer: about slots_per_wg active slots per
  * workgroup for the gate/up phase (1..16; the default, -1, sizes the grid to

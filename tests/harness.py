@@ -54,12 +54,13 @@ def make_layer(wl: Workload, l: int, where: str = "device", store: np.ndarray | 
 class OracleRun:
     """The oracle's state for every layer of a workload."""
 
-    def __init__(self, wl: Workload, keep_buffer: bool = True, window: int = 1, n_levels: int = 0):
+    def __init__(self, wl: Workload, keep_buffer: bool = True, window: int = 1, n_levels: int = 0,
+                 layout: str = "slots"):
         c = wl.cfg
         self.wl = wl
         self.layers = [O.OracleLayer(c.M, c.K, c.R, c.d, keep_buffer=keep_buffer, window=window,
                                      levels=wl.frequency_levels(l, n_levels) if n_levels else None,
-                                     n_levels=n_levels)
+                                     n_levels=n_levels, layout=layout)
                        for l in range(c.L)]
         self.mode = O.MODES[c.mode]
 

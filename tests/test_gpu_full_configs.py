@@ -24,7 +24,7 @@ def _log(msg):
 
 
 def run_full(num: int, where: str = "device", steps: int | None = None, ffn_samples: int = 10, window: int = 1,
-             n_levels: int = 0):
+             n_levels: int = 0, layout: str = "slots"):
     from delta_prefetched_ffn_amd import binding as B
     torch = torch_mod()
     assert torch.cuda.is_available()
@@ -39,8 +39,10 @@ def run_full(num: int, where: str = "device", steps: int | None = None, ffn_samp
             layers[-1].set_window(window)
         if n_levels:
             layers[-1].set_levels(wl.frequency_levels(l, n_levels), n_levels)
+        if layout != "slots":
+            layers[-1].set_layout(layout)
     _log(f"config {num}: {c.L} layers built ({where} store) in {time.time() - t0:.1f}s")
-    orc = OracleRun(wl, keep_buffer=False, window=window, n_levels=n_levels)
+    orc = OracleRun(wl, keep_buffer=False, window=window, n_levels=n_levels, layout=layout)
     x_all = wl.x_all()[:T]
     x = torch.from_numpy(np.ascontiguousarray(x_all)).cuda()
     y = torch.zeros_like(x)
@@ -54,6 +56,10 @@ def run_full(num: int, where: str = "device", steps: int | None = None, ffn_samp
             S, res = orc.step(t, l)
             compare_state(st, orc.layers[l], res, S, f"cfg{num} t={t} l={l}")
             if l == 0:
+                if res.mv_src.size:
+                    src, dst = layers[0].read_moves()
+                    assert np.array_equal(src, res.mv_src) and np.array_equal(dst, res.mv_dst), f"cfg{num} t={t}: moves"
+                    last_written[res.mv_dst] = last_written[res.mv_src]
                 last_written[res.slot_in] = res.d_in
             if l in row_layers and (t % 16 == 0 or t == T - 1) and res.d_in.size:
                 got = layers[l].read_rows(res.slot_in)
@@ -99,6 +105,13 @@ def test_full_config_residency_window(num, window):
 @pytest.mark.parametrize("num,n_levels", [(2, 8), (9, 8)])
 def test_full_config_frequency_levels(num, n_levels):
     run_full(num, "device", n_levels=n_levels)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("num,where", [(2, "device"), (9, "device"), (2, "host")])
+def test_full_config_compact_layout(num, where):
+    run_full(num, where, layout="compact", steps=None if where == "device" else 12,
+             ffn_samples=10 if where == "device" else 4)
 
 
 @pytest.mark.timeout(600)

@@ -46,6 +46,8 @@ def parse():
                    help="FFN partial-sum reduction: fp32 atomics (default) or fixed order (bit-reproducible)")
     p.add_argument("--window", type=int, default=1,
                    help="residency window in tokens (1: the buffer holds exactly the active set)")
+    p.add_argument("--layout", choices=["slots", "compact"], default="slots",
+                   help="resident buffer layout: slot map (default) or compacted prefix with row moves")
     p.add_argument("--levels", type=int, default=0,
                    help="retention by frequency level: number of levels (0: off; exclusive with --window)")
     p.add_argument("--steps", type=int, default=200)
@@ -187,6 +189,8 @@ def main():
                 L.set_window(args.window)
             if args.levels:
                 L.set_levels(wl.frequency_levels(l, args.levels), args.levels)
+            if args.layout != "slots":
+                L.set_layout(args.layout)
             L.set_ffn_reduce(args.reduce)
             out.append(L)
         return out
@@ -223,6 +227,17 @@ def main():
     eff_gbps = eff_bytes / elapsed / 1e9
     log(f"decode: {ms_per_step:.3f} ms/token, {tok_s:.1f} tok/s, effective {eff_gbps:.1f} GB/s "
         f"(host enqueue {enqueued * 1e3 / args.steps:.3f} ms/token)")
+    moves = None
+    if args.layout == "compact":  # rows moved inside the buffer (read + written in HBM), untimed pass
+        mv_toks = token_ids(1 + args.warmup + args.steps, 16, c.T)
+        n_mv = 0
+        for t in mv_toks:
+            run_tokens(layers, [t])
+            n_mv += sum(L.read_moves()[0].size for L in layers)
+        moves = {"mean_moves_per_layer": n_mv / (len(mv_toks) * c.L),
+                 "moved_bytes_per_token": 2 * n_mv / len(mv_toks) * c.bundle_bytes,
+                 "tokens": len(mv_toks)}
+        log(f"compact layout: {moves['mean_moves_per_layer']:.1f} rows moved per layer")
 
     # ---------------- FFN kernel timing (roofline of the dominant kernel) ----------------
     # As in the decode step, each FFN follows its layer's delta assignment directly and reads
@@ -352,11 +367,13 @@ def main():
                    "global_batch": 1, "layers": c.L, "d_model": c.d, "d_ff": c.M, "k_max": c.K,
                    "weights": "bf16", "backing_store": "HBM", "parallelism": "single GPU",
                    "residency_window": args.window, "frequency_levels": args.levels,
+                   "buffer_layout": args.layout,
                    "ffn_reduce": args.reduce},
         "effective_gbps": eff_gbps,
         "effective_frac_of_hbm_peak": eff_gbps / HBM_PEAK_GBPS,
         "mean_active_per_layer": act_bundles / (args.steps * c.L),
         "mean_delta_per_layer": in_bundles / (args.steps * c.L),
+        **({"compact_moves": moves} if moves else {}),
         "cold_start_ms": cold_ms,
         "host_enqueue_ms_per_step": enqueued * 1e3 / args.steps,
         "decode_launches": "captured graph replay" if args.graphs else "one by one",

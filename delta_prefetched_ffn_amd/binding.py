@@ -35,7 +35,7 @@ EXPORTS = ["np_layer_create", "np_layer_destroy", "np_layer_reset", "np_delta_as
            "np_layer_read_rows", "np_layer_info", "np_layer_counters", "np_layer_set_ffn_shape", "np_last_error",
            "np_probe_read", "np_probe_copy", "np_decode_use_graphs", "np_layer_set_window",
            "np_sparse_ffn_acc", "np_layer_set_ffn_reduce", "np_layer_set_levels",
-           "np_layer_set_layout", "np_layer_read_moves"]
+           "np_layer_set_layout", "np_layer_read_moves", "np_decode_set_staging"]
 
 
 class NPError(RuntimeError):
@@ -80,6 +80,7 @@ def lib() -> ctypes.CDLL:
         "np_layer_set_levels": [vp, i32, vp],
         "np_layer_set_layout": [vp, i32],
         "np_layer_read_moves": [vp, vp, vp, vp],
+        "np_decode_set_staging": [i64, i32],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -226,6 +227,11 @@ def decode_step(layers, cids: np.ndarray, x_ptr: int, y_ptr: int, compute_stream
     cs = compute_stream or None
     ps = cs if copy_stream is None else (copy_stream or None)
     _check(lib().np_decode_step(handles, len(layers), cids.ctypes.data, x_ptr, y_ptr, cs, ps))
+
+
+def decode_set_staging(nbytes: int, threads: int = 0) -> None:
+    """Staged delta I/O for pinned host row stores (0 bytes: zero-copy pull, the default)."""
+    _check(lib().np_decode_set_staging(nbytes, threads))
 
 
 def decode_use_graphs(enable: bool) -> None:

@@ -104,6 +104,33 @@ __global__ __launch_bounds__(kNT) void k_move_all(ScatterLaunch a) {
     }
 }
 
+// Staged delta (the I/O shape of NeuroPrefetcher section 3.5): the host gathered cnt
+// incoming bundles, in ascending neuron order, into a staging buffer that the DMA engine
+// copied to device memory; bundle i goes to slot slot_in[i]. One record per bundle, kept
+// interleaved in the slot, so the "deinterleave" is a plain bundle copy.
+__global__ __launch_bounds__(kNT) void k_scatter_staged(int32_t* counts, const int32_t* __restrict__ slot_in,
+                                                        const uint4* __restrict__ stage, uint4* __restrict__ buf,
+                                                        int32_t cnt, int32_t K, int32_t cb) {
+    for (int i = blockIdx.x; i < cnt; i += gridDim.x) {
+        const int s = slot_in[i];
+        if ((unsigned)s >= (unsigned)K) {
+            if (threadIdx.x == 0) atomicOr(&counts[3], kErrBadList);
+            continue;
+        }
+        const uint4* src = stage + (size_t)i * cb;
+        uint4* dst = buf + (size_t)s * cb;
+        for (int c = threadIdx.x; c < cb; c += kNT * kU) {
+            uint4 v[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                if (c + u * kNT < cb) v[u] = src[c + u * kNT];
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                if (c + u * kNT < cb) dst[c + u * kNT] = v[u];
+        }
+    }
+}
+
 // Streaming read: every lane sums the low words of its 16-byte loads.
 __global__ __launch_bounds__(kNT) void k_probe_read(const uint4* __restrict__ src, int64_t n16, float* sink) {
     const int64_t stride = (int64_t)gridDim.x * kNT;
@@ -146,6 +173,14 @@ hipError_t launch_scatter_all(const ScatterLaunch& a, int wgs_per_layer, hipStre
 
 hipError_t launch_move_all(const ScatterLaunch& a, int wgs_per_layer, hipStream_t s) {
     hipLaunchKernelGGL(k_move_all, dim3(wgs_per_layer, a.n_layers), dim3(kNT), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_scatter_staged(int32_t* counts, const int32_t* slot_in, const void* stage, uint16_t* buf,
+                                 int32_t cnt, int32_t K, int32_t bundle_elems, hipStream_t s) {
+    const int grid = std::max(1, std::min(cnt, 1024));
+    hipLaunchKernelGGL(k_scatter_staged, dim3(grid), dim3(kNT), 0, s, counts, slot_in,
+                       reinterpret_cast<const uint4*>(stage), reinterpret_cast<uint4*>(buf), cnt, K, bundle_elems / 8);
     return hipGetLastError();
 }
 

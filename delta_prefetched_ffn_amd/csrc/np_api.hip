@@ -12,7 +12,10 @@
 #include <map>
 #include <memory>
 #include <mutex>
+#include <condition_variable>
+#include <functional>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "np.h"
@@ -312,6 +315,158 @@ np_status enqueue_scatter(np_layer* L, hipStream_t s, bool fixed_grid = false) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// ---- staged delta I/O (NeuroPrefetcher section 3.5: the host reads the incoming rows, sorted
+// and with adjacent ones merged, into a bounded pinned staging buffer, the DMA engine copies it
+// to the device and a kernel places every bundle in its slot; a delta larger than the staging
+// is sent in chunks). The alternative, and the default, is the zero-copy pull by the scatter
+// kernel. Used by np_decode_step for host-memory row stores of layers whose delta the host
+// knows (no window, no frequency levels).
+
+// A fixed set of worker threads that run parts 1..n-1 of a job while the caller runs part 0.
+class GatherPool {
+public:
+    explicit GatherPool(int n) : n_(std::max(1, n)) {
+        for (int i = 1; i < n_; ++i) th_.emplace_back([this, i] { loop(i); });
+    }
+    ~GatherPool() {
+        {
+            std::lock_guard<std::mutex> lk(mu_);
+            stop_ = true;
+        }
+        cv_.notify_all();
+        for (auto& t : th_) t.join();
+    }
+    int size() const { return n_; }
+    void run(const std::function<void(int)>& f) {
+        {
+            std::lock_guard<std::mutex> lk(mu_);
+            job_ = &f;
+            pending_ = n_ - 1;
+            ++gen_;
+        }
+        cv_.notify_all();
+        f(0);
+        std::unique_lock<std::mutex> lk(mu_);
+        done_.wait(lk, [this] { return pending_ == 0; });
+        job_ = nullptr;
+    }
+
+private:
+    void loop(int i) {
+        uint64_t seen = 0;
+        for (;;) {
+            const std::function<void(int)>* f;
+            {
+                std::unique_lock<std::mutex> lk(mu_);
+                cv_.wait(lk, [&] { return stop_ || gen_ != seen; });
+                if (stop_) return;
+                seen = gen_;
+                f = job_;
+            }
+            (*f)(i);
+            std::lock_guard<std::mutex> lk(mu_);
+            if (--pending_ == 0) done_.notify_one();
+        }
+    }
+    int n_;
+    std::vector<std::thread> th_;
+    std::mutex mu_;
+    std::condition_variable cv_, done_;
+    const std::function<void(int)>* job_ = nullptr;
+    int pending_ = 0;
+    uint64_t gen_ = 0;
+    bool stop_ = false;
+};
+
+struct Stager {
+    int dev = -1;
+    size_t cap = 0;                 // bytes per half
+    void* host[2] = {nullptr, nullptr};  // pinned staging (hipHostMalloc)
+    void* devb[2] = {nullptr, nullptr};  // device staging
+    hipEvent_t ready[2] = {nullptr, nullptr};  // the last copy out of host[h] (and its scatter) done
+    int next = 0;
+    std::unique_ptr<GatherPool> pool;
+    ~Stager() {
+        for (int h = 0; h < 2; ++h) {
+            if (ready[h]) (void)hipEventSynchronize(ready[h]);
+            if (ready[h]) (void)hipEventDestroy(ready[h]);
+            if (host[h]) (void)hipHostFree(host[h]);
+            if (devb[h]) (void)hipFree(devb[h]);
+        }
+    }
+};
+
+std::mutex g_stage_mu;                 // guards the settings and the stagers
+size_t g_stage_bytes = 0;              // 0: zero-copy pull (default)
+int g_stage_threads = 0;
+// Never destroyed: at process exit the HIP runtime may already be gone, and the pool threads
+// are then simply ended with the process.
+std::map<int, std::unique_ptr<Stager>>& g_stagers = *new std::map<int, std::unique_ptr<Stager>>();
+
+bool staged(const np_layer* L) { return g_stage_bytes > 0 && L->store_is_host && !device_decides(L); }
+
+np_status get_stager(int dev, Stager** out) {
+    auto& sp = g_stagers[dev];
+    if (!sp) {
+        auto st = std::make_unique<Stager>();
+        st->dev = dev;
+        st->cap = g_stage_bytes;
+        for (int h = 0; h < 2; ++h) {
+            if (hipHostMalloc(&st->host[h], st->cap, hipHostMallocDefault) != hipSuccess ||
+                hipMalloc(&st->devb[h], st->cap) != hipSuccess ||
+                hipEventCreateWithFlags(&st->ready[h], hipEventDisableTiming) != hipSuccess) {
+                (void)hipGetLastError();
+                return fail(NP_ENOMEM, "cannot allocate two %zu-byte staging buffers", st->cap);
+            }
+            NP_HIP(hipEventRecord(st->ready[h], nullptr));
+        }
+        st->pool = std::make_unique<GatherPool>(g_stage_threads);
+        sp = std::move(st);
+    }
+    *out = sp.get();
+    return NP_OK;
+}
+
+// Layer L's incoming bundles (d_in ascending, as the assignment lists them) through the staging
+// buffers in chunks; everything on stream s, which must already follow L's assignment.
+np_status enqueue_staged(np_layer* L, const std::vector<int32_t>& d_in, hipStream_t s, Stager* st) {
+    const size_t bb = L->bundle_elems() * 2;
+    const int per = (int)std::min<size_t>(st->cap / bb, (size_t)L->desc.k_max);
+    if (per < 1) return fail(NP_EINVAL, "staging of %zu bytes holds no %zu-byte bundle", st->cap, bb);
+    const char* store = static_cast<const char*>(L->desc.row_store);
+    const int n = (int)d_in.size();
+    std::vector<std::pair<int, int>> runs;  // (first index in the chunk, length) of adjacent IDs
+    for (int first = 0; first < n; first += per) {
+        const int cnt = std::min(per, n - first);
+        const int h = st->next;
+        st->next ^= 1;
+        NP_HIP(hipEventSynchronize(st->ready[h]));  // the copy that last read host[h] is done
+        runs.clear();
+        for (int i = 0; i < cnt; ++i) {
+            if (!runs.empty() && d_in[first + i] == d_in[first + i - 1] + 1) ++runs.back().second;
+            else runs.emplace_back(i, 1);
+        }
+        char* dst = static_cast<char*>(st->host[h]);
+        const int parts = st->pool->size();
+        const std::function<void(int)> job = [&](int part) {
+            // runs split over the parts by bundle count
+            const int lo = (int)((int64_t)cnt * part / parts), hi = (int)((int64_t)cnt * (part + 1) / parts);
+            for (const auto& r : runs) {
+                const int a = std::max(lo, r.first), b = std::min(hi, r.first + r.second);
+                if (a >= b) continue;
+                const int32_t nid = d_in[first + r.first] + (a - r.first);
+                std::memcpy(dst + (size_t)a * bb, store + (size_t)nid * bb, (size_t)(b - a) * bb);
+            }
+        };
+        st->pool->run(job);
+        NP_HIP(hipMemcpyAsync(st->devb[h], st->host[h], (size_t)cnt * bb, hipMemcpyHostToDevice, s));
+        NP_HIP(launch_scatter_staged(L->counts, L->slot_in() + first, st->devb[h], L->buf, cnt, L->desc.k_max,
+                                     (int32_t)L->bundle_elems(), s));
+        NP_HIP(hipEventRecord(st->ready[h], s));
+    }
+    return NP_OK;
+}
+
 // A token's launches go to one queue (assign, the FFNs in layer order, which read their new
 // bundles through from device-memory row stores; one scatter launch first for host-memory
 // stores) unless some row store is in host memory and a separate copy stream is given: then
@@ -330,7 +485,8 @@ constexpr int kScatterWgsPerLayer = 64;
 // decode graph) the ids, x and y come from the parameter block instead. ev: n + 2 events, used
 // only on the two-stream path.
 np_status enqueue_token(np_layer* const* layers, int n, const int32_t* cid, const float* x, float* y,
-                        hipStream_t cs, hipStream_t ps, const DecodeParams* prm, const hipEvent_t* ev) {
+                        hipStream_t cs, hipStream_t ps, const DecodeParams* prm, const hipEvent_t* ev,
+                        const std::vector<std::vector<int32_t>>* din = nullptr, Stager* st = nullptr) {
     const int d = layers[0]->desc.d_model;
     // the assign launch clears every layer's y, so the FFN launches add into zeros
     bool any_atomic = false;
@@ -369,6 +525,11 @@ np_status enqueue_token(np_layer* const* layers, int n, const int32_t* cid, cons
         ScatterLaunch sa{};
         for (int l = 0; l < n; ++l) {
             if (!layers[l]->store_is_host) continue;
+            if (din && st && staged(layers[l])) {
+                np_status r = enqueue_staged(layers[l], (*din)[l], cs, st);
+                if (r != NP_OK) return r;
+                continue;
+            }
             sa.layers[sa.n_layers++] = layers[l]->ldev;
             if (sa.n_layers == kMaxLayersPerLaunch) {
                 NP_HIP(launch_scatter_all(sa, kScatterWgsPerLayer, cs));
@@ -377,22 +538,23 @@ np_status enqueue_token(np_layer* const* layers, int n, const int32_t* cid, cons
         }
         if (sa.n_layers > 0) NP_HIP(launch_scatter_all(sa, kScatterWgsPerLayer, cs));
         for (int l = 0; l < n; ++l) {
-            np_status st = enqueue_ffn(layers[l], prm ? nullptr : x + (size_t)l * d, prm ? nullptr : y + (size_t)l * d,
-                                       cs, prm, l, !layers[l]->store_is_host, any_atomic);
-            if (st != NP_OK) return st;
+            np_status r = enqueue_ffn(layers[l], prm ? nullptr : x + (size_t)l * d, prm ? nullptr : y + (size_t)l * d,
+                                      cs, prm, l, !layers[l]->store_is_host, any_atomic);
+            if (r != NP_OK) return r;
         }
         return NP_OK;
     }
     NP_HIP(hipEventRecord(ev[0], cs));
     NP_HIP(hipStreamWaitEvent(ps, ev[0], 0));
     for (int l = 0; l < n; ++l) {
-        np_status st = enqueue_scatter(layers[l], ps, prm != nullptr);
-        if (st != NP_OK) return st;
+        np_status r = din && st && staged(layers[l]) ? enqueue_staged(layers[l], (*din)[l], ps, st)
+                                                     : enqueue_scatter(layers[l], ps, prm != nullptr);
+        if (r != NP_OK) return r;
         NP_HIP(hipEventRecord(ev[2 + l], ps));
         NP_HIP(hipStreamWaitEvent(cs, ev[2 + l], 0));
-        st = enqueue_ffn(layers[l], prm ? nullptr : x + (size_t)l * d, prm ? nullptr : y + (size_t)l * d, cs, prm, l,
-                         false, any_atomic);
-        if (st != NP_OK) return st;
+        r = enqueue_ffn(layers[l], prm ? nullptr : x + (size_t)l * d, prm ? nullptr : y + (size_t)l * d, cs, prm, l,
+                        false, any_atomic);
+        if (r != NP_OK) return r;
     }
     NP_HIP(hipEventRecord(ev[1], ps));  // join the copy stream back to the compute stream
     NP_HIP(hipStreamWaitEvent(cs, ev[1], 0));
@@ -807,6 +969,11 @@ np_status np_decode_step(np_layer* const* layers, int32_t n_layers, const int32_
     const int dev = L0->desc.device, d = L0->desc.d_model;
     std::vector<std::vector<uint64_t>> S(n_layers);
     std::vector<int> n_act(n_layers), n_in(n_layers), u_eff(n_layers);
+    std::unique_lock<std::mutex> stage_lk(g_stage_mu);  // staging settings and buffers
+    const bool stage_on = g_stage_bytes > 0;
+    if (!stage_on) stage_lk.unlock();
+    bool any_staged = false;
+    std::vector<std::vector<int32_t>> din(n_layers);
     for (int l = 0; l < n_layers; ++l) {
         const np_layer* L = layers[l];
         if (!L) return fail(NP_EINVAL, "layer %d is NULL", l);
@@ -829,6 +996,13 @@ np_status np_decode_step(np_layer* const* layers, int32_t n_layers, const int32_
             for (int w = 0; w < L->W; ++w) ni += __builtin_popcountll(S[l][w] & ~L->h_res[w]);
         }
         n_in[l] = ni;
+        if (stage_on && staged(L)) {  // the host reads these rows itself (staged I/O)
+            any_staged = true;
+            din[l].reserve(ni);
+            for (int w = 0; w < L->W; ++w)
+                for (uint64_t b = S[l][w] & ~L->h_res[w]; b; b &= b - 1)
+                    din[l].push_back(w * 64 + __builtin_ctzll(b));
+        }
     }
     DeviceGuard g(dev);
     hipStream_t cs = (hipStream_t)compute_stream, ps = (hipStream_t)copy_stream;
@@ -844,7 +1018,7 @@ np_status np_decode_step(np_layer* const* layers, int32_t n_layers, const int32_
         }
     };
 
-    if (g_use_graphs.load() && n_layers <= kMaxGraphLayers && cs && ps) {
+    if (g_use_graphs.load() && n_layers <= kMaxGraphLayers && cs && ps && !any_staged) {
         np_status st = NP_OK;
         DecodePlan* P = get_plan(layers, n_layers, cs, ps, dev, &st);
         if (P) {
@@ -884,8 +1058,18 @@ np_status np_decode_step(np_layer* const* layers, int32_t n_layers, const int32_
     }
     // the direct launches size their grids from the new host counts; a launch failure leaves the
     // layers assigned-but-unscattered, so they need np_layer_reset before further use
+    Stager* stg = nullptr;
+    if (any_staged) {
+        for (int l = 0; l < n_layers; ++l)
+            if (staged(layers[l]) && g_stage_bytes < layers[l]->bundle_elems() * 2)
+                return fail(NP_EINVAL, "layer %d: staging of %zu bytes holds no %zu-byte bundle", l, g_stage_bytes,
+                            (size_t)layers[l]->bundle_elems() * 2);
+        np_status r = get_stager(dev, &stg);
+        if (r != NP_OK) return r;
+    }
     commit_host_state();
-    np_status st = enqueue_token(layers, n_layers, cid_eff.data(), x, y, cs, ps, nullptr, ev);
+    np_status st = enqueue_token(layers, n_layers, cid_eff.data(), x, y, cs, ps, nullptr, ev,
+                                 any_staged ? &din : nullptr, stg);
     if (st != NP_OK) return st;
     for (int l = 0; l < n_layers; ++l) layers[l]->state = kScattered;
     return NP_OK;
@@ -1090,6 +1274,17 @@ np_status np_layer_read_moves(const np_layer* L, int32_t* src, int32_t* dst, int
     if (n && src) NP_HIP(hipMemcpy(src, L->mv_src(), (size_t)n * 4, hipMemcpyDeviceToHost));
     if (n && dst) NP_HIP(hipMemcpy(dst, L->mv_dst(), (size_t)n * 4, hipMemcpyDeviceToHost));
     *n_moves = n;
+    return NP_OK;
+}
+
+np_status np_decode_set_staging(int64_t bytes, int32_t threads) {
+    if (bytes < 0 || bytes > (int64_t)1 << 30) return fail(NP_EINVAL, "staging bytes=%lld must be in [0, 1 GiB]", (long long)bytes);
+    if (threads < 0 || threads > 64) return fail(NP_EINVAL, "threads=%d must be in [0, 64]", threads);
+    std::lock_guard<std::mutex> lk(g_stage_mu);
+    g_stagers.clear();  // waits for their last copies, frees the buffers
+    g_stage_bytes = (size_t)bytes;
+    const int hw = (int)std::thread::hardware_concurrency();
+    g_stage_threads = threads ? threads : std::max(1, std::min(8, hw));
     return NP_OK;
 }
 

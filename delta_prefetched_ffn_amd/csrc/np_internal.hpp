@@ -148,6 +148,8 @@ hipError_t launch_scatter(int32_t* counts, const int32_t* d_in, const int32_t* s
                           int32_t bundle_elems, int grid, hipStream_t s);
 hipError_t launch_scatter_all(const ScatterLaunch& a, int wgs_per_layer, hipStream_t s);
 hipError_t launch_move_all(const ScatterLaunch& a, int wgs_per_layer, hipStream_t s);
+hipError_t launch_scatter_staged(int32_t* counts, const int32_t* slot_in, const void* stage, uint16_t* buf,
+                                 int32_t cnt, int32_t K, int32_t bundle_elems, hipStream_t s);
 hipError_t launch_sparse_ffn(const FfnArgs& a, const FfnShape& sh, bool gated, hipStream_t s);
 hipError_t launch_probe_read(const void* src, int64_t bytes, float* sink, hipStream_t s);
 hipError_t launch_probe_copy(void* dst, const void* src, int64_t bytes, hipStream_t s);

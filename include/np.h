@@ -186,6 +186,23 @@ np_status np_decode_step(np_layer* const* layers, int32_t n_layers, const int32_
  * one). Results are the same either way. */
 np_status np_decode_use_graphs(int32_t enable);
 
+/* Delta I/O of np_decode_step for row stores in pinned host memory.
+ * bytes = 0 (the default): zero-copy pull, the scatter kernel reads the
+ * incoming bundles over the host link. bytes > 0: the I/O shape of
+ * NeuroPrefetcher section 3.5 -- the host copies each layer's incoming
+ * bundles, in ascending neuron order and with adjacent neurons merged into
+ * one copy, into a pinned staging buffer of `bytes` (two of them, used in
+ * turn), the DMA engine copies the staging to device memory and a kernel
+ * places each bundle in its slot; a delta larger than the staging goes in
+ * several chunks. threads host threads share each gather (0: min(8, cores)).
+ * Applies to layers without a window or frequency levels (their delta is
+ * known on the host); others keep the zero-copy pull. A staged
+ * np_decode_step returns once every gather is done, and is never replayed
+ * from a graph. 0 <= bytes <= 1 GiB (a chunk must hold one bundle, else
+ * np_decode_step fails with NP_EINVAL), 0 <= threads <= 64. Waits for the
+ * copies of the staging buffers it replaces. Process-wide setting. */
+np_status np_decode_set_staging(int64_t bytes, int32_t threads);
+
 /* Synchronizes the layer's device, then copies the current state to host
  * buffers (any pointer may be NULL): slot_map int32 [d_ff], owner int32
  * [k_max], d_in / slot_in / d_out int32 [k_max] (lists of the last

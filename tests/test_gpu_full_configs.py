@@ -24,7 +24,7 @@ def _log(msg):
 
 
 def run_full(num: int, where: str = "device", steps: int | None = None, ffn_samples: int = 10, window: int = 1,
-             n_levels: int = 0, layout: str = "slots"):
+             n_levels: int = 0, layout: str = "slots", staging: int = 0):
     from delta_prefetched_ffn_amd import binding as B
     torch = torch_mod()
     assert torch.cuda.is_available()
@@ -43,6 +43,7 @@ def run_full(num: int, where: str = "device", steps: int | None = None, ffn_samp
             layers[-1].set_layout(layout)
     _log(f"config {num}: {c.L} layers built ({where} store) in {time.time() - t0:.1f}s")
     orc = OracleRun(wl, keep_buffer=False, window=window, n_levels=n_levels, layout=layout)
+    B.decode_set_staging(staging)
     x_all = wl.x_all()[:T]
     x = torch.from_numpy(np.ascontiguousarray(x_all)).cuda()
     y = torch.zeros_like(x)
@@ -82,6 +83,7 @@ def run_full(num: int, where: str = "device", steps: int | None = None, ffn_samp
         ref = O.sparse_ffn(wl.bundles(l, S), c.R, c.d, np.arange(S.size, dtype=np.int32), x_all[t, l], c.act)
         check_y(yh[t, l], ref, f"cfg{num} t={t} l={l}")
     _log(f"config {num}: {T} steps, {len(picks)} FFN samples ok in {time.time() - t0:.1f}s")
+    B.decode_set_staging(0)
     for layer in layers:
         layer.close()
     del layers
@@ -112,6 +114,14 @@ def test_full_config_frequency_levels(num, n_levels):
 def test_full_config_compact_layout(num, where):
     run_full(num, where, layout="compact", steps=None if where == "device" else 12,
              ffn_samples=10 if where == "device" else 4)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("staging", [8 << 20, 1 << 20])
+def test_full_config2_staged_delta_io(staging):
+    """Pinned host store, deltas staged by the host and copied by the DMA engine (1 MiB staging:
+    about five chunks per layer)."""
+    run_full(2, "host", steps=12, ffn_samples=4, staging=staging)
 
 
 @pytest.mark.timeout(600)

@@ -58,6 +58,10 @@ def parse():
                    help="replay each decode step as a captured HIP graph instead of launching one by one")
     p.add_argument("--pcie-steps", type=int, default=40, help="timed tokens with the store in pinned host memory")
     p.add_argument("--no-pcie", action="store_true")
+    p.add_argument("--staging-mb", type=float, default=0.0,
+                   help="also time the staged delta I/O (host gather + DMA copy + device scatter) with this "
+                        "much pinned staging per buffer (two buffers), reported as pcie_staged")
+    p.add_argument("--staging-threads", type=int, default=0, help="host gather threads (0: library default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle sample")
     p.add_argument("--slots-per-wg", type=int, default=0)
@@ -322,8 +326,7 @@ def main():
     torch.cuda.empty_cache()
 
     # ---------------- PCIe-inclusive: backing store in pinned host memory ----------------
-    pcie = None
-    if not args.no_pcie:
+    def host_leg():
         hl = make_layers("host")
         run_tokens(hl, [0])
         run_tokens(hl, token_ids(1, 4, c.T))
@@ -336,13 +339,23 @@ def main():
         el = time.perf_counter() - ts
         b1 = np.array([L.counters() for L in hl], dtype=np.int64).sum(axis=0)
         d_act, d_in = (b1 - b0).tolist()
-        pcie = {"tokens_per_s": args.pcie_steps / el, "ms_per_step": el * 1e3 / args.pcie_steps,
-                "delta_gbps_over_host_link": d_in * c.bundle_bytes / el / 1e9,
-                "steps": args.pcie_steps, "store": "pinned host memory (hipHostMalloc via torch)"}
-        log(f"pcie-inclusive: {pcie['tokens_per_s']:.1f} tok/s, delta {pcie['delta_gbps_over_host_link']:.1f} GB/s")
         for L in hl:
             L.close()
-        del hl
+        return {"tokens_per_s": args.pcie_steps / el, "ms_per_step": el * 1e3 / args.pcie_steps,
+                "delta_gbps_over_host_link": d_in * c.bundle_bytes / el / 1e9,
+                "steps": args.pcie_steps, "store": "pinned host memory (hipHostMalloc via torch)"}
+
+    pcie = staged = None
+    if not args.no_pcie:
+        pcie = host_leg()
+        log(f"pcie-inclusive: {pcie['tokens_per_s']:.1f} tok/s, delta {pcie['delta_gbps_over_host_link']:.1f} GB/s")
+        if args.staging_mb > 0:
+            B.decode_set_staging(int(args.staging_mb * (1 << 20)), args.staging_threads)
+            staged = host_leg()
+            B.decode_set_staging(0)
+            staged["staging_bytes"] = int(args.staging_mb * (1 << 20))
+            staged["gather_threads"] = args.staging_threads or "library default (min(8, cores))"
+            log(f"pcie-staged: {staged['tokens_per_s']:.1f} tok/s, delta {staged['delta_gbps_over_host_link']:.1f} GB/s")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -389,6 +402,7 @@ def main():
         "hbm_read_probe_gbps": probe_gbps,
         "hbm_copy_probe_gbps": copy_gbps,
         "pcie_inclusive": pcie,
+        **({"pcie_staged": staged} if staged else {}),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

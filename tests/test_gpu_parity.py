@@ -222,6 +222,49 @@ def test_edge_cases_empty_full_turnover_and_exact_capacity(torch):
     layer.close()
 
 
+LIMITS = [
+    # the largest d_model (16384: 512-thread FFN workgroups, four x chunks per lane, 64 tiles)
+    small_config(970, L=1, d=16384, M=320, K=200, C=4, mode="union", m=90, swap=10, T=5),
+    # the largest d_ff and k_max (65536; owner table far beyond the per-thread preload) with
+    # the smallest d_model, |S| of tens of thousands, ragged last words nowhere
+    small_config(971, L=1, d=8, M=65536, K=65536, C=3, mode="union", m=30000, swap=3000, T=4),
+    # d_ff and k_max just under the limit with ragged words, non-gated SiLU
+    small_config(972, L=1, d=24, M=65535, K=60001, C=3, mode="single", R=2, m=50000, swap=5000, T=4, act="silu"),
+    # one neuron, one slot
+    small_config(973, L=1, d=8, M=1, K=1, C=2, mode="union", m=1, swap=0, T=4),
+]
+
+
+@pytest.mark.parametrize("cfg", LIMITS, ids=lambda c: f"d{c.d}_M{c.M}_K{c.K}_{c.mode}_R{c.R}")
+def test_maximum_and_minimum_sizes(torch, cfg):
+    """The documented size limits and the degenerate one-neuron layer, through np_decode_step:
+    state and buffer bit-exact, y in tolerance."""
+    from delta_prefetched_ffn_amd import binding as B
+    print(f"[limits] d={cfg.d} M={cfg.M} K={cfg.K}", flush=True)
+    wl = Workload(cfg)
+    layers, stores = zip(*[make_layer(wl, l) for l in range(cfg.L)])
+    orc = OracleRun(wl)
+    x_all = wl.x_all()
+    x = torch.from_numpy(x_all).cuda()
+    y = torch.zeros_like(x)
+    s = _stream(torch)
+    for t in range(cfg.T):
+        B.decode_step(layers, wl.cids()[t], x[t].data_ptr(), y[t].data_ptr(), s, s)
+        for l, layer in enumerate(layers):
+            st = layer.read_state()
+            S, res = orc.step(t, l, stores[l])
+            compare_state(st, orc.layers[l], res, S, f"t={t} l={l}")
+            assert np.array_equal(layer.read_rows(), orc.layers[l].buf), f"t={t} l={l}: buffer"
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+    for t in range(cfg.T):
+        for l in range(cfg.L):
+            S = orc.active(t, l)
+            check_y(yh[t, l], O.sparse_ffn(stores[l], cfg.R, cfg.d, S, x_all[t, l], cfg.act), f"t={t} l={l}")
+    for layer in layers:
+        layer.close()
+
+
 @pytest.mark.parametrize("shape", [(3, 128, 256), (5, 256, 512), (5, 256, 1024), (2, 64, 1024), (8, 128, 512),
                                    (16, 256, 256), (1, 256, 256)])
 def test_ffn_launch_shapes(torch, shape):

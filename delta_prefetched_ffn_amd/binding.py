@@ -35,7 +35,8 @@ EXPORTS = ["np_layer_create", "np_layer_destroy", "np_layer_reset", "np_delta_as
            "np_layer_read_rows", "np_layer_info", "np_layer_counters", "np_layer_set_ffn_shape", "np_last_error",
            "np_probe_read", "np_probe_copy", "np_decode_use_graphs", "np_layer_set_window",
            "np_sparse_ffn_acc", "np_layer_set_ffn_reduce", "np_layer_set_levels",
-           "np_layer_set_layout", "np_layer_read_moves", "np_decode_set_staging"]
+           "np_layer_set_layout", "np_layer_read_moves", "np_decode_set_staging",
+           "np_layer_set_planar"]
 
 
 class NPError(RuntimeError):
@@ -81,6 +82,7 @@ def lib() -> ctypes.CDLL:
         "np_layer_set_layout": [vp, i32],
         "np_layer_read_moves": [vp, vp, vp, vp],
         "np_decode_set_staging": [i64, i32],
+        "np_layer_set_planar": [vp, i32],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -169,6 +171,10 @@ class Layer:
     def set_layout(self, layout: str) -> None:
         """"slots" (slot map, the default) or "compact" (active rows at positions 0 .. |S|-1)."""
         _check(lib().np_layer_set_layout(self.h, LAYOUTS[layout]))
+
+    def set_planar(self, planar: bool) -> None:
+        """Slot buffer as one plane per row kind (True) or one bundle per slot (False, the default)."""
+        _check(lib().np_layer_set_planar(self.h, 1 if planar else 0))
 
     def read_moves(self) -> tuple[np.ndarray, np.ndarray]:
         """(src, dst) positions of the rows the last assignment moved (compact layout)."""

@@ -193,15 +193,19 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     }
 
     // ---------------- phase 1 loads: gate/up rows of chunk w (issued first) ----------------
-    const size_t slot_bytes = (size_t)R * cpr * 16u;
+    const size_t slot_bytes = (size_t)R * cpr * 16u;  // a bundle in the row store
     const char* const buf_c = reinterpret_cast<const char*>(a.buf);
     char* const buf_w = reinterpret_cast<char*>(a.buf);
     const char* const store_c = reinterpret_cast<const char*>(a.store);
-    // Start of the bundle at window position p: its slot, or the row store for a slot
-    // filled this step (read-through).
-    auto row_base = [&](int p) -> const char* {
+    // Row r of the slot at window position p in the slot buffer (interleaved or planar).
+    auto slot_row = [&](int p, int r) -> size_t {
+        return (size_t)s_act[p] * a.slot_stride + (size_t)r * a.row_plane;
+    };
+    // Start of row r of the bundle at window position p: in its slot, or in the row store for a
+    // slot filled this step (read-through).
+    auto row_at = [&](int p, int r) -> const char* {
         const int src = s_src[p];
-        return src >= 0 ? store_c + (size_t)src * slot_bytes : buf_c + (size_t)s_act[p] * slot_bytes;
+        return src >= 0 ? store_c + (size_t)src * slot_bytes + (size_t)r * cpr * 16u : buf_c + slot_row(p, r);
     };
     const bool has1 = w < a.p1;
     const int c0 = has1 ? max(cbeg(w), plo) : 0, c1 = has1 ? min(cbeg(w + 1), phi) : 0;
@@ -211,14 +215,15 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
         for (int i = 0; i < SB; ++i) {
             const int pos = b0 + rl + RL * i;
             const bool ok = pos < c1;
-            const char* rp = ok ? row_base(pos - plo) : buf_c;
 #pragma unroll
-            for (int r = 0; r < NR1; ++r)
+            for (int r = 0; r < NR1; ++r) {
+                const char* rp = ok ? row_at(pos - plo, r) : buf_c;
 #pragma unroll
                 for (int j = 0; j < JX; ++j) {
                     const int c = cl + CL * j;
-                    wv[i][r][j] = gload(ok && c < cpr ? rp + (size_t)(r * cpr + c) * 16u : buf_c);
+                    wv[i][r][j] = gload(ok && c < cpr ? rp + (size_t)c * 16u : buf_c);
                 }
+            }
         }
     };
     // h for the batch starting at b0: dot products, reduction over the row lane, store.
@@ -230,14 +235,15 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
             for (int i = 0; i < SB; ++i) {
                 const int pos = b0 + rl + RL * i;
                 if (pos < c1 && s_src[pos - plo] >= 0) {
-                    char* dst = buf_w + (size_t)s_act[pos - plo] * slot_bytes;
 #pragma unroll
-                    for (int r = 0; r < NR1; ++r)
+                    for (int r = 0; r < NR1; ++r) {
+                        char* dst = buf_w + slot_row(pos - plo, r);
 #pragma unroll
                         for (int j = 0; j < JX; ++j) {
                             const int c = cl + CL * j;
-                            if (c < cpr) gstore(dst + (size_t)(r * cpr + c) * 16u, wv[i][r][j]);
+                            if (c < cpr) gstore(dst + (size_t)c * 16u, wv[i][r][j]);
                         }
+                    }
                 }
             }
         }
@@ -316,12 +322,12 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     const int RL2 = NT / CT;                  // row lanes
     const int c2 = tid % CT, r2 = tid / CT;
     const bool cok = (c2 << 3) < tcols;
-    const size_t dcol = ((size_t)(R - 1) * cpr + (col0 >> 3) + c2) * 16u;
+    const size_t dcol = ((size_t)(col0 >> 3) + c2) * 16u;  // this lane's columns within a down row
     uint4 dv[U2];
 #pragma unroll
     for (int u = 0; u < U2; ++u) {
         const int i = r2 + u * RL2;
-        dv[u] = gload(cok && i < wn ? row_base(i) + dcol : buf_c);
+        dv[u] = gload(cok && i < wn ? row_at(i, R - 1) + dcol : buf_c);
     }
 
     // ---------------- phase 1 compute: h for chunk w ----------------
@@ -372,7 +378,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
             if (cok && i < wn) {
                 axpy8(acc, s_h[i], dv[u]);
                 // read-through: this tile's piece of the down row goes into its slot
-                if (rt && s_src[i] >= 0) gstore(buf_w + (size_t)s_act[i] * slot_bytes + dcol, dv[u]);
+                if (rt && s_src[i] >= 0) gstore(buf_w + slot_row(i, R - 1) + dcol, dv[u]);
             }
         }
         i0 += U2 * RL2;
@@ -380,7 +386,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
 #pragma unroll
         for (int u = 0; u < U2; ++u) {
             const int i = i0 + u * RL2;
-            dv[u] = gload(cok && i < wn ? row_base(i) + dcol : buf_c);
+            dv[u] = gload(cok && i < wn ? row_at(i, R - 1) + dcol : buf_c);
         }
     }
 

@@ -16,11 +16,18 @@ namespace {
 constexpr int kNT = 256;
 constexpr int kU = 8;
 
+// 16-byte chunk c of a bundle (rows of row16 chunks, one after the other) in slot s of the
+// slot buffer: row r = c / row16 lives at s * stride16 + r * plane16 (interleaved or planar).
+__device__ inline size_t slot_chunk(int s, int c, int row16, int stride16, int64_t plane16) {
+    const int r = c / row16;
+    return (size_t)s * stride16 + (size_t)r * plane16 + (size_t)(c - r * row16);
+}
+
 __global__ __launch_bounds__(kNT) void k_scatter_rows(int32_t* counts, const int32_t* __restrict__ d_in,
                                                       const int32_t* __restrict__ slot_in,
                                                       const uint4* __restrict__ store,
                                                       uint4* __restrict__ buf, int32_t M, int32_t K,
-                                                      int32_t cb) {
+                                                      int32_t cb, int32_t row16, int32_t stride16, int64_t plane16) {
     const int n_in = min(counts[0], K);  // the lists hold at most K entries
     for (int i = blockIdx.x; i < n_in; i += gridDim.x) {
         const int n = d_in[i], s = slot_in[i];
@@ -29,7 +36,6 @@ __global__ __launch_bounds__(kNT) void k_scatter_rows(int32_t* counts, const int
             continue;
         }
         const uint4* src = store + (size_t)n * cb;
-        uint4* dst = buf + (size_t)s * cb;
         for (int c = threadIdx.x; c < cb; c += kNT * kU) {
             uint4 v[kU];
 #pragma unroll
@@ -37,7 +43,7 @@ __global__ __launch_bounds__(kNT) void k_scatter_rows(int32_t* counts, const int
                 if (c + u * kNT < cb) v[u] = src[c + u * kNT];
 #pragma unroll
             for (int u = 0; u < kU; ++u)
-                if (c + u * kNT < cb) dst[c + u * kNT] = v[u];
+                if (c + u * kNT < cb) buf[slot_chunk(s, c + u * kNT, row16, stride16, plane16)] = v[u];
         }
     }
 }
@@ -59,7 +65,6 @@ __global__ __launch_bounds__(kNT) void k_scatter_all(ScatterLaunch a) {
             continue;
         }
         const auto* src = store + (size_t)n * cb;
-        auto* dst = buf + (size_t)s * cb;
         for (int c = threadIdx.x; c < cb; c += kNT * kU) {
             typedef uint32_t u4 __attribute__((ext_vector_type(4)));
             u4 v[kU];
@@ -68,7 +73,8 @@ __global__ __launch_bounds__(kNT) void k_scatter_all(ScatterLaunch a) {
                 if (c + u * kNT < cb) v[u] = reinterpret_cast<const NP_GLOBAL u4*>(src)[c + u * kNT];
 #pragma unroll
             for (int u = 0; u < kU; ++u)
-                if (c + u * kNT < cb) reinterpret_cast<NP_GLOBAL u4*>(dst)[c + u * kNT] = v[u];
+                if (c + u * kNT < cb)
+                    reinterpret_cast<NP_GLOBAL u4*>(buf)[slot_chunk(s, c + u * kNT, L->row16, L->stride16, L->plane16)] = v[u];
         }
     }
 }
@@ -89,17 +95,17 @@ __global__ __launch_bounds__(kNT) void k_move_all(ScatterLaunch a) {
             if (threadIdx.x == 0) atomicOr(&L->counts[3], kErrBadList);
             continue;
         }
-        const auto* src = buf + (size_t)sp * cb;
-        auto* dst = buf + (size_t)dp * cb;
         for (int c = threadIdx.x; c < cb; c += kNT * kU) {
             typedef uint32_t u4 __attribute__((ext_vector_type(4)));
             u4 v[kU];
 #pragma unroll
             for (int u = 0; u < kU; ++u)
-                if (c + u * kNT < cb) v[u] = reinterpret_cast<const NP_GLOBAL u4*>(src)[c + u * kNT];
+                if (c + u * kNT < cb)
+                    v[u] = reinterpret_cast<const NP_GLOBAL u4*>(buf)[slot_chunk(sp, c + u * kNT, L->row16, L->stride16, L->plane16)];
 #pragma unroll
             for (int u = 0; u < kU; ++u)
-                if (c + u * kNT < cb) reinterpret_cast<NP_GLOBAL u4*>(dst)[c + u * kNT] = v[u];
+                if (c + u * kNT < cb)
+                    reinterpret_cast<NP_GLOBAL u4*>(buf)[slot_chunk(dp, c + u * kNT, L->row16, L->stride16, L->plane16)] = v[u];
         }
     }
 }
@@ -110,7 +116,8 @@ __global__ __launch_bounds__(kNT) void k_move_all(ScatterLaunch a) {
 // interleaved in the slot, so the "deinterleave" is a plain bundle copy.
 __global__ __launch_bounds__(kNT) void k_scatter_staged(int32_t* counts, const int32_t* __restrict__ slot_in,
                                                         const uint4* __restrict__ stage, uint4* __restrict__ buf,
-                                                        int32_t cnt, int32_t K, int32_t cb) {
+                                                        int32_t cnt, int32_t K, int32_t cb, int32_t row16,
+                                                        int32_t stride16, int64_t plane16) {
     for (int i = blockIdx.x; i < cnt; i += gridDim.x) {
         const int s = slot_in[i];
         if ((unsigned)s >= (unsigned)K) {
@@ -118,7 +125,6 @@ __global__ __launch_bounds__(kNT) void k_scatter_staged(int32_t* counts, const i
             continue;
         }
         const uint4* src = stage + (size_t)i * cb;
-        uint4* dst = buf + (size_t)s * cb;
         for (int c = threadIdx.x; c < cb; c += kNT * kU) {
             uint4 v[kU];
 #pragma unroll
@@ -126,7 +132,7 @@ __global__ __launch_bounds__(kNT) void k_scatter_staged(int32_t* counts, const i
                 if (c + u * kNT < cb) v[u] = src[c + u * kNT];
 #pragma unroll
             for (int u = 0; u < kU; ++u)
-                if (c + u * kNT < cb) dst[c + u * kNT] = v[u];
+                if (c + u * kNT < cb) buf[slot_chunk(s, c + u * kNT, row16, stride16, plane16)] = v[u];
         }
     }
 }
@@ -159,10 +165,11 @@ __global__ __launch_bounds__(kNT) void k_probe_copy(uint4* __restrict__ dst, con
 
 hipError_t launch_scatter(int32_t* counts, const int32_t* d_in, const int32_t* slot_in,
                           const uint16_t* store, uint16_t* buf, int32_t M, int32_t K,
-                          int32_t bundle_elems, int grid, hipStream_t s) {
+                          int32_t bundle_elems, int32_t row16, int32_t stride16, int64_t plane16, int grid,
+                          hipStream_t s) {
     hipLaunchKernelGGL(k_scatter_rows, dim3(grid), dim3(kNT), 0, s, counts, d_in, slot_in,
                        reinterpret_cast<const uint4*>(store), reinterpret_cast<uint4*>(buf), M, K,
-                       bundle_elems / 8);
+                       bundle_elems / 8, row16, stride16, plane16);
     return hipGetLastError();
 }
 
@@ -177,10 +184,12 @@ hipError_t launch_move_all(const ScatterLaunch& a, int wgs_per_layer, hipStream_
 }
 
 hipError_t launch_scatter_staged(int32_t* counts, const int32_t* slot_in, const void* stage, uint16_t* buf,
-                                 int32_t cnt, int32_t K, int32_t bundle_elems, hipStream_t s) {
+                                 int32_t cnt, int32_t K, int32_t bundle_elems, int32_t row16, int32_t stride16,
+                                 int64_t plane16, hipStream_t s) {
     const int grid = std::max(1, std::min(cnt, 1024));
     hipLaunchKernelGGL(k_scatter_staged, dim3(grid), dim3(kNT), 0, s, counts, slot_in,
-                       reinterpret_cast<const uint4*>(stage), reinterpret_cast<uint4*>(buf), cnt, K, bundle_elems / 8);
+                       reinterpret_cast<const uint4*>(stage), reinterpret_cast<uint4*>(buf), cnt, K, bundle_elems / 8,
+                       row16, stride16, plane16);
     return hipGetLastError();
 }
 

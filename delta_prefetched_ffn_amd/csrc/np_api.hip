@@ -94,6 +94,7 @@ struct np_layer {
     uint64_t* levels = nullptr; // n_levels > 0: [n_levels][W] neurons per frequency level
     int n_levels = 0;
     int layout = NP_LAYOUT_SLOTS;
+    int planar = 0;             // 1: one buffer per projection row instead of one bundle per slot
     int reduce = NP_REDUCE_ATOMIC;  // how the FFN combines the partial sums of its workgroups
     LayerDev ldh{};             // host copy of *ldev
     uint64_t* hpair = nullptr;
@@ -289,6 +290,8 @@ np_status enqueue_ffn(np_layer* L, const float* x, float* y, hipStream_t s, cons
         a.n = L->n_active;
     }
     a.buf_bytes = (uint32_t)((size_t)L->desc.k_max * L->bundle_elems() * 2);
+    a.slot_stride = (uint32_t)L->ldh.stride16 * 16u;
+    a.row_plane = (uint32_t)((size_t)L->ldh.plane16 * 16u);
     a.d = L->desc.d_model;
     a.K = L->desc.k_max;
     a.R = L->desc.n_rows;
@@ -309,7 +312,8 @@ np_status enqueue_ffn(np_layer* L, const float* x, float* y, hipStream_t s, cons
 np_status enqueue_scatter(np_layer* L, hipStream_t s, bool fixed_grid = false) {
     const int grid = fixed_grid || L->n_in < 0 ? std::max(1, std::min(L->desc.k_max, 1024)) : scatter_grid(L->n_in);
     NP_HIP(launch_scatter(L->counts, L->d_in(), L->slot_in(), L->store_dev, L->buf, L->desc.d_ff,
-                          L->desc.k_max, (int32_t)L->bundle_elems(), grid, s));
+                          L->desc.k_max, (int32_t)L->bundle_elems(), L->ldh.row16, L->ldh.stride16, L->ldh.plane16,
+                          grid, s));
     return NP_OK;
 }
 
@@ -461,7 +465,7 @@ np_status enqueue_staged(np_layer* L, const std::vector<int32_t>& d_in, hipStrea
         st->pool->run(job);
         NP_HIP(hipMemcpyAsync(st->devb[h], st->host[h], (size_t)cnt * bb, hipMemcpyHostToDevice, s));
         NP_HIP(launch_scatter_staged(L->counts, L->slot_in() + first, st->devb[h], L->buf, cnt, L->desc.k_max,
-                                     (int32_t)L->bundle_elems(), s));
+                                     (int32_t)L->bundle_elems(), L->ldh.row16, L->ldh.stride16, L->ldh.plane16, s));
         NP_HIP(hipEventRecord(st->ready[h], s));
     }
     return NP_OK;
@@ -808,6 +812,9 @@ np_status np_layer_create(const np_layer_desc* desc, np_layer** out) {
     ld.store = L->store_dev;
     ld.buf = L->buf;
     ld.bundle16 = (int32_t)(L->bundle_elems() / 8);
+    ld.row16 = D.d_model / 8;
+    ld.stride16 = ld.bundle16;  // interleaved until np_layer_set_planar
+    ld.plane16 = ld.row16;
     L->ldh = ld;
     hipError_t e = hipMemcpy(L->ldev, &ld, sizeof ld, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy(L->d_masks, L->h_masks.data(), mask_words * 8, hipMemcpyHostToDevice);
@@ -1110,15 +1117,30 @@ np_status np_layer_read_rows(const np_layer* L, const int32_t* slots, int32_t n,
     const size_t bb = L->bundle_elems() * 2;
     if (!slots) {
         if (n != L->desc.k_max) return fail(NP_EINVAL, "slots == NULL requires n == k_max");
-        NP_HIP(hipMemcpy(dst, L->buf, (size_t)n * bb, hipMemcpyDeviceToHost));
+    } else {
+        for (int i = 0; i < n; ++i)
+            if (slots[i] < 0 || slots[i] >= L->desc.k_max)
+                return fail(NP_EINVAL, "slot %d out of range [0, %d)", slots[i], L->desc.k_max);
+    }
+    if (!L->planar) {
+        if (!slots) {
+            NP_HIP(hipMemcpy(dst, L->buf, (size_t)n * bb, hipMemcpyDeviceToHost));
+            return NP_OK;
+        }
+        for (int i = 0; i < n; ++i)
+            NP_HIP(hipMemcpy((char*)dst + (size_t)i * bb, (const char*)L->buf + (size_t)slots[i] * bb, bb,
+                             hipMemcpyDeviceToHost));
         return NP_OK;
     }
-    for (int i = 0; i < n; ++i)
-        if (slots[i] < 0 || slots[i] >= L->desc.k_max)
-            return fail(NP_EINVAL, "slot %d out of range [0, %d)", slots[i], L->desc.k_max);
-    for (int i = 0; i < n; ++i)
-        NP_HIP(hipMemcpy((char*)dst + (size_t)i * bb, (const char*)L->buf + (size_t)slots[i] * bb, bb,
-                         hipMemcpyDeviceToHost));
+    // planar buffers: copy them whole and reassemble the bundles
+    const size_t rb = (size_t)L->desc.d_model * 2, K = (size_t)L->desc.k_max;
+    std::vector<char> all(K * bb);
+    NP_HIP(hipMemcpy(all.data(), L->buf, K * bb, hipMemcpyDeviceToHost));
+    for (int i = 0; i < n; ++i) {
+        const size_t sl = slots ? (size_t)slots[i] : (size_t)i;
+        for (int r = 0; r < L->desc.n_rows; ++r)
+            std::memcpy((char*)dst + (size_t)i * bb + r * rb, all.data() + (r * K + sl) * rb, rb);
+    }
     return NP_OK;
 }
 
@@ -1285,6 +1307,24 @@ np_status np_decode_set_staging(int64_t bytes, int32_t threads) {
     g_stage_bytes = (size_t)bytes;
     const int hw = (int)std::thread::hardware_concurrency();
     g_stage_threads = threads ? threads : std::max(1, std::min(8, hw));
+    return NP_OK;
+}
+
+np_status np_layer_set_planar(np_layer* L, int32_t planar) {
+    if (!L) return fail(NP_EINVAL, "layer must not be NULL");
+    if (planar != 0 && planar != 1) return fail(NP_EINVAL, "planar=%d must be 0 or 1", planar);
+    if (L->state != kFresh) return fail(NP_ESTATE, "set the arrangement before the first np_delta_assign (or after np_layer_reset)");
+    DeviceGuard g(L->desc.device);
+    NP_HIP(hipDeviceSynchronize());
+    LayerDev ld = L->ldh;
+    ld.stride16 = planar ? ld.row16 : ld.bundle16;
+    ld.plane16 = planar ? (int64_t)L->desc.k_max * ld.row16 : ld.row16;
+    NP_HIP(hipMemcpy(L->ldev, &ld, sizeof ld, hipMemcpyHostToDevice));
+    // the buffer is zero-filled in a fresh layer: nothing to rearrange
+    L->ldh = ld;
+    L->planar = planar;
+    drop_plans_with(L);
+    ++L->version;
     return NP_OK;
 }
 

@@ -45,7 +45,13 @@ struct LayerDev {
     int32_t mode, n_tables, C, pad;
     const uint16_t* store;   // backing row store (device address; may be mapped host memory)
     uint16_t* buf;           // [K][R][d] slot buffer
-    int32_t bundle16;        // 16-byte chunks per bundle
+    int32_t bundle16;        // 16-byte chunks per bundle (as laid out in the row store)
+    // Slot buffer arrangement, in 16-byte chunks: row r of slot s starts at
+    // s * stride16 + r * plane16. Interleaved (one bundle per slot): stride16 = bundle16,
+    // plane16 = row16. Planar (one buffer per projection): stride16 = row16, plane16 = K * row16.
+    int32_t row16;           // 16-byte chunks per row (d_model / 8)
+    int32_t stride16;
+    int64_t plane16;
     int32_t window;          // residency window in tokens (1: the buffer holds exactly S)
     // Retention by frequency level (n_levels > 0, window 1): bit masks of the neurons of each
     // level, highest level first ([n_levels][W]).
@@ -124,6 +130,8 @@ struct FfnArgs {
     const DecodeParams* prm;  // if set: seq, x and y come from prm (layer `layer`), n from counts[2]
     int32_t layer;
     uint32_t buf_bytes;     // size of buf (below 4 GiB)
+    uint32_t slot_stride;   // bytes from one slot's row to the next slot's same row
+    uint32_t row_plane;     // bytes from a slot's row r to its row r + 1
     int32_t d, K, R, M;
     int32_t p1, q, tw, nwg;
     int32_t activation;     // 0 ReLU, 1 SiLU
@@ -145,11 +153,13 @@ hipError_t launch_delta_assign(const DeltaLaunch& a, hipStream_t s);
 hipError_t launch_set_params(const ParamsUpdate& p, DecodeParams* dst, hipStream_t s);
 hipError_t launch_scatter(int32_t* counts, const int32_t* d_in, const int32_t* slot_in,
                           const uint16_t* store, uint16_t* buf, int32_t M, int32_t K,
-                          int32_t bundle_elems, int grid, hipStream_t s);
+                          int32_t bundle_elems, int32_t row16, int32_t stride16, int64_t plane16, int grid,
+                          hipStream_t s);
 hipError_t launch_scatter_all(const ScatterLaunch& a, int wgs_per_layer, hipStream_t s);
 hipError_t launch_move_all(const ScatterLaunch& a, int wgs_per_layer, hipStream_t s);
 hipError_t launch_scatter_staged(int32_t* counts, const int32_t* slot_in, const void* stage, uint16_t* buf,
-                                 int32_t cnt, int32_t K, int32_t bundle_elems, hipStream_t s);
+                                 int32_t cnt, int32_t K, int32_t bundle_elems, int32_t row16, int32_t stride16,
+                                 int64_t plane16, hipStream_t s);
 hipError_t launch_sparse_ffn(const FfnArgs& a, const FfnShape& sh, bool gated, hipStream_t s);
 hipError_t launch_probe_read(const void* src, int64_t bytes, float* sink, hipStream_t s);
 hipError_t launch_probe_copy(void* dst, const void* src, int64_t bytes, hipStream_t s);

@@ -281,6 +281,17 @@ np_status np_layer_set_layout(np_layer* layer, int32_t layout);
  * device. */
 np_status np_layer_read_moves(const np_layer* layer, int32_t* src, int32_t* dst, int32_t* n_moves);
 
+/* Arrangement of the slot buffer (NeuroPrefetcher section 3.5 keeps the
+ * resident rows in planar per-projection buffers). planar = 0 (the
+ * default): one interleaved bundle [gate|up|down^T] per slot, buffer bf16
+ * [k_max][n_rows][d_model]. planar = 1: one buffer per row kind, bf16
+ * [n_rows][k_max][d_model], so slot s's row r is plane r, row s; the scatter
+ * kernels and the FFN's read-through then split each bundle into its
+ * planes. The same bytes are read by the FFN either way; np_layer_read_rows
+ * returns bundles in both. Only before the first np_delta_assign after
+ * create or reset (NP_ESTATE). Synchronizes the layer's device. */
+np_status np_layer_set_planar(np_layer* layer, int32_t planar);
+
 /* FFN launch shape of this layer: about slots_per_wg active slots per
  * workgroup for the gate/up phase (1..16; the default, -1, sizes the grid to
  * one workgroup per compute unit), tile_cols output

@@ -24,7 +24,7 @@ def _log(msg):
 
 
 def run_full(num: int, where: str = "device", steps: int | None = None, ffn_samples: int = 10, window: int = 1,
-             n_levels: int = 0, layout: str = "slots", staging: int = 0):
+             n_levels: int = 0, layout: str = "slots", staging: int = 0, planar: bool = False):
     from delta_prefetched_ffn_amd import binding as B
     torch = torch_mod()
     assert torch.cuda.is_available()
@@ -41,6 +41,8 @@ def run_full(num: int, where: str = "device", steps: int | None = None, ffn_samp
             layers[-1].set_levels(wl.frequency_levels(l, n_levels), n_levels)
         if layout != "slots":
             layers[-1].set_layout(layout)
+        if planar:
+            layers[-1].set_planar(True)
     _log(f"config {num}: {c.L} layers built ({where} store) in {time.time() - t0:.1f}s")
     orc = OracleRun(wl, keep_buffer=False, window=window, n_levels=n_levels, layout=layout)
     B.decode_set_staging(staging)
@@ -114,6 +116,12 @@ def test_full_config_frequency_levels(num, n_levels):
 def test_full_config_compact_layout(num, where):
     run_full(num, where, layout="compact", steps=None if where == "device" else 12,
              ffn_samples=10 if where == "device" else 4)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("num", [2, 8])
+def test_full_config_planar_buffers(num):
+    run_full(num, "device", planar=True)
 
 
 @pytest.mark.timeout(600)

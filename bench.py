@@ -48,6 +48,8 @@ def parse():
                    help="residency window in tokens (1: the buffer holds exactly the active set)")
     p.add_argument("--layout", choices=["slots", "compact"], default="slots",
                    help="resident buffer layout: slot map (default) or compacted prefix with row moves")
+    p.add_argument("--planar", action="store_true",
+                   help="slot buffer as one plane per projection row instead of one bundle per slot")
     p.add_argument("--levels", type=int, default=0,
                    help="retention by frequency level: number of levels (0: off; exclusive with --window)")
     p.add_argument("--steps", type=int, default=200)
@@ -195,6 +197,8 @@ def main():
                 L.set_levels(wl.frequency_levels(l, args.levels), args.levels)
             if args.layout != "slots":
                 L.set_layout(args.layout)
+            if args.planar:
+                L.set_planar(True)
             L.set_ffn_reduce(args.reduce)
             out.append(L)
         return out
@@ -380,7 +384,7 @@ def main():
                    "global_batch": 1, "layers": c.L, "d_model": c.d, "d_ff": c.M, "k_max": c.K,
                    "weights": "bf16", "backing_store": "HBM", "parallelism": "single GPU",
                    "residency_window": args.window, "frequency_levels": args.levels,
-                   "buffer_layout": args.layout,
+                   "buffer_layout": args.layout, "planar_buffers": args.planar,
                    "ffn_reduce": args.reduce},
         "effective_gbps": eff_gbps,
         "effective_frac_of_hbm_peak": eff_gbps / HBM_PEAK_GBPS,

@@ -390,22 +390,31 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
         }
     }
 
-    // Reduce the RL2 row lanes: s_red2[r2][c2 * 8 + e].
+    // Reduce the RL2 row lanes: column c of row lane r2 sits at s_red2[r2 * TW + swz(c)], where
+    // swz keeps c's group of 8 and rotates its position in the group by (c / 32) % 8. With the
+    // plain [c2 * 8 + e] the 32 lanes storing one e hit 4 banks (an 8-way conflict on every
+    // store); rotated, the lanes storing one e and the lanes reading 32 consecutive columns
+    // each hit 32 different banks. Thread c then sums column c (consecutive columns per wave,
+    // so the atomic adds below stay coalesced).
+    auto swz = [](int c) { return (c & ~7) + (((c & 7) + (c >> 5)) & 7); };
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s_red2[r2 * a.tw + (c2 << 3) + e] = acc[e];
+    for (int e = 0; e < 8; ++e) s_red2[r2 * a.tw + swz((c2 << 3) + e)] = acc[e];
     __syncthreads();
+    const int mycol = tid;
+    const bool colok = tid < tcols;
 
     const int ncontrib = (a.nwg - 1 - t) / a.q + 1;
     const bool reducer = !a.atomic_y && w == t + a.q * (ncontrib - 1);
     float own = 0.f;                          // this workgroup's partial of column tid (tid < tcols)
-    if (tid < tcols) {
-        for (int r = 0; r < RL2; ++r) own += s_red2[r * a.tw + tid];
+    if (colok) {
+        const int sc = swz(tid);
+        for (int r = 0; r < RL2; ++r) own += s_red2[r * a.tw + sc];
         if (a.atomic_y) {
             // Atomic reduction: every contributor adds its partial into y (cleared before the
             // launch or holding the value to add to). No exchange, no reducer; the order of
             // the additions, and so the last bits of y, may differ from run to run.
             float* yp = a.prm ? a.prm->y + (size_t)a.layer * a.d : a.y;
-            unsafeAtomicAdd(yp + col0 + tid, own);
+            unsafeAtomicAdd(yp + col0 + mycol, own);
         } else if (!reducer) {
             st_pair(&a.ppair[(size_t)w * a.tw + tid], seq, own);
         }
@@ -450,12 +459,12 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
         }
         s_red2[g * a.tw + j] = gs;
         __syncthreads();
-        if (tid < tcols) {
+        if (colok) {
             float yv = 0.f;
             for (int gg = 0; gg < G; ++gg) yv += s_red2[gg * a.tw + tid];
             auto* yg = gmem(a.prm ? a.prm->y + (size_t)a.layer * a.d : a.y);
-            const float y0 = a.accumulate ? yg[col0 + tid] : 0.f;
-            yg[col0 + tid] = a.accumulate ? y0 + (yv + own) : yv + own;
+            const float y0 = a.accumulate ? yg[col0 + mycol] : 0.f;
+            yg[col0 + mycol] = a.accumulate ? y0 + (yv + own) : yv + own;
         }
     }
     if (!a.prm && n_dev != n) err |= kErrCount;

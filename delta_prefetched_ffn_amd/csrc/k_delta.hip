@@ -374,25 +374,33 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
     };
     int c_rel = 0;
     {
+        // The 64 lanes of a wave look at the 64 slots of one word (slot = tid + k * kNT, and
+        // kNT is a multiple of 64), so each word's bits come from one ballot and one lane
+        // writes them: no LDS atomics on a word that 64 lanes share.
+        auto mark = [&](int sl, int f) {
+            const uint64_t b_act = __ballot(f == 2), b_rel = __ballot(f == 1);
+            if (lane == 0 && sl < K) {
+                s_Ab[sl >> 6] |= b_act;
+                s_F0[sl >> 6] |= b_rel;
+            }
+        };
         int fv[kOwnRegs];
 #pragma unroll
         for (int k = 0; k < kOwnRegs; ++k) fv[k] = fate(tid + k * kNT, own[k]);
 #pragma unroll
         for (int k = 0; k < kOwnRegs; ++k) {
-            const int sl = tid + k * kNT;
-            if (fv[k] == 2) atomicOr((unsigned long long*)&s_Ab[sl >> 6], 1ull << (sl & 63));
+            mark(tid + k * kNT, fv[k]);
             if (fv[k] != 1) continue;
             slot_map[own[k]] = -1;
-            atomicOr((unsigned long long*)&s_F0[sl >> 6], 1ull << (sl & 63));
             ++c_rel;
         }
-        for (int sl = tid + kOwnRegs * kNT; sl < K; sl += kNT) {
-            const int n = owner[sl];
+        for (int sl0 = kOwnRegs * kNT; sl0 < K; sl0 += kNT) {  // uniform trip count: ballots stay whole-wave
+            const int sl = sl0 + tid;
+            const int n = sl < K ? owner[sl] : -1;
             const int f = fate(sl, n);
-            if (f == 2) atomicOr((unsigned long long*)&s_Ab[sl >> 6], 1ull << (sl & 63));
+            mark(sl, f);
             if (f != 1) continue;
             slot_map[n] = -1;
-            atomicOr((unsigned long long*)&s_F0[sl >> 6], 1ull << (sl & 63));
             ++c_rel;
         }
     }

@@ -140,12 +140,14 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     const int RL = NT / CL;
     const int rl = tid / CL, cl = tid % CL;
 
-    // |S| comes from the host (it validated the capacity with it); the device count,
-    // read in parallel, is only checked against it.
-    const int n_dev = a.counts[2];
-    int n = (a.n < 0 || a.prm) ? n_dev : a.n;
+    // |S| comes from the host (it validated the capacity with it); the device count is only
+    // checked against it, at the very end, so that no address waits for that load. A replayed
+    // graph has no host count and reads the device one.
+    const bool host_n = a.n >= 0 && !a.prm;
+    int n = host_n ? a.n : gmem(a.counts)[2];
     n = n < 0 ? 0 : (n > a.K ? a.K : n);
-    auto cbeg = [&](int c) { return (int)(((long long)c * n) / a.p1); };
+    // c * n <= 4096 * 65536 < 2^31: 32-bit arithmetic
+    auto cbeg = [&](int c) { return (int)(((unsigned)c * (unsigned)n) / (unsigned)a.p1); };
 
     // Window of chunks handled in phase 2: [wlo, whi]; their slot positions [plo, phi).
     const int wlo = max(0, w - a.q + 1), whi = min(w, a.p1 - 1);
@@ -467,7 +469,8 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
             yg[col0 + mycol] = a.accumulate ? y0 + (yv + own) : yv + own;
         }
     }
-    if (!a.prm && n_dev != n) err |= kErrCount;
+    if (host_n && tid == 0 && __hip_atomic_load(&a.counts[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != n)
+        err |= kErrCount;
     if (err) atomicOr(&a.counts[3], err);
 }
 

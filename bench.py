@@ -116,11 +116,11 @@ def stored_traffic(ffn_bytes_per_launch: float, config: int):
     return rec.get("traffic_bytes_per_launch"), rec.get("note", "")
 
 
-def cpu_baseline(wl, stores, seconds: float, window: int = 1, n_levels: int = 0):
+def cpu_baseline(wl, stores, seconds: float, window: int = 1, n_levels: int = 0, threads: int = 0):
     """The CPU oracle, untouched, on a bounded sample of the same workload."""
     from oracle import oracle as O
     c = wl.cfg
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads = threads or max(1, min(16, os.cpu_count() or 1))
     layers = [O.OracleLayer(c.M, c.K, c.R, c.d, window=window,
                             levels=wl.frequency_levels(l, n_levels) if n_levels else None, n_levels=n_levels)
               for l in range(c.L)]
@@ -386,6 +386,10 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         cpu = cpu_baseline(wl, stores, args.cpu_seconds, args.window, args.levels)
+        one = cpu_baseline(wl, stores, max(2.0, args.cpu_seconds / 3), args.window, args.levels, threads=1)
+        cpu["single_thread"] = {"value": one["value"], "unit": "tokens/s", "cores": 1, "sample": one["sample"],
+                                "seconds": one["seconds"]}
+        log(f"cpu baseline, one thread: {one['value']:.3f} tok/s")
         log(f"cpu baseline: {cpu['value']:.3f} tok/s on {cpu['cores']} threads")
 
     out = {

@@ -153,7 +153,8 @@ def cpu_baseline(wl, stores, seconds: float, window: int = 1, n_levels: int = 0,
     eff = (act + din) * c.bundle_bytes
     return {"value": tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{tok} tokens of the same workload (tokens 1..{c.T - 1} in order, repeating; all "
-                      f"{c.L} layers; after an untimed cold start), fp64 oracle, layers in parallel threads",
+                      f"{c.L} layers; after an untimed cold start), fp64 oracle, "
+                      + ("layers in parallel threads" if threads > 1 else "layers one after another on one thread"),
             "effective_gbps": eff / dt / 1e9, "seconds": dt}
 
 

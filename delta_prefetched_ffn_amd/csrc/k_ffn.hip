@@ -40,6 +40,8 @@
 // fences and no counters, and a reader waits only for workgroups with lower
 // IDs, which the dispatcher starts first: every wait ends. A wait also gives
 // up after a fixed number of polls and reports an error bit instead of hanging.
+#include <type_traits>
+
 #include "np_internal.hpp"
 
 namespace np {
@@ -85,6 +87,32 @@ __device__ inline void axpy8(float* acc, const float h, const uint4 v) {
     acc[5] = fmaf(h, bf_hi(v.z), acc[5]);
     acc[6] = fmaf(h, bf_lo(v.w), acc[6]);
     acc[7] = fmaf(h, bf_hi(v.w), acc[7]);
+}
+
+// Cross-lane exchanges of one wave without the LDS crossbar. Lane pairing at offset OFF:
+// 32 and 16 by the gfx950 lane-swap instructions (v_permlane32_swap / v_permlane16_swap
+// move one operand's upper half of each 2*OFF-lane group into the other operand's lower
+// half), 8 by a rotation of each 16-lane row by 8, 4 by mirroring each 8-lane half-row
+// (lane i with 7 - i, which also pairs a lane that has bit 2 clear with one that has it set),
+// 2 and 1 by quad permutations.
+template <int OFF>
+__device__ inline float lane_partner(float x) {
+    static_assert(OFF == 8 || OFF == 4 || OFF == 2 || OFF == 1, "row-local offsets only");
+    constexpr int ctrl = OFF == 8 ? 0x128 : OFF == 4 ? 0x141 : OFF == 2 ? 0x4E : 0xB1;
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xF, 0xF, false));
+}
+// Transposing exchange: lanes with the OFF bit clear return x + x(partner), lanes with it
+// set return y + y(partner).
+template <int OFF>
+__device__ inline float lane_fold(float x, float y, int lane) {
+    if constexpr (OFF == 32 || OFF == 16) {
+        const auto r = OFF == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false)
+                                 : __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else {
+        const float sx = x + lane_partner<OFF>(x), sy = y + lane_partner<OFF>(y);
+        return (lane & OFF) ? sy : sx;
+    }
 }
 
 // Weight rows are read with unconditional 16-byte loads: a lane with nothing to load
@@ -263,32 +291,46 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
         if (CL >= 64) {
             // Transposing butterfly over the wave: each exchange halves the values a lane
             // holds (the lane with the offset bit set keeps the upper half), so V values need
-            // V - 1 + log2(64 / V) exchanges instead of 6 V. Afterwards lane L holds the wave
-            // sum of value vi(L), vi = the lane bits 5, 4, ... read as a binary number.
+            // V - 1 + log2(64 / V) exchanges instead of 6 V; the remaining offsets sum the one
+            // value left. Afterwards lane L holds the wave sum of value vi(L), vi = the lane
+            // bits 5, 4, ... read as a binary number.
+            static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "V must be a power of two <= 64");
+            auto stage = [&](auto off_c) {
+                constexpr int OFF = decltype(off_c)::value;
+                constexpr int M = V * OFF / 32;  // values held before this exchange (when > 1)
+                if constexpr (M > 1) {
 #pragma unroll
-            for (int st = 0; (V >> st) > 1; ++st) {
-                const int m = V >> st, off = 32 >> st;
-                const bool upper = (lane & off) != 0;
-#pragma unroll
-                for (int j = 0; j < m / 2; ++j) {
-                    const float send = upper ? v[j] : v[j + m / 2];
-                    const float keep = upper ? v[j + m / 2] : v[j];
-                    v[j] = keep + __shfl_xor(send, off, 64);
+                    for (int j = 0; j < M / 2; ++j) v[j] = lane_fold<OFF>(v[j], v[j + M / 2], lane);
+                } else {
+                    v[0] = lane_fold<OFF>(v[0], v[0], lane);
                 }
-            }
-#pragma unroll
-            for (int off = 32 / V; off > 0; off >>= 1) v[0] += __shfl_xor(v[0], off, 64);
+            };
+            stage(std::integral_constant<int, 32>{});
+            stage(std::integral_constant<int, 16>{});
+            stage(std::integral_constant<int, 8>{});
+            stage(std::integral_constant<int, 4>{});
+            stage(std::integral_constant<int, 2>{});
+            stage(std::integral_constant<int, 1>{});
             if ((lane & (64 / V - 1)) == 0) s_red1[wave * V + (lane / (64 / V))] = v[0];
             __syncthreads();
             // across the waves of each row lane: lane cl = i of the row lane finishes slot i
             if (cl < SB) {
                 const int pos = b0 + rl + RL * cl;
                 if (pos < c1) {
+                    // the CL / 64 wave sums of each row: all reads issued, then added in order
+                    float part[NR1][kWaves];
+#pragma unroll
+                    for (int r = 0; r < NR1; ++r)
+#pragma unroll
+                        for (int k = 0; k < kWaves; ++k)
+                            part[r][k] = k < CL / 64 ? s_red1[(rl * (CL / 64) + k) * V + cl * NR1 + r] : 0.f;
                     float g[NR1];
 #pragma unroll
                     for (int r = 0; r < NR1; ++r) {
                         float sm = 0.f;
-                        for (int k = 0; k < CL / 64; ++k) sm += s_red1[(rl * (CL / 64) + k) * V + cl * NR1 + r];
+#pragma unroll
+                        for (int k = 0; k < kWaves; ++k)
+                            if (k < CL / 64) sm += part[r][k];
                         g[r] = sm;
                     }
                     const float h = neuron_h(g[0], g[NR1 - 1], GATED, a.activation);
@@ -410,7 +452,15 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     float own = 0.f;                          // this workgroup's partial of column tid (tid < tcols)
     if (colok) {
         const int sc = swz(tid);
-        for (int r = 0; r < RL2; ++r) own += s_red2[r * a.tw + sc];
+        // groups of 8 reads issued together, added in row-lane order
+        for (int r0 = 0; r0 < RL2; r0 += 8) {
+            float pr[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pr[e] = r0 + e < RL2 ? s_red2[(r0 + e) * a.tw + sc] : 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (r0 + e < RL2) own += pr[e];
+        }
         if (a.atomic_y) {
             // Atomic reduction: every contributor adds its partial into y (cleared before the
             // launch or holding the value to add to). No exchange, no reducer; the order of

@@ -316,13 +316,38 @@ def main():
         f"(back-to-back), {avg_event_us:.2f} us (own events) -> {achieved:.0f} GB/s")
     traffic, traffic_note = stored_traffic(ffn_bytes_per_launch, args.config)
 
+    # ---------------- plain read of the same bytes per launch ----------------
+    # The streaming-read kernel on as many bytes as one FFN launch moves, launched back to back
+    # by the library's own loop over rotating buffers (1.5 GB in all, more than the last-level
+    # cache, so every launch reads HBM): what moving that many bytes costs in one launch, launch
+    # gap and ramp included, with no dependent load, no exchange and no reduction.
+    sink = torch.empty(65536, dtype=torch.float32, device="cuda")
+    sb_bytes = int(ffn_bytes_per_launch) // 16 * 16
+    n_sb = max(8, -(-1_500_000_000 // sb_bytes))
+    sb_bufs = [torch.empty(sb_bytes // 2, dtype=torch.int16, device="cuda") for _ in range(n_sb)]
+    sb_ptrs = [b.data_ptr() for b in sb_bufs]
+    B.probe_read_set(sb_ptrs, sb_bytes, 1, sink.data_ptr(), s.cuda_stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    B.probe_read_set(sb_ptrs, sb_bytes, 3, sink.data_ptr(), s.cuda_stream)
+    e1.record(s)
+    s.synchronize()
+    sb_us = e0.elapsed_time(e1) * 1e3 / (3 * n_sb)
+    del sb_bufs, sb_ptrs
+    stream_bound = {"bytes_per_launch": sb_bytes, "us_per_launch": sb_us,
+                    "gbps": sb_bytes / (sb_us * 1e-6) / 1e9,
+                    "frac_of_peak": sb_bytes / (sb_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                    "ffn_launch_over_plain_read": avg_burst_us / sb_us,
+                    "how": f"plain streaming read of the same bytes, {n_sb} rotating buffers, launched back to back "
+                           "by the library (np_probe_read_set)"}
+    log(f"plain read of {sb_bytes / 1e6:.2f} MB per launch: {sb_us:.2f} us/launch "
+        f"({stream_bound['gbps']:.0f} GB/s); the FFN launch takes {avg_burst_us / sb_us:.2f}x that")
+
     # ---------------- streaming-read probe (achievable HBM read bandwidth) ----------------
     probe_bytes = 4 << 30
     buf = torch.empty(probe_bytes // 2, dtype=torch.int16, device="cuda")
-    sink = torch.empty(65536, dtype=torch.float32, device="cuda")
     for _ in range(2):
         B.probe_read(buf.data_ptr(), probe_bytes, sink.data_ptr(), s.cuda_stream)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(s)
     for _ in range(5):
         B.probe_read(buf.data_ptr(), probe_bytes, sink.data_ptr(), s.cuda_stream)
@@ -428,7 +453,8 @@ def main():
                      "avg_launch_us": avg_burst_us, "avg_launch_us_own_events": avg_event_us,
                      "timing": f"HIP events on the launch stream around back-to-back launches of the {c.L} layers, "
                                "each right after its layer's delta assignment (read-through of the new bundles)",
-                     "traffic_note": traffic_note},
+                     "traffic_note": traffic_note,
+                     "plain_read_same_bytes": stream_bound},
         "hbm_read_probe_gbps": probe_gbps,
         "hbm_copy_probe_gbps": copy_gbps,
         "pcie_inclusive": pcie,

@@ -33,7 +33,7 @@ _NAMES = {0: "NP_OK", 1: "NP_EINVAL", 2: "NP_ECAPACITY", 3: "NP_ENOMEM", 4: "NP_
 EXPORTS = ["np_layer_create", "np_layer_destroy", "np_layer_reset", "np_delta_assign",
            "np_scatter_rows", "np_sparse_ffn", "np_decode_step", "np_layer_read_state",
            "np_layer_read_rows", "np_layer_info", "np_layer_counters", "np_layer_set_ffn_shape", "np_last_error",
-           "np_probe_read", "np_probe_copy", "np_decode_use_graphs", "np_layer_set_window",
+           "np_probe_read", "np_probe_read_set", "np_probe_copy", "np_decode_use_graphs", "np_layer_set_window",
            "np_sparse_ffn_acc", "np_layer_set_ffn_reduce", "np_layer_set_levels",
            "np_layer_set_layout", "np_layer_read_moves", "np_decode_set_staging",
            "np_layer_set_planar"]
@@ -73,6 +73,7 @@ def lib() -> ctypes.CDLL:
         "np_layer_counters": [vp, vp],
         "np_layer_set_ffn_shape": [vp, i32, i32, i32],
         "np_probe_read": [vp, i64, vp, vp],
+        "np_probe_read_set": [vp, i32, i64, i32, vp, vp],
         "np_probe_copy": [vp, vp, i64, vp],
         "np_decode_use_graphs": [i32],
         "np_layer_set_window": [vp, i32],
@@ -247,6 +248,11 @@ def decode_use_graphs(enable: bool) -> None:
 
 def probe_read(src_ptr: int, nbytes: int, sink_ptr: int, stream: int = 0) -> None:
     _check(lib().np_probe_read(src_ptr, nbytes, sink_ptr, stream or None))
+
+
+def probe_read_set(src_ptrs, nbytes: int, passes: int, sink_ptr: int, stream: int = 0) -> None:
+    arr = (ctypes.c_void_p * len(src_ptrs))(*src_ptrs)
+    _check(lib().np_probe_read_set(arr, len(src_ptrs), nbytes, passes, sink_ptr, stream or None))
 
 
 def probe_copy(dst_ptr: int, src_ptr: int, nbytes: int, stream: int = 0) -> None:

@@ -53,6 +53,22 @@ __device__ inline void block_excl_scan2(int va, int vb, int* ea, int* eb, int* t
     __syncthreads();  // s_tmp may be reused right away
 }
 
+// Sum of v over the 64 lanes of a wave, in every lane, without LDS: halves exchanged by the
+// gfx950 lane-swap instructions, then row rotation, half-row mirror and quad permutations.
+// The whole wave must be active. (Adding per-thread values into one LDS word with atomics
+// instead serialises one read-modify-write per thread.)
+__device__ inline int wave_sum_i(int v) {
+    const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    v = (int)r32[0] + (int)r32[1];
+    const auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = (int)r16[0] + (int)r16[1];
+    v += __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // lane ^ 8 within a row
+    v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // lane i <-> 7 - i
+    v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // lane ^ 2
+    v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // lane ^ 1
+    return v;
+}
+
 // w with its r lowest set bits removed (r >= popcount(w) gives 0): finds the r-th set bit
 // (0-based) by halving the word six times, then clears everything below it.
 __device__ inline uint64_t drop_low_bits(uint64_t w, int r) {
@@ -273,10 +289,15 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
                 covered |= A;
             }
         }
-        atomicAdd(&s_nS, c_s);
+        // per-wave sums, then one LDS add per wave
+        const int ws = wave_sum_i(c_s);
+        if (lane == 0) atomicAdd(&s_nS, ws);
 #pragma unroll
-        for (int j = 1; j <= kMaxClasses; ++j)
-            if (cnt[j]) atomicAdd(&s_cnt[j], cnt[j]);
+        for (int j = 1; j <= kMaxClasses; ++j) {
+            if (j > nj) break;  // nj is the same for the whole workgroup
+            const int wc = wave_sum_i(cnt[j]);
+            if (lane == 0 && wc) atomicAdd(&s_cnt[j], wc);
+        }
         __syncthreads();
         if (tid == 0) {
             int room = K - s_nS, js = kMaxClasses + 1, allow = 0;

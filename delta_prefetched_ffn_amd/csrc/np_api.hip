@@ -1217,6 +1217,17 @@ np_status np_probe_read(const void* src, int64_t bytes, float* sink, void* strea
     return NP_OK;
 }
 
+np_status np_probe_read_set(const void* const* srcs, int32_t n_srcs, int64_t bytes, int32_t passes, float* sink,
+                            void* stream) {
+    if (!srcs || !sink || n_srcs < 1 || n_srcs > 4096 || passes < 1 || passes > 1000 || bytes <= 0 || bytes % 16)
+        return fail(NP_EINVAL, "probe_read_set needs 1..4096 sources, 1..1000 passes, bytes > 0 and a multiple of 16");
+    for (int32_t i = 0; i < n_srcs; ++i)
+        if (!srcs[i] || !aligned16(srcs[i])) return fail(NP_EINVAL, "probe_read_set: source %d is NULL or misaligned", i);
+    for (int32_t p = 0; p < passes; ++p)
+        for (int32_t i = 0; i < n_srcs; ++i) NP_HIP(launch_probe_read(srcs[i], bytes, sink, (hipStream_t)stream));
+    return NP_OK;
+}
+
 np_status np_probe_copy(void* dst, const void* src, int64_t bytes, void* stream) {
     if (!src || !dst || bytes <= 0 || bytes % 16 || !aligned16(src) || !aligned16(dst))
         return fail(NP_EINVAL, "probe_copy needs 16-byte aligned pointers, bytes a multiple of 16");

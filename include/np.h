@@ -314,6 +314,15 @@ const char* np_last_error(void);
  * loads are not dead. */
 np_status np_probe_read(const void* src, int64_t bytes, float* sink, void* stream);
 
+/* The same streaming read over n_srcs buffers of `bytes` each (srcs: host array of device
+ * pointers, each 16-byte aligned), launched `passes` times over the whole set, back to back on
+ * `stream` from the library's own loop: the per-launch cost of a plain read of that many bytes
+ * without host launch overhead. Rotating over more bytes than the GPU's last-level cache keeps
+ * every launch a read from HBM. 1 <= n_srcs <= 4096, 1 <= passes <= 1000; all checks run
+ * before the first launch (NP_EINVAL). */
+np_status np_probe_read_set(const void* const* srcs, int32_t n_srcs, int64_t bytes, int32_t passes, float* sink,
+                            void* stream);
+
 /* Plain 128-bit copy kernel, bytes a multiple of 16, no overlap. */
 np_status np_probe_copy(void* dst, const void* src, int64_t bytes, void* stream);
 

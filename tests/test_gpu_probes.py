@@ -38,6 +38,27 @@ def test_read_probe_fills_its_sink(torch):
     assert written > 0 and (sink[:written] >= 0).all()
 
 
+def test_read_probe_set_reads_every_buffer(torch):
+    from delta_prefetched_ffn_amd import binding as B
+    n = 4 << 20
+    bufs = [torch.ones(n // 4, dtype=torch.int32, device="cuda") for _ in range(3)]
+    sink = torch.full((65536,), float("nan"), dtype=torch.float32, device="cuda")
+    B.probe_read_set([b.data_ptr() for b in bufs], n, 2, sink.data_ptr())
+    torch.cuda.synchronize()
+    written = torch.isfinite(sink).sum().item()
+    assert written > 0 and (sink[:written] >= 0).all()
+    with pytest.raises(B.NPError):
+        B.probe_read_set([], n, 1, sink.data_ptr())
+    with pytest.raises(B.NPError):
+        B.probe_read_set([bufs[0].data_ptr(), 0], n, 1, sink.data_ptr())
+    with pytest.raises(B.NPError):
+        B.probe_read_set([bufs[0].data_ptr() + 8], n, 1, sink.data_ptr())
+    with pytest.raises(B.NPError):
+        B.probe_read_set([bufs[0].data_ptr()], n + 8, 1, sink.data_ptr())
+    with pytest.raises(B.NPError):
+        B.probe_read_set([bufs[0].data_ptr()], n, 0, sink.data_ptr())
+
+
 def test_probe_arguments_are_checked(torch):
     from delta_prefetched_ffn_amd import binding as B
     buf = torch.zeros(1 << 12, dtype=torch.int32, device="cuda")

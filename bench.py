@@ -89,16 +89,25 @@ def token_ids(first: int, count: int, T: int) -> list[int]:
     return [1 + ((first - 1 + i) % (T - 1)) for i in range(count)]
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and with whitespace runs collapsed: what the compiler
+    sees, so that a comment edit does not count as a kernel change."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
-    """Hash of what the sparse-FFN kernel is built from: k_ffn.hip and the launch structs
-    (FfnShape, FfnArgs) of np_internal.hpp."""
+    """Hash of what the sparse-FFN kernel is built from: the code (comments aside) of k_ffn.hip
+    and of the launch structs (FfnShape, FfnArgs) of np_internal.hpp."""
     csrc = os.path.join(ROOT, "delta_prefetched_ffn_amd", "csrc")
     h = hashlib.sha256()
-    h.update(open(os.path.join(csrc, "k_ffn.hip"), "rb").read())
+    h.update(_code_only(open(os.path.join(csrc, "k_ffn.hip")).read()).encode())
     hdr = open(os.path.join(csrc, "np_internal.hpp")).read()
     i = hdr.index("struct FfnShape")
     j = hdr.index("};", hdr.index("struct FfnArgs")) + 2
-    h.update(hdr[i:j].encode())
+    h.update(_code_only(hdr[i:j]).encode())
     return h.hexdigest()[:16]
 
 

@@ -35,8 +35,9 @@
 //
 // Exchanges between workgroups carry their own validity: every h value and
 // every partial sum is stored as one 64-bit word (launch sequence number,
-// value) with an L2-coherent (agent-scope) store, and the reader re-reads a
-// word until its sequence number is this launch's. So there are no flags, no
+// value) with an agent-scope store, which writes through the XCD's own L2 so
+// that workgroups on the other XCDs see it, and the reader re-reads a word
+// with agent-scope loads until its sequence number is this launch's. So there are no flags, no
 // fences and no counters, and a reader waits only for workgroups with lower
 // IDs, which the dispatcher starts first: every wait ends. A wait also gives
 // up after a fixed number of polls and reports an error bit instead of hanging.

@@ -33,7 +33,7 @@ _NAMES = {0: "NP_OK", 1: "NP_EINVAL", 2: "NP_ECAPACITY", 3: "NP_ENOMEM", 4: "NP_
 EXPORTS = ["np_layer_create", "np_layer_destroy", "np_layer_reset", "np_delta_assign",
            "np_scatter_rows", "np_sparse_ffn", "np_decode_step", "np_layer_read_state",
            "np_layer_read_rows", "np_layer_info", "np_layer_counters", "np_layer_set_ffn_shape", "np_last_error",
-           "np_probe_read", "np_probe_read_set", "np_probe_copy", "np_decode_use_graphs", "np_layer_set_window",
+           "np_layer_raise_error", "np_probe_read", "np_probe_read_set", "np_probe_copy", "np_decode_use_graphs", "np_layer_set_window",
            "np_sparse_ffn_acc", "np_layer_set_ffn_reduce", "np_layer_set_levels",
            "np_layer_set_layout", "np_layer_read_moves", "np_decode_set_staging",
            "np_layer_set_planar"]
@@ -72,6 +72,7 @@ def lib() -> ctypes.CDLL:
         "np_layer_info": [vp, vp],
         "np_layer_counters": [vp, vp],
         "np_layer_set_ffn_shape": [vp, i32, i32, i32],
+        "np_layer_raise_error": [vp, i32, vp],
         "np_probe_read": [vp, i64, vp, vp],
         "np_probe_read_set": [vp, i32, i64, i32, vp, vp],
         "np_probe_copy": [vp, vp, i64, vp],
@@ -176,6 +177,10 @@ class Layer:
     def set_planar(self, planar: bool) -> None:
         """Slot buffer as one plane per row kind (True) or one bundle per slot (False, the default)."""
         _check(lib().np_layer_set_planar(self.h, 1 if planar else 0))
+
+    def raise_error(self, bits: int, stream: int = 0) -> None:
+        """Raise device error bits as a failing kernel would (tests of error reporting)."""
+        _check(lib().np_layer_raise_error(self.h, bits, stream or None))
 
     def read_moves(self) -> tuple[np.ndarray, np.ndarray]:
         """(src, dst) positions of the rows the last assignment moved (compact layout)."""

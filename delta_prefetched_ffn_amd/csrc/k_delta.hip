@@ -554,7 +554,7 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
         counts[1] = n_out;
         counts[2] = n_act;
         counts[4] = tok + 1;
-        if (s_err) atomicOr(&L.counts[3], s_err);
+        if (s_err) raise_err(L.counts, s_err);
         auto* acc = gmem(L.acc);
         acc[0] += (unsigned long long)n_act;
         acc[1] += (unsigned long long)n_in;

@@ -522,7 +522,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     }
     if (host_n && tid == 0 && __hip_atomic_load(&a.counts[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != n)
         err |= kErrCount;
-    if (err) atomicOr(&a.counts[3], err);
+    if (err) raise_err(a.counts, err);
 }
 
 template <int NT, int JX, bool G>

@@ -32,7 +32,7 @@ __global__ __launch_bounds__(kNT) void k_scatter_rows(int32_t* counts, const int
     for (int i = blockIdx.x; i < n_in; i += gridDim.x) {
         const int n = d_in[i], s = slot_in[i];
         if ((unsigned)n >= (unsigned)M || (unsigned)s >= (unsigned)K) {
-            if (threadIdx.x == 0) atomicOr(&counts[3], kErrBadList);
+            if (threadIdx.x == 0) raise_err(counts, kErrBadList);
             continue;
         }
         const uint4* src = store + (size_t)n * cb;
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kNT) void k_scatter_all(ScatterLaunch a) {
     for (int i = blockIdx.x; i < n_in; i += gridDim.x) {
         const int n = d_in[i], s = slot_in[i];
         if ((unsigned)n >= (unsigned)M || (unsigned)s >= (unsigned)K) {
-            if (threadIdx.x == 0) atomicOr(&L->counts[3], kErrBadList);
+            if (threadIdx.x == 0) raise_err(L->counts, kErrBadList);
             continue;
         }
         const auto* src = store + (size_t)n * cb;
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kNT) void k_move_all(ScatterLaunch a) {
     for (int i = blockIdx.x; i < n_mv; i += gridDim.x) {
         const int sp = src_l[i], dp = dst_l[i];
         if ((unsigned)sp >= (unsigned)K || (unsigned)dp >= (unsigned)K) {
-            if (threadIdx.x == 0) atomicOr(&L->counts[3], kErrBadList);
+            if (threadIdx.x == 0) raise_err(L->counts, kErrBadList);
             continue;
         }
         for (int c = threadIdx.x; c < cb; c += kNT * kU) {
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kNT) void k_scatter_staged(int32_t* counts, const i
     for (int i = blockIdx.x; i < cnt; i += gridDim.x) {
         const int s = slot_in[i];
         if ((unsigned)s >= (unsigned)K) {
-            if (threadIdx.x == 0) atomicOr(&counts[3], kErrBadList);
+            if (threadIdx.x == 0) raise_err(counts, kErrBadList);
             continue;
         }
         const uint4* src = stage + (size_t)i * cb;
@@ -171,7 +171,17 @@ __global__ __launch_bounds__(kNT) void k_probe_copy(uint4* __restrict__ dst, con
     for (int64_t i = (int64_t)blockIdx.x * kNT + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
 }
 
+// Raises error bits as a kernel that finds an inconsistency does (for tests of the reporting).
+__global__ void k_raise_err(int32_t* counts, int bits) {
+    if (threadIdx.x == 0) raise_err(counts, bits);
+}
+
 }  // namespace
+
+hipError_t launch_raise_err(int32_t* counts, int bits, hipStream_t s) {
+    hipLaunchKernelGGL(k_raise_err, dim3(1), dim3(64), 0, s, counts, bits);
+    return hipGetLastError();
+}
 
 hipError_t launch_scatter(int32_t* counts, const int32_t* d_in, const int32_t* slot_in,
                           const uint16_t* store, uint16_t* buf, int32_t M, int32_t K,

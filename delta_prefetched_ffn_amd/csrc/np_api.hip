@@ -62,7 +62,8 @@ struct DeviceGuard {
 };
 
 enum LayerState { kFresh = 0, kAssigned = 1, kScattered = 2 };
-constexpr size_t kCountsBytes = 8 * 4 + 2 * 8;  // int32 counts[8] + 2 x uint64 running sums
+constexpr size_t kCountsBytes = 8 * 4 + 2 * 8;  // int32 counts[8] + 2 x uint64 running sums (cleared by resets)
+constexpr size_t kCountsAlloc = kCountsBytes + 8;  // + the device address of the host error word
 constexpr int kLists = 7;                        // K-entry lists per layer
 
 constexpr int kDefaultSlotsPerWg = 0;  // 0: one workgroup per compute unit
@@ -88,7 +89,8 @@ struct np_layer {
     uint64_t* res = nullptr;
     uint64_t* freeb = nullptr;
     int32_t* lists = nullptr;  // d_in | slot_in | d_out | act | act_src | mv_src | mv_dst, K each
-    int32_t* counts = nullptr;  // int32 [8], then the two 64-bit running sums (LayerDev::acc)
+    int32_t* counts = nullptr;  // int32 [8], the two 64-bit running sums (LayerDev::acc), the error word's address
+    uint32_t* err_h = nullptr;  // pinned host word: error bits a kernel raised since the last reset
     uint64_t* ring = nullptr;   // window > 1: [window - 1][W] recent active sets
     int window = 1;
     uint64_t* levels = nullptr; // n_levels > 0: [n_levels][W] neurons per frequency level
@@ -197,6 +199,7 @@ void free_layer(np_layer* L) {
     for (void* p : ptrs)
         if (p) (void)hipFree(p);
     if (L->ev_scatter) (void)hipEventDestroy(L->ev_scatter);
+    if (L->err_h) (void)hipHostFree(L->err_h);
     delete L;
 }
 
@@ -214,6 +217,7 @@ np_status init_state(np_layer* L) {
     NP_HIP(hipMemset(L->counts, 0, kCountsBytes));
     if (L->ring) NP_HIP(hipMemset(L->ring, 0, (size_t)(L->window - 1) * L->W * 8));
     NP_HIP(hipDeviceSynchronize());
+    if (L->err_h) __atomic_store_n(L->err_h, 0u, __ATOMIC_RELEASE);  // no kernel of the layer is in flight
     std::fill(L->h_res.begin(), L->h_res.end(), 0ull);
     L->n_active = 0;
     L->n_in = 0;
@@ -318,6 +322,19 @@ np_status enqueue_scatter(np_layer* L, hipStream_t s, bool fixed_grid = false) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Error bits that a kernel of the layer raised since its last reset (read without synchronizing:
+// a kernel still running may add some later). Calls that enqueue work for the layer refuse it
+// with NP_EDEVICE while any are set.
+np_status check_device_err(const np_layer* L, int index = -1) {
+    const uint32_t bits = L->err_h ? __atomic_load_n(L->err_h, __ATOMIC_ACQUIRE) : 0u;
+    if (!bits) return NP_OK;
+    if (index >= 0)
+        return fail(NP_EDEVICE, "layer %d: a kernel reported error bits 0x%x (np_layer_read_state shows them all; "
+                    "np_layer_reset clears them)", index, bits);
+    return fail(NP_EDEVICE, "a kernel reported error bits 0x%x (np_layer_read_state shows them all; np_layer_reset "
+                "clears them)", bits);
+}
 
 // ---- staged delta I/O (NeuroPrefetcher section 3.5: the host reads the incoming rows, sorted
 // and with adjacent ones merged, into a bounded pinned staging buffer, the DMA engine copies it
@@ -769,7 +786,7 @@ np_status np_layer_create(const np_layer_desc* desc, np_layer** out) {
     bool ok = dmalloc((void**)&L->d_masks, mask_words * 8) && dmalloc((void**)&L->buf, buf_bytes) &&
               dmalloc((void**)&L->slot_map, (size_t)M * 4) && dmalloc((void**)&L->owner, (size_t)K * 4) &&
               dmalloc((void**)&L->res, (size_t)L->W * 8) && dmalloc((void**)&L->freeb, (size_t)L->Kw * 8) &&
-              dmalloc((void**)&L->lists, (size_t)kLists * K * 4) && dmalloc((void**)&L->counts, kCountsBytes) &&
+              dmalloc((void**)&L->lists, (size_t)kLists * K * 4) && dmalloc((void**)&L->counts, kCountsAlloc) &&
               dmalloc((void**)&L->hpair, (size_t)K * 8) &&
               dmalloc((void**)&L->ldev, sizeof(LayerDev));
     if (!ok) {
@@ -780,6 +797,23 @@ np_status np_layer_create(const np_layer_desc* desc, np_layer** out) {
     if (st != NP_OK) {
         free_layer(L);
         return st;
+    }
+    {
+        // the host error word: pinned, coherent, mapped; its device address follows the counts
+        void* dp = nullptr;
+        if (hipHostMalloc((void**)&L->err_h, sizeof(uint32_t),
+                          hipHostMallocMapped | hipHostMallocCoherent | hipHostMallocPortable) != hipSuccess ||
+            hipHostGetDevicePointer(&dp, L->err_h, 0) != hipSuccess || !dp) {
+            (void)hipGetLastError();
+            free_layer(L);
+            return fail(NP_ENOMEM, "cannot allocate the pinned error word");
+        }
+        *L->err_h = 0;
+        if (hipMemcpy(L->counts + kErrMirrorSlot, &dp, sizeof dp, hipMemcpyHostToDevice) != hipSuccess) {
+            (void)hipGetLastError();
+            free_layer(L);
+            return fail(NP_EHIP, "cannot record the error word's address");
+        }
     }
     LayerDev ld{};
     ld.masks = L->d_masks;
@@ -887,6 +921,8 @@ np_status np_layer_set_ffn_shape(np_layer* L, int32_t slots_per_wg, int32_t tile
 
 np_status np_delta_assign(np_layer* L, int32_t gate_cid, int32_t up_cid, void* stream) {
     if (!L) return fail(NP_EINVAL, "layer must not be NULL");
+    const np_status de = check_device_err(L);
+    if (de != NP_OK) return de;
     if (L->state == kAssigned)
         return fail(NP_ESTATE, "previous delta not scattered: call np_scatter_rows first");
     int32_t u;
@@ -926,6 +962,8 @@ np_status np_delta_assign(np_layer* L, int32_t gate_cid, int32_t up_cid, void* s
 np_status np_scatter_rows(np_layer* L, void* stream) {
     if (!L) return fail(NP_EINVAL, "layer must not be NULL");
     if (L->state != kAssigned) return fail(NP_ESTATE, "np_scatter_rows needs a preceding np_delta_assign");
+    const np_status de = check_device_err(L);
+    if (de != NP_OK) return de;
     DeviceGuard g(L->desc.device);
     np_status st = enqueue_scatter(L, (hipStream_t)stream);
     if (st != NP_OK) return st;
@@ -941,6 +979,8 @@ np_status sparse_ffn_call(np_layer* L, const float* x, float* y, void* stream, b
     const bool read_through = L->state == kAssigned;
     if (read_through && L->store_is_host)
         return fail(NP_ESTATE, "the row store is host memory: call np_scatter_rows before np_sparse_ffn");
+    const np_status de = check_device_err(L);
+    if (de != NP_OK) return de;
     DeviceGuard g(L->desc.device);
     np_status st = enqueue_ffn(L, x, y, (hipStream_t)stream, nullptr, 0, read_through, acc);
     if (st != NP_OK) return st;
@@ -989,6 +1029,8 @@ np_status np_decode_step(np_layer* const* layers, int32_t n_layers, const int32_
         for (int k = 0; k < l; ++k)
             if (layers[k] == L) return fail(NP_EINVAL, "layer %d appears twice", l);
         if (L->state == kAssigned) return fail(NP_ESTATE, "layer %d has an unscattered delta", l);
+        const np_status de = check_device_err(L, l);
+        if (de != NP_OK) return de;
         int32_t u;
         np_status st = check_cids(L, cids[2 * l], cids[2 * l + 1], &u);
         if (st != NP_OK) return fail(st, "layer %d: %s", l, g_err.c_str());
@@ -1207,6 +1249,14 @@ np_status np_layer_set_window(np_layer* L, int32_t window) {
     L->ldh = ld;
     NP_HIP(hipMemset(L->counts, 0, kCountsBytes));  // token count and running sums restart
     ++L->version;
+    return NP_OK;
+}
+
+np_status np_layer_raise_error(np_layer* L, int32_t bits, void* stream) {
+    if (!L) return fail(NP_EINVAL, "layer must not be NULL");
+    if (bits <= 0) return fail(NP_EINVAL, "bits=%d must be positive", bits);
+    DeviceGuard g(L->desc.device);
+    NP_HIP(launch_raise_err(L->counts, bits, (hipStream_t)stream));
     return NP_OK;
 }
 

@@ -26,6 +26,19 @@ constexpr int kErrWindow = 4;          // FFN: window larger than the LDS stagin
 constexpr int kErrSpin = 8;            // FFN: a wait hit its iteration limit
 constexpr int kErrCount = 16;          // FFN: host and device active counts differ
 
+// A layer's counts block: int32 [8] (counts[3] = error bits), 2 x uint64 running sums, then
+// (int32 index 12, 8-byte aligned, not cleared by resets) the device address of the layer's
+// pinned host error word. A kernel that raises error bits ORs them into counts[3] and stores
+// them into the host word with a system-scope store, so the host sees them at the layer's next
+// call without synchronizing (the host word may miss bits that two kernels raise at once;
+// counts[3] has them all).
+constexpr int kErrMirrorSlot = 12;
+__device__ inline void raise_err(int32_t* counts, int bits) {
+    atomicOr(&counts[3], bits);
+    uint32_t* const m = *reinterpret_cast<uint32_t* const*>(counts + kErrMirrorSlot);
+    if (m) __hip_atomic_store(m, (uint32_t)bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // Everything a kernel needs about one layer; lives in device memory.
 struct LayerDev {
     const uint64_t* masks;   // [n_tables][C][W]
@@ -151,6 +164,7 @@ __device__ inline NP_GLOBAL T* gmem(T* p) {
 // Launchers (return hipError_t from the launch).
 hipError_t launch_delta_assign(const DeltaLaunch& a, hipStream_t s);
 hipError_t launch_set_params(const ParamsUpdate& p, DecodeParams* dst, hipStream_t s);
+hipError_t launch_raise_err(int32_t* counts, int bits, hipStream_t s);
 hipError_t launch_scatter(int32_t* counts, const int32_t* d_in, const int32_t* slot_in,
                           const uint16_t* store, uint16_t* buf, int32_t M, int32_t K,
                           int32_t bundle_elems, int32_t row16, int32_t stride16, int64_t plane16, int grid,

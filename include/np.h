@@ -60,7 +60,7 @@ typedef enum {
     NP_ENOMEM = 3,     /* device or host allocation failed                       */
     NP_EHIP = 4,       /* a HIP runtime call failed (text in np_last_error)      */
     NP_ESTATE = 5,     /* call-order violation (see np_delta_assign)             */
-    NP_EDEVICE = 6     /* a kernel reported an inconsistency (np_layer_read_*)   */
+    NP_EDEVICE = 6     /* a kernel of the layer reported an inconsistency        */
 } np_status;
 
 /* How the two centroid masks combine into the active set (section 3.4 of the
@@ -306,6 +306,19 @@ np_status np_layer_set_ffn_shape(np_layer* layer, int32_t slots_per_wg, int32_t 
 
 /* Thread-local text of the calling thread's last error ("" if none). */
 const char* np_last_error(void);
+
+/* Device-side errors. A kernel that finds an inconsistency (a list entry out of range, no
+ * free slot, a wait that hit its iteration limit, host and device counts that differ) ORs
+ * error bits into the layer's device counts and stores them into a pinned host word of the
+ * layer, without stopping. From then on, every call that enqueues work for the layer
+ * (np_delta_assign, np_scatter_rows, np_sparse_ffn, np_sparse_ffn_acc, np_decode_step) fails
+ * with NP_EDEVICE before enqueuing anything, and np_layer_read_state returns the bits (with
+ * NP_EDEVICE); np_layer_reset clears them. The host word is read without synchronizing, so the
+ * report comes at the first such call after the kernel's store reached host memory.
+ *
+ * np_layer_raise_error makes the layer raise `bits` (> 0) through that same device path, as a
+ * kernel on `stream` would: for testing the reporting without a failing kernel. */
+np_status np_layer_raise_error(np_layer* layer, int32_t bits, void* stream);
 
 /* ---- measurement probes (roofline denominators and counter scaling) ---- */
 

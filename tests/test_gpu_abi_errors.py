@@ -158,3 +158,47 @@ def test_read_through_needs_a_device_store(env):
         compare_state(L.read_state(), ol, res, np.arange(64), "first")
         assert np.array_equal(L.read_rows(), ol.buf)
     hl.close()
+
+
+def test_device_errors_are_refused_until_reset(env):
+    """Error bits raised on the device (here by np_layer_raise_error, through the path a failing
+    kernel takes) make every later enqueueing call of the layer fail with NP_EDEVICE before it
+    enqueues anything; np_layer_read_state returns the bits; np_layer_reset clears them; another
+    layer is not affected."""
+    torch, B, layer, store, masks, dev = env
+    other = B.Layer(d_model=d, d_ff=M, k_max=K, n_rows=R, masks=masks, mask_mode=B.MASK_UNION,
+                    row_store=dev.data_ptr(), keepalive=dev)
+    s = torch.cuda.current_stream().cuda_stream
+    x = torch.ones(2, d, device="cuda")
+    y = torch.zeros(2, d, device="cuda")
+    layer.delta_assign(0, 0, s)
+    layer.sparse_ffn(x[0].data_ptr(), y[0].data_ptr(), s)
+    torch.cuda.synchronize()
+    assert layer.read_state()["err"] == 0
+    before = layer.read_state()
+    layer.raise_error(8, s)
+    torch.cuda.synchronize()
+    for call in (lambda: layer.delta_assign(1, 1, s),
+                 lambda: layer.sparse_ffn(x[0].data_ptr(), y[0].data_ptr(), s),
+                 lambda: B.decode_step([other, layer], np.array([[1, 1], [1, 1]], dtype=np.int32),
+                                       x.data_ptr(), y.data_ptr(), s, s)):
+        with pytest.raises(B.NPError) as e:
+            call()
+        assert e.value.status == B.NP_EDEVICE and "0x8" in str(e.value)
+    st = layer.read_state(check=False)
+    assert st["err"] == 8
+    for k in ("slot_map", "owner", "d_in", "slot_in", "d_out", "act"):
+        assert np.array_equal(st[k], before[k]), k           # nothing was enqueued
+    assert other.read_state()["err"] == 0 and other.info()["n_active"] == 0
+    with pytest.raises(B.NPError) as e:
+        layer.read_state()
+    assert e.value.status == B.NP_EDEVICE
+    with pytest.raises(B.NPError):
+        layer.raise_error(0, s)
+    layer.reset()
+    assert layer.read_state()["err"] == 0
+    layer.delta_assign(1, 1, s)
+    layer.sparse_ffn(x[0].data_ptr(), y[0].data_ptr(), s)
+    torch.cuda.synchronize()
+    assert layer.read_state()["err"] == 0
+    other.close()

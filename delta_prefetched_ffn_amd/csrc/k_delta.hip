@@ -14,7 +14,7 @@
 namespace np {
 namespace {
 
-constexpr int kNT = 256;
+constexpr int kNT = 512;
 constexpr int kWaves = kNT / 64;
 
 // Exclusive scans of two ints per thread over the workgroup in one pass; *ta and *tb get
@@ -92,7 +92,7 @@ __device__ inline uint64_t valid_bits(int v, int Kw, int K) {
     return (v == Kw - 1 && (K & 63)) ? ((1ull << (K & 63)) - 1) : ~0ull;
 }
 
-constexpr int kOwnRegs = 32;  // owner entries per thread loaded with the masks (K <= 8192 in one pass)
+constexpr int kOwnRegs = 16;  // owner entries per thread loaded with the masks (K <= 8192 in one pass)
 
 // Bits of the positions below lim in word v.
 __device__ inline uint64_t below(int v, int lim) {

@@ -435,15 +435,32 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
         }
     }
 
-    // Reduce the RL2 row lanes: column c of row lane r2 sits at s_red2[r2 * TW + swz(c)], where
-    // swz keeps c's group of 8 and rotates its position in the group by (c / 32) % 8. With the
-    // plain [c2 * 8 + e] the 32 lanes storing one e hit 4 banks (an 8-way conflict on every
+    // Reduce the RL2 row lanes: column c of wave k's partial sums sits at s_red2[k * TW + swz(c)],
+    // where swz keeps c's group of 8 and rotates its position in the group by (c / 32) % 8. With
+    // the plain [c2 * 8 + e] the 32 lanes storing one e hit 4 banks (an 8-way conflict on every
     // store); rotated, the lanes storing one e and the lanes reading 32 consecutive columns
     // each hit 32 different banks. Thread c then sums column c (consecutive columns per wave,
     // so the atomic adds below stay coalesced).
     auto swz = [](int c) { return (c & ~7) + (((c & 7) + (c >> 5)) & 7); };
+    // The 64 / CT row lanes of a wave hold the same columns (lanes l and l + CT): they are
+    // added inside the wave first (lane swaps over 32 and 16 lanes, a row rotation over 8),
+    // so one row per wave goes through LDS, written by the wave's first CT lanes.
+    if (CT <= 32) {  // uniform over the workgroup
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s_red2[r2 * a.tw + swz((c2 << 3) + e)] = acc[e];
+        for (int e = 0; e < 8; ++e) acc[e] = lane_fold<32>(acc[e], acc[e], lane);
+        if (CT <= 16) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = lane_fold<16>(acc[e], acc[e], lane);
+        }
+        if (CT <= 8) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = lane_fold<8>(acc[e], acc[e], lane);
+        }
+    }
+    if (lane < CT) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_red2[wave * a.tw + swz((c2 << 3) + e)] = acc[e];
+    }
     __syncthreads();
     const int mycol = tid;
     const bool colok = tid < tcols;
@@ -453,15 +470,12 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     float own = 0.f;                          // this workgroup's partial of column tid (tid < tcols)
     if (colok) {
         const int sc = swz(tid);
-        // groups of 8 reads issued together, added in row-lane order
-        for (int r0 = 0; r0 < RL2; r0 += 8) {
-            float pr[8];
+        // one row per wave, the reads issued together, added in wave order
+        float pr[kWaves];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pr[e] = r0 + e < RL2 ? s_red2[(r0 + e) * a.tw + sc] : 0.f;
+        for (int k = 0; k < kWaves; ++k) pr[k] = s_red2[k * a.tw + sc];
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (r0 + e < RL2) own += pr[e];
-        }
+        for (int k = 0; k < kWaves; ++k) own += pr[k];
         if (a.atomic_y) {
             // Atomic reduction: every contributor adds its partial into y (cleared before the
             // launch or holding the value to add to). No exchange, no reducer; the order of

@@ -358,6 +358,10 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
         }
     };
     if (has1) load_batch(c0);
+    // Every wave issues its gate/up loads before any wave issues down loads: each SIMD issues
+    // its oldest wave's loads back to back, so without this barrier the down rows of the first
+    // waves queue ahead of the gate/up rows of the last ones and h waits for the whole stream.
+    __syncthreads();
 
     // ---------------- phase 2 loads: first batch of the down tile (overlaps phase 1) -------------
     const int t = w % a.q;

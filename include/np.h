@@ -26,7 +26,10 @@
  *     enqueued nothing and changed no state; np_last_error() returns a
  *     thread-local description of the last failure of the calling thread.
  *   - All argument, range, capacity and call-order checks run on the host,
- *     synchronously, before anything is enqueued.
+ *     synchronously, before anything is enqueued. What only a kernel can
+ *     detect is reported asynchronously: after a kernel of a layer raised
+ *     error bits, the layer's enqueueing calls fail with NP_EDEVICE (see
+ *     "Device-side errors" below).
  *   - "stream" arguments are hipStream_t handles passed as void*; NULL means
  *     the device's null stream. Compute calls are asynchronous on their
  *     stream; np_layer_read_* calls synchronize the layer's device.
@@ -160,9 +163,11 @@ np_status np_layer_set_ffn_reduce(np_layer* layer, int32_t mode);
  * (sections 3.1, 3.4, 3.5): validates every layer's cids on the host (a
  * failure leaves every layer unchanged), then enqueues the token. When every
  * row store is device memory, or copy_stream equals compute_stream, all work
- * goes to compute_stream: one launch assigns the deltas of all layers, one
- * launch copies the new bundles of all layers, then the FFNs run in layer
- * order. When some row store is pinned host memory and the streams differ,
+ * goes to compute_stream: one launch assigns the deltas of all layers, then
+ * the FFNs run in layer order, each reading its new bundles through from a
+ * device-memory row store (as np_sparse_ffn right after np_delta_assign);
+ * bundles from pinned host stores are copied by one launch for all those
+ * layers before the FFNs. When some row store is pinned host memory and the streams differ,
  * layer l's scatter runs on copy_stream after the assignment and layer l's
  * FFN on compute_stream waits only for it, so the host-link transfers of
  * later layers overlap earlier FFNs; copy_stream is joined back into

@@ -8,6 +8,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
+#include <utility>
 #include <atomic>
 #include <map>
 #include <memory>
@@ -326,6 +328,24 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // Error bits that a kernel of the layer raised since its last reset (read without synchronizing:
 // a kernel still running may add some later). Calls that enqueue work for the layer refuse it
 // with NP_EDEVICE while any are set.
+// x and y must be memory the layer's device can read and write: its own device memory or pinned
+// host memory mapped for it. A pageable host pointer (or another device's memory) would fault the
+// GPU instead of failing here.
+np_status check_io_ptr(const void* p, int dev, const char* what) {
+    hipPointerAttribute_t attr;
+    std::memset(&attr, 0, sizeof attr);
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(NP_EINVAL, "%s is neither device memory nor pinned host memory", what);
+    }
+    if (attr.type == hipMemoryTypeDevice) {
+        if (attr.device != dev) return fail(NP_EINVAL, "%s lives on device %d, the layer on device %d", what, attr.device, dev);
+        return NP_OK;
+    }
+    if (attr.type == hipMemoryTypeHost && attr.devicePointer) return NP_OK;
+    return fail(NP_EINVAL, "%s (memory type %d) is not device memory or mapped pinned host memory", what, (int)attr.type);
+}
+
 np_status check_device_err(const np_layer* L, int index = -1) {
     const uint32_t bits = L->err_h ? __atomic_load_n(L->err_h, __ATOMIC_ACQUIRE) : 0u;
     if (!bits) return NP_OK;
@@ -976,6 +996,10 @@ np_status sparse_ffn_call(np_layer* L, const float* x, float* y, void* stream, b
     if (!L) return fail(NP_EINVAL, "layer must not be NULL");
     if (!x || !y || !aligned16(x) || !aligned16(y)) return fail(NP_EINVAL, "x and y must be 16-byte aligned device pointers");
     if (L->state == kFresh) return fail(NP_ESTATE, "np_sparse_ffn needs a preceding np_delta_assign");
+    for (const auto& io : {std::make_pair((const void*)x, "x"), std::make_pair((const void*)y, "y")}) {
+        const np_status pe = check_io_ptr(io.first, L->desc.device, io.second);
+        if (pe != NP_OK) return pe;
+    }
     const bool read_through = L->state == kAssigned;
     if (read_through && L->store_is_host)
         return fail(NP_ESTATE, "the row store is host memory: call np_scatter_rows before np_sparse_ffn");
@@ -1014,6 +1038,10 @@ np_status np_decode_step(np_layer* const* layers, int32_t n_layers, const int32_
     const np_layer* L0 = layers[0];
     if (!L0) return fail(NP_EINVAL, "layer 0 is NULL");
     const int dev = L0->desc.device, d = L0->desc.d_model;
+    for (const auto& io : {std::make_pair((const void*)x, "x"), std::make_pair((const void*)y, "y")}) {
+        const np_status pe = check_io_ptr(io.first, dev, io.second);
+        if (pe != NP_OK) return pe;
+    }
     std::vector<std::vector<uint64_t>> S(n_layers);
     std::vector<int> n_act(n_layers), n_in(n_layers), u_eff(n_layers);
     std::unique_lock<std::mutex> stage_lk(g_stage_mu);  // staging settings and buffers

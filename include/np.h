@@ -133,7 +133,9 @@ np_status np_scatter_rows(np_layer* layer, void* stream);
 /* Step 5: y[d_model] = sum over the resident (= active) slots of
  * down * act(gate . x) * (up . x), bf16 weights, fp32 arithmetic and
  * accumulation; the cross-workgroup reduction is set by np_layer_set_ffn_reduce.
- * x and y are device fp32 [d_model], 16-byte aligned, not overlapping. The
+ * x and y are fp32 [d_model], 16-byte aligned, not overlapping, in memory the layer's device
+ * can access (its device memory, or mapped pinned host memory; anything else is NP_EINVAL
+ * before any launch, as for np_decode_step's x and y). The
  * result is run-to-run identical with NP_REDUCE_ORDERED (np_layer_set_ffn_reduce).
  * Called right after np_delta_assign (no np_scatter_rows) with a row store in
  * device memory, it does step 4 itself: the bundles of the slots filled by

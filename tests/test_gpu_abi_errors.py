@@ -202,3 +202,32 @@ def test_device_errors_are_refused_until_reset(env):
     torch.cuda.synchronize()
     assert layer.read_state()["err"] == 0
     other.close()
+
+
+def test_io_pointers_must_be_gpu_accessible(env):
+    """x and y must be device memory of the layer's device or mapped pinned host memory: a
+    pageable host pointer is refused on the host (NP_EINVAL) instead of faulting the GPU."""
+    torch, B, layer, store, masks, dev = env
+    s = torch.cuda.current_stream().cuda_stream
+    layer.delta_assign(0, 0, s)
+    layer.scatter_rows(s)
+    raw = np.zeros(d + 64, dtype=np.float32)
+    off = (-raw.ctypes.data % 64) // 4
+    pageable = raw[off:off + d]
+    assert pageable.ctypes.data % 16 == 0
+    x = torch.ones(d, device="cuda")
+    y = torch.zeros(d, device="cuda")
+    for xp, yp, name in ((pageable.ctypes.data, y.data_ptr(), "x"), (x.data_ptr(), pageable.ctypes.data, "y")):
+        with pytest.raises(B.NPError) as e:
+            layer.sparse_ffn(xp, yp, s)
+        assert e.value.status == B.NP_EINVAL and str(e.value).split(": ", 1)[1].startswith(name)
+    with pytest.raises(B.NPError) as e:
+        B.decode_step([layer], np.array([[1, 1]], dtype=np.int32), pageable.ctypes.data, y.data_ptr(), s, s)
+    assert e.value.status == B.NP_EINVAL
+    assert layer.info()["n_active"] > 0 and layer.read_state()["err"] == 0   # nothing was enqueued
+    xh = torch.ones(d, dtype=torch.float32, pin_memory=True)               # mapped pinned host memory
+    layer.sparse_ffn(xh.data_ptr(), y.data_ptr(), s)
+    ref = y.clone()
+    layer.sparse_ffn(x.data_ptr(), y.data_ptr(), s)
+    torch.cuda.synchronize()
+    assert torch.equal(ref, y) or torch.allclose(ref, y, rtol=0, atol=1e-6)

@@ -1288,9 +1288,22 @@ np_status np_layer_raise_error(np_layer* L, int32_t bits, void* stream) {
     return NP_OK;
 }
 
+// The probes run on the current device: their pointers must be memory it can access.
+static np_status check_probe_ptrs(std::initializer_list<std::pair<const void*, const char*>> ptrs) {
+    int dev = 0;
+    NP_HIP(hipGetDevice(&dev));
+    for (const auto& p : ptrs) {
+        const np_status st = check_io_ptr(p.first, dev, p.second);
+        if (st != NP_OK) return st;
+    }
+    return NP_OK;
+}
+
 np_status np_probe_read(const void* src, int64_t bytes, float* sink, void* stream) {
     if (!src || !sink || bytes <= 0 || bytes % 16 || !aligned16(src))
         return fail(NP_EINVAL, "probe_read needs 16-byte aligned src, bytes > 0 and a multiple of 16");
+    const np_status pc = check_probe_ptrs({{src, "src"}, {sink, "sink"}});
+    if (pc != NP_OK) return pc;
     NP_HIP(launch_probe_read(src, bytes, sink, (hipStream_t)stream));
     return NP_OK;
 }
@@ -1299,8 +1312,13 @@ np_status np_probe_read_set(const void* const* srcs, int32_t n_srcs, int64_t byt
                             void* stream) {
     if (!srcs || !sink || n_srcs < 1 || n_srcs > 4096 || passes < 1 || passes > 1000 || bytes <= 0 || bytes % 16)
         return fail(NP_EINVAL, "probe_read_set needs 1..4096 sources, 1..1000 passes, bytes > 0 and a multiple of 16");
-    for (int32_t i = 0; i < n_srcs; ++i)
+    for (int32_t i = 0; i < n_srcs; ++i) {
         if (!srcs[i] || !aligned16(srcs[i])) return fail(NP_EINVAL, "probe_read_set: source %d is NULL or misaligned", i);
+        const np_status pc = check_probe_ptrs({{srcs[i], "a source"}});
+        if (pc != NP_OK) return pc;
+    }
+    const np_status pc = check_probe_ptrs({{sink, "sink"}});
+    if (pc != NP_OK) return pc;
     for (int32_t p = 0; p < passes; ++p)
         for (int32_t i = 0; i < n_srcs; ++i) NP_HIP(launch_probe_read(srcs[i], bytes, sink, (hipStream_t)stream));
     return NP_OK;
@@ -1309,6 +1327,8 @@ np_status np_probe_read_set(const void* const* srcs, int32_t n_srcs, int64_t byt
 np_status np_probe_copy(void* dst, const void* src, int64_t bytes, void* stream) {
     if (!src || !dst || bytes <= 0 || bytes % 16 || !aligned16(src) || !aligned16(dst))
         return fail(NP_EINVAL, "probe_copy needs 16-byte aligned pointers, bytes a multiple of 16");
+    const np_status pc = check_probe_ptrs({{src, "src"}, {dst, "dst"}});
+    if (pc != NP_OK) return pc;
     NP_HIP(launch_probe_copy(dst, src, bytes, (hipStream_t)stream));
     return NP_OK;
 }

@@ -96,3 +96,20 @@ def test_counters_and_info_match_the_oracle(torch):
         layer.reset()
         assert tuple(layer.counters()) == (0, 0)
         layer.close()
+
+
+def test_probe_pointers_must_be_gpu_accessible(torch):
+    """A pageable host pointer given to a probe is refused on the host, before any launch."""
+    from delta_prefetched_ffn_amd import binding as B
+    raw = np.zeros((1 << 16) + 64, dtype=np.uint8)
+    host = raw.ctypes.data + (-raw.ctypes.data % 64)
+    dev = torch.zeros(1 << 14, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(65536, dtype=torch.float32, device="cuda")
+    for call in (lambda: B.probe_read(host, 1 << 16, sink.data_ptr()),
+                 lambda: B.probe_read(dev.data_ptr(), 1 << 16, host),
+                 lambda: B.probe_read_set([dev.data_ptr(), host], 1 << 16, 1, sink.data_ptr()),
+                 lambda: B.probe_copy(dev.data_ptr(), host, 1 << 16),
+                 lambda: B.probe_copy(host, dev.data_ptr(), 1 << 16)):
+        with pytest.raises(B.NPError) as e:
+            call()
+        assert e.value.status == B.NP_EINVAL

@@ -73,7 +73,7 @@ __device__ inline int wave_sum_i(int v) {
 // (0-based) by halving the word six times, then clears everything below it.
 __device__ inline uint64_t drop_low_bits(uint64_t w, int r) {
     if (r <= 0) return w;
-    if (r >= __popcll(w)) return 0;
+    if (r >= (int)__popcll(w)) return 0;
     int pos = 0;
     uint64_t x = w;
 #pragma unroll
@@ -282,11 +282,12 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
             uint64_t covered = 0;
             c_s += __popcll(s_S[w]);
 #pragma unroll
-            for (int j = 1; j <= kMaxClasses; ++j) {
-                if (j > nj) break;
-                const uint64_t A = ring_word(j, w);
-                cnt[j] += __popcll(A & base & ~covered);
-                covered |= A;
+            for (int j = 1; j <= kMaxClasses; ++j) {  // guarded, not left with a break: it unrolls,
+                if (j <= nj) {                        // so cnt[] stays in registers
+                    const uint64_t A = ring_word(j, w);
+                    cnt[j] += __popcll(A & base & ~covered);
+                    covered |= A;
+                }
             }
         }
         // per-wave sums, then one LDS add per wave
@@ -294,9 +295,10 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
         if (lane == 0) atomicAdd(&s_nS, ws);
 #pragma unroll
         for (int j = 1; j <= kMaxClasses; ++j) {
-            if (j > nj) break;  // nj is the same for the whole workgroup
-            const int wc = wave_sum_i(cnt[j]);
-            if (lane == 0 && wc) atomicAdd(&s_cnt[j], wc);
+            if (j <= nj) {  // nj is the same for the whole workgroup
+                const int wc = wave_sum_i(cnt[j]);
+                if (lane == 0 && wc) atomicAdd(&s_cnt[j], wc);
+            }
         }
         __syncthreads();
         if (tid == 0) {

@@ -1,17 +1,23 @@
 """Benchmark: sparse-FFN decode at batch 1 on the Llama-2-7B-shaped workload.
 
-One step = one decode token through all 31 sparse layers (np_decode_step):
-active-set decode, set difference and slot assignment for all layers in one
-launch, then the fused sparse FFN of each layer in layer order, each reading
-its new bundles from the row store and writing them into their slots
-(read-through scatter). Inputs (centroid IDs, x, the backing row store) are
-resident in HBM before the timed region; the PCIe-inclusive rate with the
-row store in pinned host memory (per-layer scatter over the host link on a
-copy stream) is reported beside it under "pcie_inclusive".
+One step = one decode token through all 31 sparse layers (np_decode_step), with
+the row stores in pinned host memory as the workload specifies: one launch
+decodes the active sets, diffs them against the resident rows and assigns
+slots for all layers; then, per layer, a scatter kernel on a copy stream pulls
+the token's new [gate|up|down^T] bundles over the host link into their slots,
+and the layer's fused sparse FFN runs on the compute stream as soon as its
+scatter is done, so later layers' transfers overlap earlier layers' FFNs.
+Centroid IDs and x are resident in HBM before the timed region; the deltas
+cross the host link inside it. `value` is that decode rate.
+
+Beside it: the FFN kernel's own time per launch (the roofline: HBM bytes per
+launch over launch time, against the 8 TB/s peak and a plain read of the same
+bytes), the scatter kernel's rate against the host link's measured ceilings,
+the same decode with the row stores moved into HBM ("hbm_store": the FFN then
+reads the new bundles through and no scatter runs), and the CPU oracle.
 
 --config N runs another built-in workload the same way (6-8: the paper's
-Mistral-7B shape with SwiGLU and intersected masks); the default, 2, is the
-headline workload.
+Mistral-7B shape with SwiGLU and intersected masks).
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -42,8 +48,9 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--config", type=int, default=DEFAULT_WORKLOAD, help="built-in workload number")
-    p.add_argument("--reduce", choices=["atomic", "ordered"], default="atomic",
-                   help="FFN partial-sum reduction: fp32 atomics (default) or fixed order (bit-reproducible)")
+    p.add_argument("--reduce", choices=["atomic", "ordered"], default="ordered",
+                   help="FFN partial-sum reduction: fixed order without atomics (default, bit-reproducible) "
+                        "or fp32 atomics")
     p.add_argument("--window", type=int, default=1,
                    help="residency window in tokens (1: the buffer holds exactly the active set)")
     p.add_argument("--layout", choices=["slots", "compact"], default="slots",
@@ -58,11 +65,12 @@ def parse():
                    help="tokens in each of the two per-kernel FFN timing passes")
     p.add_argument("--graphs", action="store_true",
                    help="replay each decode step as a captured HIP graph instead of launching one by one")
-    p.add_argument("--pcie-steps", type=int, default=40, help="timed tokens with the store in pinned host memory")
-    p.add_argument("--no-pcie", action="store_true")
+    p.add_argument("--pcie-steps", type=int, default=40, help="timed tokens of the staged delta I/O leg")
+    p.add_argument("--hbm-steps", type=int, default=200, help="timed tokens with the row stores moved into HBM")
+    p.add_argument("--no-hbm-store", action="store_true", help="skip the leg with the row stores in HBM")
     p.add_argument("--staging-mb", type=float, default=0.0,
                    help="also time the staged delta I/O (host gather + DMA copy + device scatter) with this "
-                        "much pinned staging per buffer (two buffers), reported as pcie_staged")
+                        "much pinned staging per buffer (two buffers), reported as staged_delta_io")
     p.add_argument("--staging-threads", type=int, default=0, help="host gather threads (0: library default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle sample")
@@ -118,10 +126,10 @@ def stored_traffic(ffn_bytes_per_launch: float, config: int):
     if not os.path.exists(path):
         return None, "no counter summary"
     rec = json.load(open(path))
-    if rec.get("kernel_hash") != kernel_source_hash():
-        return None, "kernel changed since the counters were taken"
     if rec.get("config") != config:
         return None, f"counters taken on workload {rec.get('config')}, not this one"
+    if rec.get("kernel_hash") != kernel_source_hash():
+        return None, "kernel changed since the counters were taken"
     return rec.get("traffic_bytes_per_launch"), rec.get("note", "")
 
 
@@ -160,11 +168,32 @@ def cpu_baseline(wl, stores, seconds: float, window: int = 1, n_levels: int = 0,
                 break
         dt = time.perf_counter() - t0
     eff = (act + din) * c.bundle_bytes
-    return {"value": tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": tok / dt, "unit": "tokens/s", "cores": threads, "host_cpu_count": os.cpu_count(),
+            "threads_note": "threads = min(16, os.cpu_count()): the oracle's thread pool, capped at the "
+                            "GPU box's CPU share", "kind": "oracle",
             "sample": f"{tok} tokens of the same workload (tokens 1..{c.T - 1} in order, repeating; all "
                       f"{c.L} layers; after an untimed cold start), fp64 oracle, "
                       + ("layers in parallel threads" if threads > 1 else "layers one after another on one thread"),
             "effective_gbps": eff / dt / 1e9, "seconds": dt}
+
+
+def pinned_store(t, reuse: dict):
+    """t (a CPU tensor) copied into pinned host memory, or an earlier pinned store when the
+    host's pinned-memory limit is reached (reuse["distinct"] records how many could be pinned)."""
+    import torch
+    if reuse["distinct"] is None:
+        try:
+            p = torch.empty(t.numel(), dtype=torch.int16, pin_memory=True)
+            p.copy_(t)
+            reuse["pinned"].append(p)
+            return p
+        except (RuntimeError, torch.AcceleratorError) as e:  # the pinned-memory limit
+            if not reuse["pinned"]:
+                raise
+            reuse["distinct"] = len(reuse["pinned"])
+            log(f"pinning stopped after {len(reuse['pinned'])} row stores ({e.__class__.__name__}): "
+                "later layers reuse them (same transfer sizes, other weight values)")
+    return reuse["pinned"][reuse["n"] % len(reuse["pinned"])]
 
 
 def main():
@@ -190,30 +219,17 @@ def main():
     cids = wl.cids()
     x = torch.from_numpy(x_all).cuda()
     y = torch.zeros_like(x)
-
-    pinned_reuse = {"distinct": None}
+    reuse = {"distinct": None, "pinned": [], "n": 0}
 
     def make_layers(where: str):
         out = []
-        pinned = []
         for l in range(c.L):
             t = torch.from_numpy(stores[l].reshape(-1).view(np.int16))
             if where == "device":
                 dev = t.to("cuda")
-            elif pinned_reuse["distinct"] is None:
-                try:
-                    dev = torch.empty(t.numel(), dtype=torch.int16, pin_memory=True)
-                    dev.copy_(t)
-                    pinned.append(dev)
-                except (RuntimeError, torch.AcceleratorError) as e:  # the pinned-memory limit
-                    if not pinned:
-                        raise
-                    pinned_reuse["distinct"] = len(pinned)
-                    log(f"pinning stopped after {len(pinned)} row stores ({e.__class__.__name__}): "
-                        "later layers reuse them (same transfer sizes, other weight values)")
-                    dev = pinned[l % len(pinned)]
             else:
-                dev = pinned[l % len(pinned)]
+                reuse["n"] = l
+                dev = pinned_store(t, reuse)
             L = B.Layer(d_model=c.d, d_ff=c.M, k_max=c.K, n_rows=c.R, masks=wl.masks(l),
                         mask_mode=B.MODES[c.mode], act=B.ACTS[c.act], row_store=dev.data_ptr(), keepalive=dev)
             if args.slots_per_wg or args.tile_cols:
@@ -236,107 +252,191 @@ def main():
         for t in toks:
             B.decode_step(layers, cids[t], x[t].data_ptr(), y[t].data_ptr(), cs.cuda_stream, ps.cuda_stream)
 
-    # ---------------- main timed run: backing store in HBM ----------------
-    layers = make_layers("device")
-    torch.cuda.synchronize()
-    log(f"layers ready in {time.time() - t0:.1f}s")
-    tc = time.perf_counter()
-    run_tokens(layers, [0])                                   # cold start: whole active sets
-    torch.cuda.synchronize()
-    cold_ms = (time.perf_counter() - tc) * 1e3
-    run_tokens(layers, token_ids(1, args.warmup, c.T))
-    torch.cuda.synchronize()
-    before = np.array([L.counters() for L in layers], dtype=np.int64).sum(axis=0)
-    toks = token_ids(1 + args.warmup, args.steps, c.T)
-    torch.cuda.synchronize()
-    ts = time.perf_counter()
-    run_tokens(layers, toks)
-    enqueued = time.perf_counter() - ts
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - ts
-    after = np.array([L.counters() for L in layers], dtype=np.int64).sum(axis=0)
-    act_bundles, in_bundles = (after - before).tolist()
-    ms_per_step = elapsed * 1e3 / args.steps
-    tok_s = args.steps / elapsed
-    eff_bytes = (act_bundles + in_bundles) * c.bundle_bytes
-    eff_gbps = eff_bytes / elapsed / 1e9
-    log(f"decode: {ms_per_step:.3f} ms/token, {tok_s:.1f} tok/s, effective {eff_gbps:.1f} GB/s "
-        f"(host enqueue {enqueued * 1e3 / args.steps:.3f} ms/token)")
+    def decode_leg(layers, steps, warmup):
+        """Cold start (timed on its own), warm-up, then `steps` timed tokens."""
+        torch.cuda.synchronize()
+        tc = time.perf_counter()
+        run_tokens(layers, [0])                               # cold start: whole active sets
+        torch.cuda.synchronize()
+        cold = (time.perf_counter() - tc) * 1e3
+        run_tokens(layers, token_ids(1, warmup, c.T))
+        torch.cuda.synchronize()
+        before = np.array([L.counters() for L in layers], dtype=np.int64).sum(axis=0)
+        toks = token_ids(1 + warmup, steps, c.T)
+        torch.cuda.synchronize()
+        ts = time.perf_counter()
+        run_tokens(layers, toks)
+        enq = time.perf_counter() - ts
+        torch.cuda.synchronize()
+        el = time.perf_counter() - ts
+        after = np.array([L.counters() for L in layers], dtype=np.int64).sum(axis=0)
+        act_b, in_b = (after - before).tolist()
+        return {"tokens_per_s": steps / el, "ms_per_step": el * 1e3 / steps, "cold_start_ms": cold,
+                "host_enqueue_ms_per_step": enq * 1e3 / steps,
+                "effective_gbps": (act_b + in_b) * c.bundle_bytes / el / 1e9,
+                "delta_gbps": in_b * c.bundle_bytes / el / 1e9,
+                "mean_active_per_layer": act_b / (steps * c.L), "mean_delta_per_layer": in_b / (steps * c.L),
+                "steps": steps, "warmup": warmup, "next_token": 1 + warmup + steps}
+
+    def ffn_timing(layers, first_tok, n_tok, scatter: bool):
+        """The FFN launches of one token back to back between two HIP events on their stream, after
+        the token's assignments (and, for host-memory stores, its scatters) are done; on odd
+        tokens each launch between its own events. scatter=False: each FFN reads its new bundles
+        through from the (device) row store, as in a decode step with HBM stores. Algorithmic
+        bytes of a launch: active bundles read (+ new bundles written when reading through) +
+        x + y. Also times the scatter launches of the same tokens back to back."""
+        s = cs
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(c.L)]
+        burst = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        sc_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        acc = dict(burst_ms=0.0, event_ms=0.0, bytes=0, act_bytes=0, n=0, ev_n=0, sc_ms=0.0, sc_bytes=0, sc_n=0)
+        for i, t in enumerate(token_ids(first_tok, 2 * n_tok, c.T)):
+            ns = []
+            for l, L in enumerate(layers):
+                g, u = (int(v) for v in cids[t, l])
+                L.delta_assign(g, u, s.cuda_stream)
+                info = L.info()
+                ns.append((info["n_active"], info["n_in"]))
+            if scatter:
+                sc_ev[0].record(s)
+                for L in layers:
+                    L.scatter_rows(s.cuda_stream)
+                sc_ev[1].record(s)
+            s.synchronize()
+            if scatter:
+                acc["sc_ms"] += sc_ev[0].elapsed_time(sc_ev[1])
+                acc["sc_bytes"] += sum(ni for _, ni in ns) * c.bundle_bytes
+                acc["sc_n"] += c.L
+            if i % 2 == 0:
+                burst[0].record(s)
+                for l, L in enumerate(layers):
+                    L.sparse_ffn(x[t, l].data_ptr(), y[t, l].data_ptr(), s.cuda_stream)
+                burst[1].record(s)
+                s.synchronize()
+                acc["burst_ms"] += burst[0].elapsed_time(burst[1])
+                acc["bytes"] += sum((na + (0 if scatter else ni)) * c.bundle_bytes + 2 * c.d * 4 for na, ni in ns)
+                acc["act_bytes"] += sum(na * c.bundle_bytes for na, _ in ns)
+                acc["n"] += c.L
+            else:
+                for l, L in enumerate(layers):
+                    ev[l][0].record(s)
+                    L.sparse_ffn(x[t, l].data_ptr(), y[t, l].data_ptr(), s.cuda_stream)
+                    ev[l][1].record(s)
+                s.synchronize()
+                acc["event_ms"] += sum(a.elapsed_time(b) for a, b in ev)
+                acc["ev_n"] += c.L
+        us = acc["burst_ms"] * 1e3 / acc["n"]
+        bpl = acc["bytes"] / acc["n"]
+        apl = acc["act_bytes"] / acc["n"]
+        out = {"bytes_per_launch": bpl, "active_row_bytes_per_launch": apl, "avg_launch_us": us,
+               "avg_launch_us_own_events": acc["event_ms"] * 1e3 / max(acc["ev_n"], 1),
+               "achieved_gbps": bpl / (us * 1e-6) / 1e9, "active_row_gbps": apl / (us * 1e-6) / 1e9,
+               "launches": acc["n"]}
+        if scatter:
+            out["scatter"] = {"us_per_layer": acc["sc_ms"] * 1e3 / acc["sc_n"],
+                              "bytes_per_layer": acc["sc_bytes"] / acc["sc_n"],
+                              "gbps": acc["sc_bytes"] / (acc["sc_ms"] * 1e-3) / 1e9,
+                              "timing": f"HIP events around the {c.L} layers' scatter launches of a token, back to back"}
+        return out
+
+    # ---------------- the workload as specified: row stores in pinned host memory ----------------
+    # Per token: one assignment launch for all layers, then per layer a scatter on the copy
+    # stream that pulls the new bundles over the host link, and the layer's FFN on the compute
+    # stream once its scatter is done, so later layers' transfers overlap earlier FFNs.
+    hl = make_layers("host")
+    log(f"pinned-host layers ready in {time.time() - t0:.1f}s")
+    dec = decode_leg(hl, args.steps, args.warmup)
+    log(f"decode (pinned-host stores): {dec['ms_per_step']:.3f} ms/token, {dec['tokens_per_s']:.1f} tok/s, "
+        f"deltas {dec['delta_gbps']:.1f} GB/s over the host link")
     moves = None
     if args.layout == "compact":  # rows moved inside the buffer (read + written in HBM), untimed pass
-        mv_toks = token_ids(1 + args.warmup + args.steps, 16, c.T)
+        mv_toks = token_ids(dec["next_token"], 16, c.T)
         n_mv = 0
         for t in mv_toks:
-            run_tokens(layers, [t])
-            n_mv += sum(L.read_moves()[0].size for L in layers)
+            run_tokens(hl, [t])
+            n_mv += sum(L.read_moves()[0].size for L in hl)
         moves = {"mean_moves_per_layer": n_mv / (len(mv_toks) * c.L),
-                 "moved_bytes_per_token": 2 * n_mv / len(mv_toks) * c.bundle_bytes,
-                 "tokens": len(mv_toks)}
+                 "moved_bytes_per_token": 2 * n_mv / len(mv_toks) * c.bundle_bytes, "tokens": len(mv_toks)}
         log(f"compact layout: {moves['mean_moves_per_layer']:.1f} rows moved per layer")
+    torch.cuda.synchronize()
+    ffn = ffn_timing(hl, dec["next_token"] + 16, args.ffn_steps, scatter=True)
+    log(f"k_sparse_ffn (rows resident): {ffn['bytes_per_launch'] / 1e6:.2f} MB/launch, {ffn['avg_launch_us']:.2f} "
+        f"us/launch (back-to-back), {ffn['avg_launch_us_own_events']:.2f} us (own events) -> "
+        f"{ffn['achieved_gbps']:.0f} GB/s; scatter {ffn['scatter']['us_per_layer']:.1f} us/layer, "
+        f"{ffn['scatter']['gbps']:.1f} GB/s")
+    staged = None
+    if args.staging_mb > 0:
+        B.decode_set_staging(int(args.staging_mb * (1 << 20)), args.staging_threads)
+        for L in hl:
+            L.reset()
+        staged = decode_leg(hl, args.pcie_steps, 4)
+        B.decode_set_staging(0)
+        staged["staging_bytes"] = int(args.staging_mb * (1 << 20))
+        staged["gather_threads"] = args.staging_threads or "library default (min(8, cores))"
+        log(f"staged delta I/O: {staged['tokens_per_s']:.1f} tok/s, deltas {staged['delta_gbps']:.1f} GB/s")
+    for L in hl:
+        L.close()
+    del hl
 
-    # ---------------- FFN kernel timing (roofline of the dominant kernel) ----------------
-    # As in the decode step, each FFN follows its layer's delta assignment directly and reads
-    # the new bundles through from the row store (writing them into their slots). Even tokens:
-    # all 31 launches back to back between two events; odd tokens: each launch between its own
-    # events. y is cleared before the launches (a decode step clears it inside its assign
-    # launch) and each launch adds into it, as in a decode step. Algorithmic bytes of a launch:
-    # active bundles read + new bundles written + x + y.
-    ffn_toks = token_ids(1 + args.warmup + args.steps, 2 * args.ffn_steps, c.T)
+    # ---------------- host-link ceilings ----------------
+    # Pull: the streaming-read kernel reading pinned host memory (what the scatter kernel does);
+    # DMA: the copy engine moving pinned host memory to the device (hipMemcpyAsync).
+    sink = torch.empty(65536, dtype=torch.float32, device="cuda")
     s = cs
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(c.L)]
-    burst = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    burst_ms, event_ms, burst_bytes, burst_act_bytes, burst_n, event_n = 0.0, 0.0, 0, 0, 0, 0
-    for i, t in enumerate(ffn_toks):
-        ns = []
-        for l, L in enumerate(layers):
-            g, u = (int(v) for v in cids[t, l])
-            L.delta_assign(g, u, s.cuda_stream)
-            info = L.info()
-            ns.append((info["n_active"], info["n_in"]))
-        if i % 2 == 0:
-            with torch.cuda.stream(s):
-                y[t].zero_()  # as a decode step's assign launch does, outside the timed launches
-            burst[0].record(s)
-            for l, L in enumerate(layers):
-                L.sparse_ffn_acc(x[t, l].data_ptr(), y[t, l].data_ptr(), s.cuda_stream)
-            burst[1].record(s)
-            s.synchronize()
-            burst_ms += burst[0].elapsed_time(burst[1])
-            burst_bytes += sum((na + ni) * c.bundle_bytes + 2 * c.d * 4 for na, ni in ns)
-            burst_act_bytes += sum(na * c.bundle_bytes for na, _ in ns)
-            burst_n += c.L
-        else:
-            with torch.cuda.stream(s):
-                y[t].zero_()
-            for l, L in enumerate(layers):
-                ev[l][0].record(s)
-                L.sparse_ffn_acc(x[t, l].data_ptr(), y[t, l].data_ptr(), s.cuda_stream)
-                ev[l][1].record(s)
-            s.synchronize()
-            event_ms += sum(a.elapsed_time(b) for a, b in ev)
-            event_n += c.L
-    ffn_bytes_per_launch = burst_bytes / burst_n
-    act_bytes_per_launch = burst_act_bytes / burst_n
-    avg_burst_us = burst_ms * 1e3 / burst_n
-    avg_event_us = event_ms * 1e3 / max(event_n, 1)
-    achieved = ffn_bytes_per_launch / (avg_burst_us * 1e-6) / 1e9
-    log(f"k_sparse_ffn (read-through): {ffn_bytes_per_launch / 1e6:.2f} MB/launch "
-        f"({act_bytes_per_launch / 1e6:.2f} MB active rows), {avg_burst_us:.2f} us/launch "
-        f"(back-to-back), {avg_event_us:.2f} us (own events) -> {achieved:.0f} GB/s")
-    traffic, traffic_note = stored_traffic(ffn_bytes_per_launch, args.config)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    link_bytes = 1 << 30
+    hb = reuse["pinned"][0] if reuse["pinned"] else None
+    if hb is None or hb.numel() * 2 < link_bytes:
+        hb = torch.empty(link_bytes // 2, dtype=torch.int16, pin_memory=True)
+    B.probe_read(hb.data_ptr(), link_bytes, sink.data_ptr(), s.cuda_stream)
+    e0.record(s)
+    for _ in range(3):
+        B.probe_read(hb.data_ptr(), link_bytes, sink.data_ptr(), s.cuda_stream)
+    e1.record(s)
+    s.synchronize()
+    pull_gbps = 3 * link_bytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    db = torch.empty(link_bytes // 2, dtype=torch.int16, device="cuda")
+    with torch.cuda.stream(s):
+        db.copy_(hb[: link_bytes // 2], non_blocking=True)
+        e0.record(s)
+        for _ in range(3):
+            db.copy_(hb[: link_bytes // 2], non_blocking=True)
+        e1.record(s)
+    s.synchronize()
+    dma_gbps = 3 * link_bytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del db, hb
+    reuse["pinned"].clear()
+    log(f"host link: pull {pull_gbps:.1f} GB/s, DMA {dma_gbps:.1f} GB/s")
+
+    # ---------------- the same decode with the row stores moved into HBM ----------------
+    # Not the specified workload (no host-link transfer): each FFN reads its new bundles from the
+    # store in HBM and writes them into their slots (read-through), so no scatter runs.
+    hbm = None
+    if not args.no_hbm_store:
+        dl = make_layers("device")
+        hdec = decode_leg(dl, args.hbm_steps, args.warmup)
+        hffn = ffn_timing(dl, hdec["next_token"], args.ffn_steps, scatter=False)
+        for L in dl:
+            L.close()
+        del dl
+        torch.cuda.empty_cache()
+        hbm = {**{k: v for k, v in hdec.items() if k != "next_token"},
+               "ffn_read_through": {**hffn, "frac_of_peak": hffn["achieved_gbps"] / HBM_PEAK_GBPS,
+                                    "kernel": "k_sparse_ffn (read-through instantiation)"},
+               "store": "HBM (device memory), new bundles read through by the FFN"}
+        log(f"decode (HBM stores): {hdec['tokens_per_s']:.1f} tok/s; read-through FFN {hffn['avg_launch_us']:.2f} "
+            f"us/launch, {hffn['achieved_gbps']:.0f} GB/s")
 
     # ---------------- plain read of the same bytes per launch ----------------
-    # The streaming-read kernel on as many bytes as one FFN launch moves, launched back to back
+    # The streaming-read kernel on as many bytes as one FFN launch reads, launched back to back
     # by the library's own loop over rotating buffers (1.5 GB in all, more than the last-level
     # cache, so every launch reads HBM): what moving that many bytes costs in one launch, launch
     # gap and ramp included, with no dependent load, no exchange and no reduction.
-    sink = torch.empty(65536, dtype=torch.float32, device="cuda")
-    sb_bytes = int(ffn_bytes_per_launch) // 16 * 16
+    sb_bytes = int(ffn["bytes_per_launch"]) // 16 * 16
     n_sb = max(8, -(-1_500_000_000 // sb_bytes))
     sb_bufs = [torch.empty(sb_bytes // 2, dtype=torch.int16, device="cuda") for _ in range(n_sb)]
     sb_ptrs = [b.data_ptr() for b in sb_bufs]
     B.probe_read_set(sb_ptrs, sb_bytes, 1, sink.data_ptr(), s.cuda_stream)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(s)
     B.probe_read_set(sb_ptrs, sb_bytes, 3, sink.data_ptr(), s.cuda_stream)
     e1.record(s)
@@ -346,13 +446,13 @@ def main():
     stream_bound = {"bytes_per_launch": sb_bytes, "us_per_launch": sb_us,
                     "gbps": sb_bytes / (sb_us * 1e-6) / 1e9,
                     "frac_of_peak": sb_bytes / (sb_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
-                    "ffn_launch_over_plain_read": avg_burst_us / sb_us,
+                    "ffn_launch_over_plain_read": ffn["avg_launch_us"] / sb_us,
                     "how": f"plain streaming read of the same bytes, {n_sb} rotating buffers, launched back to back "
                            "by the library (np_probe_read_set)"}
     log(f"plain read of {sb_bytes / 1e6:.2f} MB per launch: {sb_us:.2f} us/launch "
-        f"({stream_bound['gbps']:.0f} GB/s); the FFN launch takes {avg_burst_us / sb_us:.2f}x that")
+        f"({stream_bound['gbps']:.0f} GB/s); the FFN launch takes {ffn['avg_launch_us'] / sb_us:.2f}x that")
 
-    # ---------------- streaming-read probe (achievable HBM read bandwidth) ----------------
+    # ---------------- streaming-read and copy probes (HBM) ----------------
     probe_bytes = 4 << 30
     buf = torch.empty(probe_bytes // 2, dtype=torch.int16, device="cuda")
     for _ in range(2):
@@ -373,49 +473,9 @@ def main():
     e1.record(s)
     s.synchronize()
     copy_gbps = 3 * 2 * copy_bytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    log(f"copy probe: {copy_gbps:.0f} GB/s (read + write)")
     del buf, cdst
-    log(f"streaming-read probe: {probe_gbps:.0f} GB/s")
-    for L in layers:
-        L.close()
-    del layers
-    torch.cuda.empty_cache()
-
-    # ---------------- PCIe-inclusive: backing store in pinned host memory ----------------
-    def host_leg():
-        hl = make_layers("host")
-        run_tokens(hl, [0])
-        run_tokens(hl, token_ids(1, 4, c.T))
-        torch.cuda.synchronize()
-        b0 = np.array([L.counters() for L in hl], dtype=np.int64).sum(axis=0)
-        toks = token_ids(5, args.pcie_steps, c.T)
-        ts = time.perf_counter()
-        run_tokens(hl, toks)
-        torch.cuda.synchronize()
-        el = time.perf_counter() - ts
-        b1 = np.array([L.counters() for L in hl], dtype=np.int64).sum(axis=0)
-        d_act, d_in = (b1 - b0).tolist()
-        for L in hl:
-            L.close()
-        store = "pinned host memory (hipHostMalloc via torch)"
-        if pinned_reuse["distinct"]:
-            store += (f"; only {pinned_reuse['distinct']} of {c.L} row stores could be pinned, the other layers "
-                      "reuse them (the host-link traffic is the same, the weights differ)")
-        return {"tokens_per_s": args.pcie_steps / el, "ms_per_step": el * 1e3 / args.pcie_steps,
-                "delta_gbps_over_host_link": d_in * c.bundle_bytes / el / 1e9,
-                "steps": args.pcie_steps, "store": store}
-
-    pcie = staged = None
-    if not args.no_pcie:
-        pcie = host_leg()
-        log(f"pcie-inclusive: {pcie['tokens_per_s']:.1f} tok/s, delta {pcie['delta_gbps_over_host_link']:.1f} GB/s")
-        if args.staging_mb > 0:
-            B.decode_set_staging(int(args.staging_mb * (1 << 20)), args.staging_threads)
-            staged = host_leg()
-            B.decode_set_staging(0)
-            staged["staging_bytes"] = int(args.staging_mb * (1 << 20))
-            staged["gather_threads"] = args.staging_threads or "library default (min(8, cores))"
-            log(f"pcie-staged: {staged['tokens_per_s']:.1f} tok/s, delta {staged['delta_gbps_over_host_link']:.1f} GB/s")
+    log(f"HBM probes: streaming read {probe_gbps:.0f} GB/s, copy {copy_gbps:.0f} GB/s (read + write)")
+    traffic, traffic_note = stored_traffic(ffn["bytes_per_launch"], args.config)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -427,47 +487,60 @@ def main():
         log(f"cpu baseline, one thread: {one['value']:.3f} tok/s")
         log(f"cpu baseline: {cpu['value']:.3f} tok/s on {cpu['cores']} threads")
 
+    store_text = "pinned host memory (hipHostMalloc via torch), the new bundles of every token pulled over the host link"
+    if reuse["distinct"]:
+        store_text += (f"; only {reuse['distinct']} of {c.L} row stores could be pinned, the other layers reuse them "
+                       "(the host-link traffic is the same, the weights differ)")
     out = {
         "metric": "sparse-FFN decode tokens/s at batch 1; effective HBM GB/s vs peak",
-        "value": tok_s,
+        "value": dec["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": dec["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16 weights / fp32 accumulation",
         "data": "synthetic",
-        "config": {"workload": workload_text(c, act_bundles / (args.steps * c.L)),
+        "config": {"workload": workload_text(c, dec["mean_active_per_layer"]),
                    "global_batch": 1, "layers": c.L, "d_model": c.d, "d_ff": c.M, "k_max": c.K,
-                   "weights": "bf16", "backing_store": "HBM", "parallelism": "single GPU",
+                   "weights": "bf16", "backing_store": store_text, "parallelism": "single GPU",
                    "residency_window": args.window, "frequency_levels": args.levels,
                    "buffer_layout": args.layout, "planar_buffers": args.planar,
                    "ffn_reduce": args.reduce},
-        "effective_gbps": eff_gbps,
-        "effective_frac_of_hbm_peak": eff_gbps / HBM_PEAK_GBPS,
-        "mean_active_per_layer": act_bundles / (args.steps * c.L),
-        "mean_delta_per_layer": in_bundles / (args.steps * c.L),
+        "effective_gbps": dec["effective_gbps"],
+        "effective_frac_of_hbm_peak": dec["effective_gbps"] / HBM_PEAK_GBPS,
+        "delta_gbps_over_host_link": dec["delta_gbps"],
+        "mean_active_per_layer": dec["mean_active_per_layer"],
+        "mean_delta_per_layer": dec["mean_delta_per_layer"],
         **({"compact_moves": moves} if moves else {}),
-        "cold_start_ms": cold_ms,
-        "host_enqueue_ms_per_step": enqueued * 1e3 / args.steps,
+        "cold_start_ms": dec["cold_start_ms"],
+        "host_enqueue_ms_per_step": dec["host_enqueue_ms_per_step"],
         "decode_launches": "captured graph replay" if args.graphs else "one by one",
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "k_sparse_ffn", "bytes_per_launch": ffn_bytes_per_launch,
-                     "active_row_bytes_per_launch": act_bytes_per_launch,
-                     "active_row_gbps": act_bytes_per_launch / (avg_burst_us * 1e-6) / 1e9,
-                     "avg_launch_us": avg_burst_us, "avg_launch_us_own_events": avg_event_us,
-                     "timing": f"HIP events on the launch stream around back-to-back launches of the {c.L} layers, "
-                               "each right after its layer's delta assignment (read-through of the new bundles)",
+        "roofline": {"bound": "hbm", "achieved": ffn["achieved_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": ffn["achieved_gbps"] / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel": "k_sparse_ffn", "bytes_per_launch": ffn["bytes_per_launch"],
+                     "active_row_bytes_per_launch": ffn["active_row_bytes_per_launch"],
+                     "active_row_gbps": ffn["active_row_gbps"],
+                     "avg_launch_us": ffn["avg_launch_us"], "avg_launch_us_own_events": ffn["avg_launch_us_own_events"],
+                     "timing": f"HIP events on the launch stream around the {c.L} FFN launches of a token back to back, "
+                               "after that token's assignments and scatters (the FFN of the pinned-host decode: rows "
+                               "resident, nothing written but y)",
                      "traffic_note": traffic_note,
                      "plain_read_same_bytes": stream_bound},
+        "host_link": {"pull_probe_gbps": pull_gbps, "dma_probe_gbps": dma_gbps,
+                      "pcie_gen5_x16_gbps_per_direction": 63.0,
+                      "decode_delta_gbps": dec["delta_gbps"],
+                      "decode_frac_of_pull_probe": dec["delta_gbps"] / pull_gbps,
+                      "scatter_kernel": {**ffn["scatter"], "frac_of_pull_probe": ffn["scatter"]["gbps"] / pull_gbps},
+                      "how": "pull: the streaming-read kernel on 1 GiB of pinned host memory; DMA: hipMemcpyAsync of "
+                             "1 GiB pinned host -> device (torch copy_); both timed with HIP events"},
+        "hbm_store": hbm,
         "hbm_read_probe_gbps": probe_gbps,
         "hbm_copy_probe_gbps": copy_gbps,
-        "pcie_inclusive": pcie,
-        **({"pcie_staged": staged} if staged else {}),
+        **({"staged_delta_io": staged} if staged else {}),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

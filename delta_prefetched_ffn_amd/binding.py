@@ -154,7 +154,7 @@ class Layer:
         _check(lib().np_sparse_ffn_acc(self.h, x_ptr, y_ptr, stream or None))
 
     def set_ffn_reduce(self, mode: str) -> None:
-        """"atomic" (default; fp32 atomics, order free) or "ordered" (fixed order, bit-reproducible)."""
+        """"ordered" (default; atomics-free, fixed order, bit-reproducible) or "atomic" (fp32 atomics, order free)."""
         _check(lib().np_layer_set_ffn_reduce(self.h, REDUCES[mode]))
 
     def set_window(self, window: int) -> None:

@@ -144,8 +144,9 @@ __device__ inline uint32_t pair_seq(uint64_t p) { return (uint32_t)p; }
 __device__ inline float pair_val(uint64_t p) { return __uint_as_float((uint32_t)(p >> 32)); }
 
 // NT threads; JX 16-byte x chunks per lane; SB slots per phase-1 batch per row lane;
-// U2 down rows per lane per phase-2 batch.
-template <int NT, int JX, bool GATED, int SB, int U2>
+// U2 down rows per lane per phase-2 batch; RT read-through of the slots filled this step (a
+// separate instantiation, so that a profile tells the two kinds of launch apart).
+template <int NT, int JX, bool GATED, int SB, int U2, bool RT>
 __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     constexpr int kWaves = NT / 64;
     constexpr int R = GATED ? 3 : 2;
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     // The slot list of the window and its sources: unconditional loads (clamped indexes,
     // values selected afterwards), so that staging waits for exactly these loads.
     constexpr int kStage = (kWinMax + NT - 1) / NT;
-    const bool rt = a.read_through != 0;
+    constexpr bool rt = RT;
     int sv[kStage], su[kStage];
 #pragma unroll
     for (int k = 0; k < kStage; ++k) {
@@ -549,7 +550,10 @@ hipError_t launch_t(const FfnArgs& a, const FfnShape& sh, hipStream_t s) {
     // sized so that about five slots per workgroup take one batch each.
     constexpr int SB = 4;
     constexpr int U2 = NT >= 1024 ? 4 : (NT >= 512 ? 6 : 12);
-    hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2>), dim3(sh.nwg), dim3(NT), 0, s, a);
+    if (a.read_through)
+        hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, true>), dim3(sh.nwg), dim3(NT), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, false>), dim3(sh.nwg), dim3(NT), 0, s, a);
     return hipGetLastError();
 }
 

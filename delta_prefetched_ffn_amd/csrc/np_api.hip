@@ -99,7 +99,7 @@ struct np_layer {
     int n_levels = 0;
     int layout = NP_LAYOUT_SLOTS;
     int planar = 0;             // 1: one buffer per projection row instead of one bundle per slot
-    int reduce = NP_REDUCE_ATOMIC;  // how the FFN combines the partial sums of its workgroups
+    int reduce = NP_REDUCE_ORDERED;  // how the FFN combines the partial sums of its workgroups
     LayerDev ldh{};             // host copy of *ldev
     uint64_t* hpair = nullptr;
     uint64_t* ppair = nullptr;
@@ -633,7 +633,9 @@ struct DecodePlan {
 };
 
 std::mutex g_plan_mu;
-std::vector<std::unique_ptr<DecodePlan>> g_plans;  // most recently used last
+// Plans are shared: a caller keeps its plan alive from lookup until its graph launch is
+// enqueued, even if another thread drops the plan from the cache meanwhile.
+std::vector<std::shared_ptr<DecodePlan>> g_plans;  // most recently used last
 std::atomic<int> g_use_graphs{0};
 constexpr size_t kMaxPlans = 8;
 
@@ -680,7 +682,8 @@ np_status capture_plan(DecodePlan* P) {
 }
 
 // The cached plan for these layers and streams, captured on first use.
-DecodePlan* get_plan(np_layer* const* layers, int n, hipStream_t cs, hipStream_t ps, int dev, np_status* st) {
+std::shared_ptr<DecodePlan> get_plan(np_layer* const* layers, int n, hipStream_t cs, hipStream_t ps, int dev,
+                                     np_status* st) {
     std::lock_guard<std::mutex> lk(g_plan_mu);
     for (size_t i = 0; i < g_plans.size(); ++i) {
         DecodePlan* P = g_plans[i].get();
@@ -690,10 +693,10 @@ DecodePlan* get_plan(np_layer* const* layers, int n, hipStream_t cs, hipStream_t
         if (!same) continue;
         auto keep = std::move(g_plans[i]);
         g_plans.erase(g_plans.begin() + i);
-        g_plans.push_back(std::move(keep));
-        return g_plans.back().get();
+        g_plans.push_back(keep);
+        return keep;
     }
-    auto P = std::make_unique<DecodePlan>();
+    auto P = std::make_shared<DecodePlan>();
     P->layers.assign(layers, layers + n);
     for (int l = 0; l < n; ++l) P->versions.push_back(layers[l]->version);
     P->cs = cs;
@@ -702,8 +705,8 @@ DecodePlan* get_plan(np_layer* const* layers, int n, hipStream_t cs, hipStream_t
     *st = capture_plan(P.get());
     if (*st != NP_OK) return nullptr;
     if (g_plans.size() >= kMaxPlans) g_plans.erase(g_plans.begin());
-    g_plans.push_back(std::move(P));
-    return g_plans.back().get();
+    g_plans.push_back(P);
+    return P;
 }
 
 }  // namespace
@@ -1097,7 +1100,7 @@ np_status np_decode_step(np_layer* const* layers, int32_t n_layers, const int32_
 
     if (g_use_graphs.load() && n_layers <= kMaxGraphLayers && cs && ps && !any_staged) {
         np_status st = NP_OK;
-        DecodePlan* P = get_plan(layers, n_layers, cs, ps, dev, &st);
+        const std::shared_ptr<DecodePlan> P = get_plan(layers, n_layers, cs, ps, dev, &st);
         if (P) {
             for (int l0 = 0; l0 < n_layers; l0 += kParamsPerLaunch) {
                 ParamsUpdate pu{};

@@ -99,13 +99,23 @@ typedef struct np_layer_desc {
     const void* row_store;
 } np_layer_desc;
 
-/* Validates desc, allocates the slot buffer bf16 [k_max][n_rows][d_model]
- * (zero-filled), the slot map int32 [d_ff] (= -1), the owner table int32
- * [k_max] (= -1), the resident and free bitsets, the delta lists and the
- * FFN scratch, and copies the masks to the device. */
+/* Sets up one sparse layer: the resident row buffer of k_max slots that
+ * NeuroPrefetcher section 3.4 keeps per layer (allocated bf16
+ * [k_max][n_rows][d_model], zero-filled), its slot map int32 [d_ff] (-1 for
+ * a neuron that is not resident, section 3.4), the owner table int32
+ * [k_max] (-1 = free slot), the resident and free bitsets, the delta lists
+ * and the FFN scratch, and a device copy of the centroid masks (section 3.1
+ * keeps the centroid table resident on the GPU). desc is read, not kept;
+ * *out receives the layer, owned by the caller until np_layer_destroy.
+ * Errors: NP_EINVAL (a limit above, a NULL or misaligned pointer, stray mask
+ * bits, a row store that is neither device memory of `device` nor mapped
+ * pinned host memory), NP_ENOMEM, NP_EHIP; *out is NULL on any error. */
 np_status np_layer_create(const np_layer_desc* desc, np_layer** out);
 
-/* Frees everything the layer allocated (synchronizes its device first). */
+/* Library infrastructure (no passage of the pages defines it): synchronizes
+ * the layer's device, drops cached decode graphs that use the layer and
+ * frees everything the layer allocated. The row store is the caller's and
+ * is not touched. NP_EINVAL for NULL. */
 np_status np_layer_destroy(np_layer* layer);
 
 /* Back to the state np_layer_create leaves (empty buffer, zero-filled); the
@@ -150,13 +160,14 @@ np_status np_sparse_ffn(np_layer* layer, const float* x, float* y, void* stream)
 np_status np_sparse_ffn_acc(np_layer* layer, const float* x, float* y, void* stream);
 
 /* How the FFN's workgroups combine the partial sums of y (section 3.4 fixes
- * only the sum). NP_REDUCE_ATOMIC (the default): every workgroup adds its
- * partial sums into y with fp32 atomics; the order of the additions, and so
- * the last bits of y, can differ from run to run. np_sparse_ffn then clears y
- * with one extra launch; np_decode_step clears it inside its assign launch.
- * NP_REDUCE_ORDERED: the partial sums are exchanged and added in a fixed
- * order by one workgroup per output tile, one more cross-workgroup hop per
- * launch, bit-identical results run to run. Synchronizes the device. */
+ * only the sum). NP_REDUCE_ORDERED (the default): the partial sums are
+ * exchanged without atomics and added in a fixed order by one workgroup per
+ * output tile, so y is bit-identical run to run. NP_REDUCE_ATOMIC (an
+ * option): every workgroup adds its partial sums into y with fp32 atomics,
+ * one cross-workgroup hop less; the order of the additions, and so the last
+ * bits of y, can differ from run to run. np_sparse_ffn then clears y with
+ * one extra launch; np_decode_step clears it inside its assign launch.
+ * Synchronizes the device. */
 typedef enum { NP_LAYOUT_SLOTS = 0, NP_LAYOUT_COMPACT = 1 } np_layout;
 typedef enum { NP_REDUCE_ATOMIC = 0, NP_REDUCE_ORDERED = 1 } np_reduce;
 np_status np_layer_set_ffn_reduce(np_layer* layer, int32_t mode);
@@ -210,8 +221,11 @@ np_status np_decode_use_graphs(int32_t enable);
  * copies of the staging buffers it replaces. Process-wide setting. */
 np_status np_decode_set_staging(int64_t bytes, int32_t threads);
 
-/* Synchronizes the layer's device, then copies the current state to host
- * buffers (any pointer may be NULL): slot_map int32 [d_ff], owner int32
+/* Inspection of the state NeuroPrefetcher section 3.4 defines: the slot map
+ * (-1 for a neuron without a slot), the delta lists of the last set
+ * difference (D_in = S \ R and D_out = R \ S, ascending) and the slots the
+ * incoming neurons took. Synchronizes the layer's device, then copies the
+ * current state to host buffers (any pointer may be NULL): slot_map int32 [d_ff], owner int32
  * [k_max], d_in / slot_in / d_out int32 [k_max] (lists of the last
  * assignment), act_slots int32 [k_max] (ascending slots of S; with window 1
  * these are all occupied slots), counts
@@ -222,9 +236,14 @@ np_status np_layer_read_state(const np_layer* layer, int32_t* slot_map, int32_t*
                               int32_t* d_in, int32_t* slot_in, int32_t* d_out,
                               int32_t* act_slots, int32_t* counts);
 
-/* Synchronizes, then copies the bundles of the given slots (each < k_max)
- * into dst (host, n * n_rows * d_model bf16). slots == NULL with
- * n == k_max copies the whole buffer. */
+/* Inspection of the resident buffer (NeuroPrefetcher section 3.4: the rows of
+ * the active neurons at the slots the slot map gives; section 3.5: one
+ * neuron-centric [gate|up|down^T] record per neuron). Synchronizes, then
+ * copies the bundles of the given slots (each < k_max) into dst (host,
+ * n * n_rows * d_model bf16, in bundle order whatever the buffer
+ * arrangement). slots == NULL with n == k_max copies the whole buffer,
+ * stale rows of freed slots included. NP_EINVAL for a slot out of range
+ * (nothing copied). */
 np_status np_layer_read_rows(const np_layer* layer, const int32_t* slots, int32_t n, void* dst);
 
 /* Host-side view: out[0..5] = {d_model, d_ff, k_max, n_rows, n_active of the
@@ -311,7 +330,9 @@ np_status np_layer_set_planar(np_layer* layer, int32_t planar);
  * NP_EINVAL if the shape cannot cover k_max active slots. */
 np_status np_layer_set_ffn_shape(np_layer* layer, int32_t slots_per_wg, int32_t tile_cols, int32_t threads);
 
-/* Thread-local text of the calling thread's last error ("" if none). */
+/* Library infrastructure (no passage of the pages defines it): the calling
+ * thread's text of its last failed call ("" if none). The pointer stays
+ * valid until that thread's next failing call. */
 const char* np_last_error(void);
 
 /* Device-side errors. A kernel that finds an inconsistency (a list entry out of range, no

@@ -41,11 +41,32 @@ def build_lib(force: bool = False) -> str:
     return _LIB_PATH
 
 
+def build_sanitized_lib(out_dir: str, force: bool = False) -> str:
+    """oracle.c with AddressSanitizer and UndefinedBehaviorSanitizer (clang, shared sanitizer
+    runtime, any UB report fatal) into out_dir/liboracle_san.so, for the host sanitizer tests."""
+    src = os.path.join(_HERE, "oracle.c")
+    out = os.path.join(out_dir, "liboracle_san.so")
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
+        os.makedirs(out_dir, exist_ok=True)
+        tmp = out + f".tmp{os.getpid()}"
+        cmd = (f"{SAN_CC} -O1 -g -std=c11 -fPIC -shared -ffp-contract=off -fno-omit-frame-pointer "
+               f"-fsanitize=address,undefined -fno-sanitize-recover=undefined -shared-libasan -o {tmp} {src} -lm")
+        if os.system(cmd) != 0:
+            raise RuntimeError(f"failed: {cmd}")
+        os.replace(tmp, out)
+    return out
+
+
+SAN_CC = "/opt/rocm/llvm/bin/clang"
+
+
 @lru_cache(maxsize=1)
 def _lib():
-    if not os.path.exists(_LIB_PATH):
+    # NPO_LIB selects another build of oracle.c (the sanitizer build of the host sanitizer tests)
+    path = os.environ.get("NPO_LIB") or _LIB_PATH
+    if path == _LIB_PATH and not os.path.exists(_LIB_PATH):
         build_lib()
-    lib = ctypes.CDLL(_LIB_PATH)
+    lib = ctypes.CDLL(path)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.npo_active_set.argtypes = [vp, vp, i32, i32, vp]
     lib.npo_active_set.restype = i32

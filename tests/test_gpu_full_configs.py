@@ -1,5 +1,7 @@
-"""GPU parity at the full workload shapes, in the launch configuration the
-benchmark times (np_decode_step on a compute and a copy stream).
+"""GPU parity of the options at full workload shapes (page-native SwiGLU shapes, residency
+window, frequency levels, compacted and planar buffers, staged delta I/O), in the launch
+configuration the benchmark times (np_decode_step on a compute and a copy stream). The
+benchmark's own workloads have the complete check in test_gpu_full_complete.py.
 
 Every (step, layer): delta lists, slot map, owner table and active-slot list
 bit-exact against the oracle. Written rows bit-exact on three layers at every
@@ -93,8 +95,10 @@ def run_full(num: int, where: str = "device", steps: int | None = None, ffn_samp
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("num", [2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("num", [6, 7, 8])
 def test_full_config_device_store(num):
+    """The paper's own shape (SwiGLU, intersected masks) at its three K_max budgets. Configs 2-5
+    have the complete check in test_gpu_full_complete.py."""
     run_full(num, "device")
 
 
@@ -131,8 +135,3 @@ def test_full_config2_staged_delta_io(staging):
     about five chunks per layer)."""
     run_full(2, "host", steps=12, ffn_samples=4, staging=staging)
 
-
-@pytest.mark.timeout(600)
-def test_full_config2_pinned_host_store():
-    """The row store in pinned host memory: the scatter pulls bundles over the host link."""
-    run_full(2, "host", steps=12, ffn_samples=4)

@@ -447,9 +447,11 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     // each hit 32 different banks. Thread c then sums column c (consecutive columns per wave,
     // so the atomic adds below stay coalesced).
     auto swz = [](int c) { return (c & ~7) + (((c & 7) + (c >> 5)) & 7); };
-    // The 64 / CT row lanes of a wave hold the same columns (lanes l and l + CT): they are
-    // added inside the wave first (lane swaps over 32 and 16 lanes, a row rotation over 8),
-    // so one row per wave goes through LDS, written by the wave's first CT lanes.
+    // When a row segment is narrower than a wave (CT <= 32), the 64 / CT row lanes of a wave
+    // hold the same columns (lanes l and l + CT): they are added inside the wave first (lane
+    // swaps over 32 and 16 lanes, a row rotation over 8) and one row per wave goes through LDS,
+    // written by the wave's first CT lanes. Otherwise each row lane (one wave at CT = 64, two
+    // at CT = 128) writes its own LDS row: NT / CT rows of 8 CT columns, 8 NT floats either way.
     if (CT <= 32) {  // uniform over the workgroup
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = lane_fold<32>(acc[e], acc[e], lane);
@@ -462,9 +464,11 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
             for (int e = 0; e < 8; ++e) acc[e] = lane_fold<8>(acc[e], acc[e], lane);
         }
     }
-    if (lane < CT) {
+    const int lds_rows = CT >= 64 ? RL2 : kWaves;
+    if (CT >= 64 || lane < CT) {
+        const int row = CT >= 64 ? r2 : wave;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s_red2[wave * a.tw + swz((c2 << 3) + e)] = acc[e];
+        for (int e = 0; e < 8; ++e) s_red2[row * a.tw + swz((c2 << 3) + e)] = acc[e];
     }
     __syncthreads();
     const int mycol = tid;
@@ -475,12 +479,13 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     float own = 0.f;                          // this workgroup's partial of column tid (tid < tcols)
     if (colok) {
         const int sc = swz(tid);
-        // one row per wave, the reads issued together, added in wave order
+        // the LDS rows, the reads issued together, added in row order
         float pr[kWaves];
 #pragma unroll
-        for (int k = 0; k < kWaves; ++k) pr[k] = s_red2[k * a.tw + sc];
+        for (int k = 0; k < kWaves; ++k) pr[k] = k < lds_rows ? s_red2[k * a.tw + sc] : 0.f;
 #pragma unroll
-        for (int k = 0; k < kWaves; ++k) own += pr[k];
+        for (int k = 0; k < kWaves; ++k)
+            if (k < lds_rows) own += pr[k];
         if (a.atomic_y) {
             // Atomic reduction: every contributor adds its partial into y (cleared before the
             // launch or holding the value to add to). No exchange, no reducer; the order of

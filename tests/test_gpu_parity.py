@@ -266,7 +266,7 @@ def test_maximum_and_minimum_sizes(torch, cfg):
 
 
 @pytest.mark.parametrize("shape", [(3, 128, 256), (5, 256, 512), (5, 256, 1024), (2, 64, 1024), (8, 128, 512),
-                                   (16, 256, 256), (1, 256, 256)])
+                                   (16, 256, 256), (1, 256, 256), (4, 512, 512), (4, 1024, 1024), (6, 512, 1024)])
 def test_ffn_launch_shapes(torch, shape):
     """Every launch shape gives the oracle's y (tolerance) and exact results on dyadic inputs."""
     from delta_prefetched_ffn_amd import binding as B

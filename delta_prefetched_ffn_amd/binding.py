@@ -36,7 +36,7 @@ EXPORTS = ["np_layer_create", "np_layer_destroy", "np_layer_reset", "np_delta_as
            "np_layer_raise_error", "np_probe_read", "np_probe_read_set", "np_probe_copy", "np_decode_use_graphs", "np_layer_set_window",
            "np_sparse_ffn_acc", "np_layer_set_ffn_reduce", "np_layer_set_levels",
            "np_layer_set_layout", "np_layer_read_moves", "np_decode_set_staging",
-           "np_layer_set_planar"]
+           "np_layer_set_planar", "np_sparse_ffn_noalloc"]
 
 
 class NPError(RuntimeError):
@@ -85,6 +85,7 @@ def lib() -> ctypes.CDLL:
         "np_layer_read_moves": [vp, vp, vp, vp],
         "np_decode_set_staging": [i64, i32],
         "np_layer_set_planar": [vp, i32],
+        "np_sparse_ffn_noalloc": [vp, vp, vp, vp],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -152,6 +153,10 @@ class Layer:
     def sparse_ffn_acc(self, x_ptr: int, y_ptr: int, stream: int = 0) -> None:
         """y += FFN(x)."""
         _check(lib().np_sparse_ffn_acc(self.h, x_ptr, y_ptr, stream or None))
+
+    def sparse_ffn_noalloc(self, x_ptr: int, y_ptr: int, stream: int = 0) -> None:
+        """np_sparse_ffn_noalloc: the FFN with its exchange words in the library's static scratch."""
+        _check(lib().np_sparse_ffn_noalloc(self.h, x_ptr, y_ptr, stream or None))
 
     def set_ffn_reduce(self, mode: str) -> None:
         """"ordered" (default; atomics-free, fixed order, bit-reproducible) or "atomic" (fp32 atomics, order free)."""

@@ -29,7 +29,36 @@ int ffn_win_max();
 
 using namespace np;
 
+// Scratch of np_sparse_ffn_noalloc: the FFN's cross-workgroup exchange words, 2 MiB per device,
+// held from the library's load until the process ends. Host code never uses this name as an
+// address (in host code it is a stand-in, not device memory): the device address comes from
+// hipGetSymbolAddress, once per device, when the first layer of that device is created.
 namespace {
+constexpr size_t kScratchWords = size_t(1) << 18;   // 64-bit (sequence, value) words: 2 MiB
+constexpr size_t kScratchHWords = size_t(1) << 16;  // the first 64 Ki words: h (one per active slot)
+}  // namespace
+static __device__ __align__(256) uint64_t scratch[kScratchWords];
+
+namespace {
+
+struct DeviceScratch {
+    uint64_t* ptr = nullptr;  // device address of `scratch` on that device (nullptr if unavailable)
+    uint32_t seq = 0;         // sequence number of the last launch that used it
+};
+std::mutex g_scratch_mu;
+std::map<int, DeviceScratch>& g_scratch = *new std::map<int, DeviceScratch>();
+
+// Once per device, with that device current (called by np_layer_create).
+void setup_scratch(int dev) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch.count(dev)) return;
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+        (void)hipGetLastError();
+        p = nullptr;  // np_sparse_ffn_noalloc then fails with NP_EHIP on this device
+    }
+    g_scratch[dev].ptr = static_cast<uint64_t*>(p);
+}
 
 thread_local std::string g_err;
 
@@ -268,8 +297,17 @@ int scatter_grid(int n_in) { return std::max(1, std::min(n_in, 4096)); }
 // y_holds_base: y already holds the value to add the FFN output to (zeros in a decode step,
 // whose assign launch clears y, or the caller's value for np_sparse_ffn_acc); otherwise the
 // FFN output replaces y.
+// xch (optional): exchange words and sequence number to use instead of the layer's own (the
+// no-allocation entry point passes its static scratch); the reduction is then the ordered one.
+struct Exchange {
+    uint64_t* hpair;
+    uint64_t* ppair;
+    uint32_t seq;
+};
+
 np_status enqueue_ffn(np_layer* L, const float* x, float* y, hipStream_t s, const DecodeParams* prm = nullptr,
-                      int layer = 0, bool read_through = false, bool y_holds_base = false) {
+                      int layer = 0, bool read_through = false, bool y_holds_base = false,
+                      const Exchange* xch = nullptr) {
     FfnShape sh{};
     if (!ffn_shape(L, L->n_active, &sh, prm != nullptr))
         return fail(NP_EINVAL, "no FFN launch shape for d_model=%d n=%d tile=%d", L->desc.d_model,
@@ -283,13 +321,16 @@ np_status enqueue_ffn(np_layer* L, const float* x, float* y, hipStream_t s, cons
     a.counts = L->counts;
     a.x = x;
     a.y = y;
-    a.hpair = L->hpair;
-    a.ppair = L->ppair;
+    a.hpair = xch ? xch->hpair : L->hpair;
+    a.ppair = xch ? xch->ppair : L->ppair;
     a.prm = prm;
     a.layer = layer;
     if (prm) {
         a.seq = 0;
         a.n = -1;
+    } else if (xch) {
+        a.seq = xch->seq;
+        a.n = L->n_active;
     } else {
         if (++L->ffn_seq == 0) L->ffn_seq = 1;  // 0 marks never-written words
         a.seq = L->ffn_seq;
@@ -303,7 +344,7 @@ np_status enqueue_ffn(np_layer* L, const float* x, float* y, hipStream_t s, cons
     a.R = L->desc.n_rows;
     a.M = L->desc.d_ff;
     a.activation = L->desc.act;
-    a.atomic_y = L->reduce == NP_REDUCE_ATOMIC ? 1 : 0;
+    a.atomic_y = !xch && L->reduce == NP_REDUCE_ATOMIC ? 1 : 0;
     a.accumulate = y_holds_base ? 1 : 0;
     if (a.atomic_y && !y_holds_base)  // the atomic reduction adds into y: start from zero
         NP_HIP(hipMemsetAsync(y, 0, (size_t)L->desc.d_model * sizeof(float), s));
@@ -761,6 +802,7 @@ np_status np_layer_create(const np_layer_desc* desc, np_layer** out) {
         delete L;
         return fail(NP_EHIP, "hipSetDevice(%d) failed", D.device);
     }
+    setup_scratch(D.device);
     // Classify the row store: device memory of this device, or pinned host memory.
     hipPointerAttribute_t attr;
     std::memset(&attr, 0, sizeof attr);
@@ -995,7 +1037,8 @@ np_status np_scatter_rows(np_layer* L, void* stream) {
 }
 
 namespace {
-np_status sparse_ffn_call(np_layer* L, const float* x, float* y, void* stream, bool acc) {
+np_status sparse_ffn_call(np_layer* L, const float* x, float* y, void* stream, bool acc,
+                          const Exchange* xch = nullptr) {
     if (!L) return fail(NP_EINVAL, "layer must not be NULL");
     if (!x || !y || !aligned16(x) || !aligned16(y)) return fail(NP_EINVAL, "x and y must be 16-byte aligned device pointers");
     if (L->state == kFresh) return fail(NP_ESTATE, "np_sparse_ffn needs a preceding np_delta_assign");
@@ -1009,7 +1052,32 @@ np_status sparse_ffn_call(np_layer* L, const float* x, float* y, void* stream, b
     const np_status de = check_device_err(L);
     if (de != NP_OK) return de;
     DeviceGuard g(L->desc.device);
-    np_status st = enqueue_ffn(L, x, y, (hipStream_t)stream, nullptr, 0, read_through, acc);
+    Exchange xs{};
+    if (xch) {
+        // the no-allocation entry point: exchange words in the device's static scratch
+        FfnShape sh{};
+        if (!ffn_shape(L, L->n_active, &sh))
+            return fail(NP_EINVAL, "no FFN launch shape for d_model=%d n=%d", L->desc.d_model, L->n_active);
+        const size_t pwords = (size_t)sh.nwg * sh.tw;
+        if ((size_t)L->desc.k_max > kScratchHWords || pwords > kScratchWords - kScratchHWords)
+            return fail(NP_EINVAL, "the FFN launch needs %d h words and %zu partial-sum words; the no-allocation "
+                        "scratch holds %zu and %zu (use np_sparse_ffn)", L->desc.k_max, pwords, kScratchHWords,
+                        kScratchWords - kScratchHWords);
+        uint64_t* base = nullptr;
+        uint32_t seq = 0;
+        {
+            std::lock_guard<std::mutex> lk(g_scratch_mu);
+            auto it = g_scratch.find(L->desc.device);
+            if (it != g_scratch.end()) {
+                base = it->second.ptr;
+                if (++it->second.seq == 0) it->second.seq = 1;  // 0: words never written
+                seq = it->second.seq;
+            }
+        }
+        if (!base) return fail(NP_EHIP, "the static scratch of device %d has no device address", L->desc.device);
+        xs = Exchange{base, base + kScratchHWords, seq};
+    }
+    np_status st = enqueue_ffn(L, x, y, (hipStream_t)stream, nullptr, 0, read_through, acc, xch ? &xs : nullptr);
     if (st != NP_OK) return st;
     L->state = kScattered;
     return NP_OK;
@@ -1022,6 +1090,11 @@ np_status np_sparse_ffn(np_layer* L, const float* x, float* y, void* stream) {
 
 np_status np_sparse_ffn_acc(np_layer* L, const float* x, float* y, void* stream) {
     return sparse_ffn_call(L, x, y, stream, true);
+}
+
+np_status np_sparse_ffn_noalloc(np_layer* L, const float* x, float* y, void* stream) {
+    const Exchange tag{};
+    return sparse_ffn_call(L, x, y, stream, false, &tag);
 }
 
 np_status np_layer_set_ffn_reduce(np_layer* L, int32_t mode) {

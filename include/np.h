@@ -159,6 +159,24 @@ np_status np_sparse_ffn(np_layer* layer, const float* x, float* y, void* stream)
  * (the residual stream of a transformer block). Same state rules. */
 np_status np_sparse_ffn_acc(np_layer* layer, const float* x, float* y, void* stream);
 
+/* For callers that cannot allocate device memory while they run (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the FFN
+ * step of np_sparse_ffn, with the same state rules and the same result, bit for
+ * bit, as np_sparse_ffn with the ordered reduction (the default), but its
+ * cross-workgroup exchange words live in a static per-device scratch of 2 MiB
+ * (one word per active slot and one per partial sum of the launch) instead of
+ * the layer's own. The call allocates and frees nothing (the layer itself is
+ * created beforehand); it always uses the ordered reduction. The scratch is
+ * part of the library, held on every device it runs on until the process
+ * ends; every call on one device shares it, so calls that overlap on one
+ * device (other streams, other host threads) race and give wrong results:
+ * order them. Its address is taken when the device's first layer is created.
+ * Errors: as np_sparse_ffn; NP_EINVAL (nothing enqueued) when the launch needs
+ * more than 65,536 h words or 196,608 partial-sum words (launch shapes with
+ * very many workgroups; np_sparse_ffn serves those); NP_EHIP if the scratch
+ * has no device address on this device. */
+np_status np_sparse_ffn_noalloc(np_layer* layer, const float* x, float* y, void* stream);
+
 /* How the FFN's workgroups combine the partial sums of y (section 3.4 fixes
  * only the sum). NP_REDUCE_ORDERED (the default): the partial sums are
  * exchanged without atomics and added in a fixed order by one workgroup per

@@ -16,13 +16,6 @@ namespace {
 constexpr int kNT = 256;
 constexpr int kU = 8;
 
-// 16-byte chunk c of a bundle (rows of row16 chunks, one after the other) in slot s of the
-// slot buffer: row r = c / row16 lives at s * stride16 + r * plane16 (interleaved or planar).
-__device__ inline size_t slot_chunk(int s, int c, int row16, int stride16, int64_t plane16) {
-    const int r = c / row16;
-    return (size_t)s * stride16 + (size_t)r * plane16 + (size_t)(c - r * row16);
-}
-
 __global__ __launch_bounds__(kNT) void k_scatter_rows(int32_t* counts, const int32_t* __restrict__ d_in,
                                                       const int32_t* __restrict__ slot_in,
                                                       const uint4* __restrict__ store,
@@ -51,32 +44,7 @@ __global__ __launch_bounds__(kNT) void k_scatter_rows(int32_t* counts, const int
 // All layers of a decode step at once: blockIdx.y picks the layer, blockIdx.x strides over
 // that layer's incoming bundles.
 __global__ __launch_bounds__(kNT) void k_scatter_all(ScatterLaunch a) {
-    const LayerDev* L = a.layers[blockIdx.y];
-    const int M = L->M, K = L->K, cb = L->bundle16;
-    const int n_in = min(gmem(L->counts)[0], K);  // the lists hold at most K entries
-    const auto* store = gmem(reinterpret_cast<const uint4*>(L->store));
-    auto* buf = gmem(reinterpret_cast<uint4*>(L->buf));
-    const auto* d_in = gmem(L->d_in);
-    const auto* slot_in = gmem(L->slot_in);
-    for (int i = blockIdx.x; i < n_in; i += gridDim.x) {
-        const int n = d_in[i], s = slot_in[i];
-        if ((unsigned)n >= (unsigned)M || (unsigned)s >= (unsigned)K) {
-            if (threadIdx.x == 0) raise_err(L->counts, kErrBadList);
-            continue;
-        }
-        const auto* src = store + (size_t)n * cb;
-        for (int c = threadIdx.x; c < cb; c += kNT * kU) {
-            typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-            u4 v[kU];
-#pragma unroll
-            for (int u = 0; u < kU; ++u)
-                if (c + u * kNT < cb) v[u] = reinterpret_cast<const NP_GLOBAL u4*>(src)[c + u * kNT];
-#pragma unroll
-            for (int u = 0; u < kU; ++u)
-                if (c + u * kNT < cb)
-                    reinterpret_cast<NP_GLOBAL u4*>(buf)[slot_chunk(s, c + u * kNT, L->row16, L->stride16, L->plane16)] = v[u];
-        }
-    }
+    scatter_bundles<kNT, kU>(a.layers[blockIdx.y], blockIdx.x, gridDim.x);
 }
 
 // Compacted layout: the rows moved by the last assignment, buf[mv_dst[k]] = buf[mv_src[k]]

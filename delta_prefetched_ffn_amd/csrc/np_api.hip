@@ -299,15 +299,26 @@ int scatter_grid(int n_in) { return std::max(1, std::min(n_in, 4096)); }
 // FFN output replaces y.
 // xch (optional): exchange words and sequence number to use instead of the layer's own (the
 // no-allocation entry point passes its static scratch); the reduction is then the ordered one.
+// Prefetch workgroups per FFN launch (each on a compute unit of its own; the FFN takes the
+// rest): a few bundles per workgroup, at most kPrefetchWgsMax workgroups.
+constexpr int kPrefetchWgsMax = 16;
+constexpr int kPrefetchBundlesPerWg = 8;
+int prefetch_wgs(int n_bundles) {
+    return std::max(1, std::min(kPrefetchWgsMax, (n_bundles + kPrefetchBundlesPerWg - 1) / kPrefetchBundlesPerWg));
+}
+
 struct Exchange {
     uint64_t* hpair;
     uint64_t* ppair;
     uint32_t seq;
 };
 
+// pf (optional): a layer with a host-memory row store whose last assignment is not scattered
+// yet; the launch also scatters its new bundles (prefetch workgroups), pf_fixed (a captured
+// launch) with a grid that does not depend on the host's count of them.
 np_status enqueue_ffn(np_layer* L, const float* x, float* y, hipStream_t s, const DecodeParams* prm = nullptr,
                       int layer = 0, bool read_through = false, bool y_holds_base = false,
-                      const Exchange* xch = nullptr) {
+                      const Exchange* xch = nullptr, const np_layer* pf = nullptr, bool pf_fixed = false) {
     FfnShape sh{};
     if (!ffn_shape(L, L->n_active, &sh, prm != nullptr))
         return fail(NP_EINVAL, "no FFN launch shape for d_model=%d n=%d tile=%d", L->desc.d_model,
@@ -352,6 +363,10 @@ np_status enqueue_ffn(np_layer* L, const float* x, float* y, hipStream_t s, cons
     a.q = sh.q;
     a.tw = sh.tw;
     a.nwg = sh.nwg;
+    if (pf) {
+        a.pf = pf->ldev;
+        a.pf_wgs = prefetch_wgs(pf_fixed || pf->n_in < 0 ? pf->desc.k_max : pf->n_in);
+    }
     NP_HIP(launch_sparse_ffn(a, sh, L->desc.n_rows == 3, s));
     return NP_OK;
 }
@@ -565,7 +580,7 @@ constexpr int kScatterWgsPerLayer = 64;
 
 // One token's launches. cid: host [n][2] (gate, effective up) ids; with prm (capture into a
 // decode graph) the ids, x and y come from the parameter block instead. ev: n + 2 events, used
-// only on the two-stream path.
+// only on the two-stream path of staged delta I/O.
 np_status enqueue_token(np_layer* const* layers, int n, const int32_t* cid, const float* x, float* y,
                         hipStream_t cs, hipStream_t ps, const DecodeParams* prm, const hipEvent_t* ev,
                         const std::vector<std::vector<int32_t>>* din = nullptr, Stager* st = nullptr) {
@@ -601,6 +616,28 @@ np_status enqueue_token(np_layer* const* layers, int n, const int32_t* cid, cons
         }
         if (ma.n_layers > 0) NP_HIP(launch_move_all(ma, kScatterWgsPerLayer, cs));
     }
+    bool uses_stager = false;
+    for (int l = 0; l < n && din && st; ++l) uses_stager |= staged(layers[l]);
+    if (!uses_stager) {
+        // Everything on compute_stream, one launch per layer. Device-memory row stores: each
+        // FFN reads its new bundles from the store and writes them into their slots
+        // (read-through). Host-memory row stores: layer 0's scatter runs alone, and the scatter
+        // of layer l + 1 runs in layer l's FFN launch (prefetch workgroups), so the host link
+        // carries the next layer's delta while this layer's FFN reads its resident rows.
+        if (layers[0]->store_is_host) {
+            const np_status r = enqueue_scatter(layers[0], cs, prm != nullptr);
+            if (r != NP_OK) return r;
+        }
+        for (int l = 0; l < n; ++l) {
+            const np_layer* pf = l + 1 < n && layers[l + 1]->store_is_host ? layers[l + 1] : nullptr;
+            np_status r = enqueue_ffn(layers[l], prm ? nullptr : x + (size_t)l * d, prm ? nullptr : y + (size_t)l * d,
+                                      cs, prm, l, !layers[l]->store_is_host, any_atomic, nullptr, pf, prm != nullptr);
+            if (r != NP_OK) return r;
+        }
+        return NP_OK;
+    }
+    // Staged delta I/O for some layer: the host's gathers and DMA copies of layer l overlap
+    // the device's work on earlier layers.
     if (one_queue(layers, n, cs, ps)) {
         // Device-memory row stores: each FFN reads its new bundles from the store and writes
         // them into their slots (read-through). Host-memory stores: one scatter launch first.
@@ -643,7 +680,7 @@ np_status enqueue_token(np_layer* const* layers, int n, const int32_t* cid, cons
     return NP_OK;
 }
 
-// Events for the two-stream path of direct launches: per thread and device, grown on demand.
+// Events for the two-stream path of staged steps: per thread and device, grown on demand.
 np_status step_events(int dev, int n, const hipEvent_t** out) {
     thread_local std::map<int, std::vector<hipEvent_t>> evs;
     auto& v = evs[dev];
@@ -665,10 +702,8 @@ struct DecodePlan {
     int device = 0;
     DecodeParams* prm = nullptr;
     hipGraphExec_t exec = nullptr;
-    std::vector<hipEvent_t> events;
     ~DecodePlan() {
         if (exec) (void)hipGraphExecDestroy(exec);
-        for (hipEvent_t e : events) (void)hipEventDestroy(e);
         if (prm) (void)hipFree(prm);
     }
 };
@@ -691,18 +726,12 @@ void drop_plans_with(const np_layer* L) {
 
 np_status capture_plan(DecodePlan* P) {
     const int n = (int)P->layers.size();
-    const bool two = P->cs != P->ps;
     NP_HIP(hipMalloc(&P->prm, sizeof(DecodeParams)));
     NP_HIP(hipMemset(P->prm, 0, sizeof(DecodeParams)));
-    const int n_ev = two ? n + 2 : 0;  // used only by the two-stream structure
-    for (int i = 0; i < n_ev; ++i) {
-        hipEvent_t e;
-        NP_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
-        P->events.push_back(e);
-    }
     NP_HIP(hipStreamBeginCapture(P->cs, hipStreamCaptureModeRelaxed));
+    // a captured step never stages, so it runs on compute_stream alone and needs no events
     const np_status st = enqueue_token(P->layers.data(), n, nullptr, nullptr, nullptr, P->cs, P->ps, P->prm,
-                                       P->events.data());
+                                       nullptr);
     hipGraph_t graph = nullptr;
     const hipError_t ee = hipStreamEndCapture(P->cs, &graph);
     if (st != NP_OK) {  // the failing call has set the message
@@ -1200,7 +1229,7 @@ np_status np_decode_step(np_layer* const* layers, int32_t n_layers, const int32_
     }
 
     const hipEvent_t* ev = nullptr;
-    if (!one_queue(layers, n_layers, cs, ps)) {
+    if (any_staged && !one_queue(layers, n_layers, cs, ps)) {
         np_status st = step_events(dev, n_layers, &ev);
         if (st != NP_OK) return st;
     }

@@ -150,6 +150,10 @@ struct FfnArgs {
     int32_t activation;     // 0 ReLU, 1 SiLU
     int32_t atomic_y;       // 1: every workgroup adds its tile partials into y with float atomics
     int32_t accumulate;     // ordered reduction only: y = y + FFN instead of y = FFN
+    // Prefetch (pf_wgs > 0): the launch's first pf_wgs workgroups scatter the new bundles of
+    // another layer (pf) from its row store into its slots; the FFN workgroups follow them.
+    const LayerDev* pf;
+    int32_t pf_wgs;
 };
 
 // Device code: view a pointer read from memory as a global-memory pointer. Without it the
@@ -159,6 +163,45 @@ struct FfnArgs {
 template <typename T>
 __device__ inline NP_GLOBAL T* gmem(T* p) {
     return (NP_GLOBAL T*)p;
+}
+
+// 16-byte chunk c of a bundle (rows of row16 chunks, one after the other) in slot s of the
+// slot buffer: row r = c / row16 lives at s * stride16 + r * plane16 (interleaved or planar).
+__device__ inline size_t slot_chunk(int s, int c, int row16, int stride16, int64_t plane16) {
+    const int r = c / row16;
+    return (size_t)s * stride16 + (size_t)r * plane16 + (size_t)(c - r * row16);
+}
+
+// Copies the bundles that layer L's last assignment brought in (d_in / slot_in, counts[0] of
+// them) from its row store into their slots. Workgroup g of ng (NT threads) takes bundles
+// g, g + ng, ...; each lane moves U 16-byte chunks per pass, all U loads issued before the
+// stores.
+template <int NT, int U>
+__device__ inline void scatter_bundles(const LayerDev* L, int g, int ng) {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    const int M = L->M, K = L->K, cb = L->bundle16;
+    const int n_in = min(gmem(L->counts)[0], K);  // the lists hold at most K entries
+    const auto* store = gmem(reinterpret_cast<const u4*>(L->store));
+    auto* buf = gmem(reinterpret_cast<u4*>(L->buf));
+    const auto* d_in = gmem(L->d_in);
+    const auto* slot_in = gmem(L->slot_in);
+    for (int i = g; i < n_in; i += ng) {
+        const int n = d_in[i], s = slot_in[i];
+        if ((unsigned)n >= (unsigned)M || (unsigned)s >= (unsigned)K) {
+            if (threadIdx.x == 0) raise_err(L->counts, kErrBadList);
+            continue;
+        }
+        const auto* src = store + (size_t)n * cb;
+        for (int c = threadIdx.x; c < cb; c += NT * U) {
+            u4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (c + u * NT < cb) v[u] = src[c + u * NT];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (c + u * NT < cb) buf[slot_chunk(s, c + u * NT, L->row16, L->stride16, L->plane16)] = v[u];
+        }
+    }
 }
 
 // Launchers (return hipError_t from the launch).

@@ -14,7 +14,9 @@
  *      (section 3.4; no compaction);
  *   4. the incoming neurons' [gate|up|down^T] bundles are scattered from the
  *      backing row store into their slots (section 3.5, the fused
- *      deinterleave-and-scatter on its own stream);
+ *      deinterleave-and-scatter, which there runs on a stream of its own so
+ *      that it overlaps compute; in np_decode_step it runs inside the
+ *      previous layer's FFN launch, on compute units of its own);
  *   5. the sparse FFN y = sum_{i in S} down_i * relu(gate_i . x) * (up_i . x)
  *      runs over the resident slots only (section 3.4: row i of gate, up and
  *      down^T per active neuron; the slot map locates the rows). A non-gated
@@ -192,16 +194,18 @@ np_status np_layer_set_ffn_reduce(np_layer* layer, int32_t mode);
 
 /* One decode token over n_layers layers of one device with equal d_model
  * (sections 3.1, 3.4, 3.5): validates every layer's cids on the host (a
- * failure leaves every layer unchanged), then enqueues the token. When every
- * row store is device memory, or copy_stream equals compute_stream, all work
- * goes to compute_stream: one launch assigns the deltas of all layers, then
- * the FFNs run in layer order, each reading its new bundles through from a
- * device-memory row store (as np_sparse_ffn right after np_delta_assign);
- * bundles from pinned host stores are copied by one launch for all those
- * layers before the FFNs. When some row store is pinned host memory and the streams differ,
- * layer l's scatter runs on copy_stream after the assignment and layer l's
- * FFN on compute_stream waits only for it, so the host-link transfers of
- * later layers overlap earlier FFNs; copy_stream is joined back into
+ * failure leaves every layer unchanged), then enqueues the token on
+ * compute_stream: one launch assigns the deltas of all layers, then one
+ * launch per layer runs that layer's FFN. A layer whose row store is device
+ * memory has its FFN read the new bundles through from the store (as
+ * np_sparse_ffn right after np_delta_assign). For pinned host row stores the
+ * prefetch of section 3.5 overlaps the host link with the FFNs: layer 0's
+ * bundles are scattered by a launch of their own, and the FFN launch of
+ * layer l also scatters layer l + 1's new bundles from its host store, on a
+ * few compute units of their own, while the FFN runs on the rest.
+ * copy_stream is used only for staged delta I/O (np_decode_set_staging):
+ * then the staged layers' copies and scatters run there and layer l's FFN
+ * waits only for layer l's, and copy_stream is joined back into
  * compute_stream at the end. cids: host int32 [n_layers][2] (gate, up).
  * x, y: device fp32 [n_layers][d_model]. Every layer must be in the fresh
  * or scattered state (NP_ESTATE otherwise); after NP_EHIP the layers need

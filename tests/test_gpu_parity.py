@@ -139,8 +139,10 @@ def test_exact_dyadic_inputs_bit_exact(torch, R):
 
 def test_decode_paths_agree_and_repeat_bitwise(torch):
     """With the ordered reduction: graph replay and direct launches, one stream and two streams,
-    device and pinned-host row stores (the latter takes the per-layer two-stream structure), and
-    per-layer calls give bit-identical y; reruns too."""
+    device, pinned-host and mixed row stores (with host stores each FFN launch also scatters the
+    next layer's new bundles; mixed: a device-store layer between two host-store layers, whose
+    FFN reads through and carries the prefetch), and per-layer calls give bit-identical y and
+    slot buffers; reruns too."""
     from delta_prefetched_ffn_amd import binding as B
     cfg = small_config(960, L=3, d=4096, M=3000, K=600, C=6, mode="union", m=250, swap=30, T=6)
     wl = Workload(cfg)
@@ -148,10 +150,10 @@ def test_decode_paths_agree_and_repeat_bitwise(torch):
     x = torch.from_numpy(x_all).cuda()
     outs, bufs = [], []
     for path in ["two", "one", "calls", "calls-rt", "two-direct", "one-direct", "two-host", "two-host-direct",
-                 "two"]:
+                 "one-host", "one-host-direct", "two-mixed", "two-mixed-direct", "two"]:
         B.decode_use_graphs(not path.endswith("direct"))
-        where = "host" if "host" in path else "device"
-        layers = [make_layer(wl, l, where)[0] for l in range(cfg.L)]
+        where = ["host" if "host" in path or ("mixed" in path and l != 1) else "device" for l in range(cfg.L)]
+        layers = [make_layer(wl, l, where[l])[0] for l in range(cfg.L)]
         for layer in layers:
             layer.set_ffn_reduce("ordered")  # bit-identical results need the fixed-order reduction
         y = torch.zeros_like(x)

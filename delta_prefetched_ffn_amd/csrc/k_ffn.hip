@@ -154,55 +154,11 @@ __device__ inline void st_pair(uint64_t* p, uint32_t seq, float v) {
 __device__ inline uint32_t pair_seq(uint64_t p) { return (uint32_t)p; }
 __device__ inline float pair_val(uint64_t p) { return __uint_as_float((uint32_t)(p >> 32)); }
 
-// Prefetch workgroup g of ng: copies bundles [n_in g / ng, n_in (g + 1) / ng) of layer L's
-// last assignment from its row store into their slots, as one run of 16-byte chunks over all
-// NT lanes with kPfU loads per lane in flight. The workgroup's (neuron, slot) list goes through
-// LDS (s_n, s_s) in pieces of kWinMax entries.
-constexpr int kPfU = 8;
-template <int NT>
-__device__ void prefetch_bundles(const LayerDev* L, int g, int ng, int* s_n, int* s_s) {
-    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-    const int M = L->M, K = L->K, cb = L->bundle16;
-    const int row16 = L->row16, stride16 = L->stride16;
-    const int64_t plane16 = L->plane16;
-    const int n_in = max(0, min(gmem(L->counts)[0], K));  // the lists hold at most K entries
-    const auto* store = gmem(reinterpret_cast<const u4*>(L->store));
-    auto* buf = gmem(reinterpret_cast<u4*>(L->buf));
-    const int b0 = (int)((int64_t)n_in * g / ng), b1 = (int)((int64_t)n_in * (g + 1) / ng);
-    int err = 0;
-    for (int p0 = b0; p0 < b1; p0 += kWinMax) {
-        const int np = min(kWinMax, b1 - p0);
-        __syncthreads();  // the previous piece's list is no longer read
-        for (int i = threadIdx.x; i < np; i += NT) {
-            const int n = gmem(L->d_in)[p0 + i], s = gmem(L->slot_in)[p0 + i];
-            const bool bad = (unsigned)n >= (unsigned)M || (unsigned)s >= (unsigned)K;
-            err |= bad ? kErrBadList : 0;
-            s_n[i] = bad ? -1 : n;
-            s_s[i] = s;
-        }
-        __syncthreads();
-        const int total = np * cb;  // np <= 2048, cb <= 3 * 2048: fits 32 bits
-        for (int k0 = threadIdx.x; k0 < total; k0 += NT * kPfU) {
-            u4 v[kPfU];
-#pragma unroll
-            for (int u = 0; u < kPfU; ++u) {
-                const int k = k0 + u * NT, b = k / cb, n = k < total ? s_n[b] : -1;
-                if (n >= 0) v[u] = store[(size_t)n * cb + (k - b * cb)];
-            }
-#pragma unroll
-            for (int u = 0; u < kPfU; ++u) {
-                const int k = k0 + u * NT, b = k / cb, n = k < total ? s_n[b] : -1;
-                if (n >= 0) buf[slot_chunk(s_s[b], k - b * cb, row16, stride16, plane16)] = v[u];
-            }
-        }
-    }
-    if (err) raise_err(L->counts, err);
-}
-
 // NT threads; JX 16-byte x chunks per lane; SB slots per phase-1 batch per row lane;
 // U2 down rows per lane per phase-2 batch; RT read-through of the slots filled this step (a
-// separate instantiation, so that a profile tells the two kinds of launch apart).
-template <int NT, int JX, bool GATED, int SB, int U2, bool RT>
+// separate instantiation, so that a profile tells the two kinds of launch apart); PF prefetch
+// workgroups ahead of the FFN's (separate too: without them the kernel is unchanged).
+template <int NT, int JX, bool GATED, int SB, int U2, bool RT, bool PF>
 __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     constexpr int kWaves = NT / 64;
     constexpr int R = GATED ? 3 : 2;
@@ -214,11 +170,13 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     __shared__ float s_red1[kWaves * SB * NR1];  // wave sums of the gate/up dot products
     __shared__ float s_red2[NT * 8];
 
-    if ((int)blockIdx.x < a.pf_wgs) {
-        prefetch_bundles<NT>(a.pf, blockIdx.x, a.pf_wgs, s_act, s_src);
-        return;
+    if constexpr (PF) {
+        if ((int)blockIdx.x < a.pf_wgs) {
+            scatter_flat<NT, kWinMax>(a.pf, blockIdx.x, a.pf_wgs, s_act, s_src);
+            return;
+        }
     }
-    const int w = blockIdx.x - a.pf_wgs, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int w = PF ? blockIdx.x - a.pf_wgs : blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int d = a.d, cpr = d >> 3;
     // In a replayed decode step the per-token values come from the parameter block.
     const uint32_t seq = a.prm ? a.prm->seq[a.layer] : a.seq;
@@ -615,10 +573,17 @@ hipError_t launch_t(const FfnArgs& a, const FfnShape& sh, hipStream_t s) {
     // sized so that about five slots per workgroup take one batch each.
     constexpr int SB = 4;
     constexpr int U2 = NT >= 1024 ? 4 : (NT >= 512 ? 6 : 12);
-    if (a.read_through)
-        hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, true>), dim3(sh.nwg + a.pf_wgs), dim3(NT), 0, s, a);
-    else
-        hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, false>), dim3(sh.nwg + a.pf_wgs), dim3(NT), 0, s, a);
+    const dim3 grid(sh.nwg + a.pf_wgs), block(NT);
+    if (a.pf_wgs > 0) {
+        if (a.read_through)
+            hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, true, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, false, true>), grid, block, 0, s, a);
+    } else if (a.read_through) {
+        hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, true, false>), grid, block, 0, s, a);
+    } else {
+        hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, false, false>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 

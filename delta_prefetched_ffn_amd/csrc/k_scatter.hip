@@ -47,6 +47,14 @@ __global__ __launch_bounds__(kNT) void k_scatter_all(ScatterLaunch a) {
     scatter_bundles<kNT, kU>(a.layers[blockIdx.y], blockIdx.x, gridDim.x);
 }
 
+// A row store in pinned host memory: a few workgroups of kFlatNT threads (scatter_flat).
+constexpr int kFlatNT = 1024;
+constexpr int kFlatCap = 2048;
+__global__ __launch_bounds__(kFlatNT) void k_scatter_flat(const LayerDev* L) {
+    __shared__ int s_n[kFlatCap], s_s[kFlatCap];
+    scatter_flat<kFlatNT, kFlatCap>(L, blockIdx.x, gridDim.x, s_n, s_s);
+}
+
 // Compacted layout: the rows moved by the last assignment, buf[mv_dst[k]] = buf[mv_src[k]]
 // for k < counts[5], all layers at once (blockIdx.y = layer). Sources (the end of the old
 // region) and destinations (holes below it) are disjoint, so the copies are independent.
@@ -163,6 +171,11 @@ hipError_t launch_scatter(int32_t* counts, const int32_t* d_in, const int32_t* s
 
 hipError_t launch_scatter_all(const ScatterLaunch& a, int wgs_per_layer, hipStream_t s) {
     hipLaunchKernelGGL(k_scatter_all, dim3(wgs_per_layer, a.n_layers), dim3(kNT), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_scatter_flat(const LayerDev* L, int wgs, hipStream_t s) {
+    hipLaunchKernelGGL(k_scatter_flat, dim3(wgs), dim3(kFlatNT), 0, s, L);
     return hipGetLastError();
 }
 

@@ -299,10 +299,13 @@ int scatter_grid(int n_in) { return std::max(1, std::min(n_in, 4096)); }
 // FFN output replaces y.
 // xch (optional): exchange words and sequence number to use instead of the layer's own (the
 // no-allocation entry point passes its static scratch); the reduction is then the ordered one.
-// Prefetch workgroups per FFN launch (each on a compute unit of its own; the FFN takes the
-// rest): a few bundles per workgroup, at most kPrefetchWgsMax workgroups.
-constexpr int kPrefetchWgsMax = 16;
-constexpr int kPrefetchBundlesPerWg = 8;
+// Workgroups of the scatter from a host-memory row store (scatter_flat), in a launch of its
+// own or as the prefetch workgroups of an FFN launch (each on a compute unit of its own; the
+// FFN takes the rest): about four bundles per workgroup, at most kPrefetchWgsMax workgroups
+// (48, six per XCD: on the Llama-2-7B-shaped decode, 16 to 64 keep the host link within 2 %
+// of its best and 48 was the best).
+constexpr int kPrefetchWgsMax = 48;
+constexpr int kPrefetchBundlesPerWg = 4;
 int prefetch_wgs(int n_bundles) {
     return std::max(1, std::min(kPrefetchWgsMax, (n_bundles + kPrefetchBundlesPerWg - 1) / kPrefetchBundlesPerWg));
 }
@@ -372,6 +375,10 @@ np_status enqueue_ffn(np_layer* L, const float* x, float* y, hipStream_t s, cons
 }
 
 np_status enqueue_scatter(np_layer* L, hipStream_t s, bool fixed_grid = false) {
+    if (L->store_is_host) {  // a few workgroups hold the host link at its ceiling
+        NP_HIP(launch_scatter_flat(L->ldev, prefetch_wgs(fixed_grid || L->n_in < 0 ? L->desc.k_max : L->n_in), s));
+        return NP_OK;
+    }
     const int grid = fixed_grid || L->n_in < 0 ? std::max(1, std::min(L->desc.k_max, 1024)) : scatter_grid(L->n_in);
     NP_HIP(launch_scatter(L->counts, L->d_in(), L->slot_in(), L->store_dev, L->buf, L->desc.d_ff,
                           L->desc.k_max, (int32_t)L->bundle_elems(), L->ldh.row16, L->ldh.stride16, L->ldh.plane16,

@@ -204,6 +204,53 @@ __device__ inline void scatter_bundles(const LayerDev* L, int g, int ng) {
     }
 }
 
+// The scatter for a row store in pinned host memory. A compute unit keeps only a few
+// kilobytes of host-link loads in flight (about 6 GB/s per unit), so a few dozen units hold the
+// link at its ceiling; more workgroups only take units from other work. Workgroup g of ng (NT
+// threads) copies bundles [n_in g / ng, n_in (g + 1) / ng) of layer L's last assignment as one
+// run of 16-byte chunks, kFlatU loads per lane in flight; its (neuron, slot) list goes through
+// LDS (s_n, s_s: CAP entries each) in pieces.
+constexpr int kFlatU = 8;
+template <int NT, int CAP>
+__device__ inline void scatter_flat(const LayerDev* L, int g, int ng, int* s_n, int* s_s) {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    const int M = L->M, K = L->K, cb = L->bundle16;
+    const int row16 = L->row16, stride16 = L->stride16;
+    const int64_t plane16 = L->plane16;
+    const int n_in = max(0, min(gmem(L->counts)[0], K));  // the lists hold at most K entries
+    const auto* store = gmem(reinterpret_cast<const u4*>(L->store));
+    auto* buf = gmem(reinterpret_cast<u4*>(L->buf));
+    const int b0 = (int)((int64_t)n_in * g / ng), b1 = (int)((int64_t)n_in * (g + 1) / ng);
+    int err = 0;
+    for (int p0 = b0; p0 < b1; p0 += CAP) {
+        const int np = min(CAP, b1 - p0);
+        __syncthreads();  // the previous piece's list is no longer read
+        for (int i = threadIdx.x; i < np; i += NT) {
+            const int n = gmem(L->d_in)[p0 + i], s = gmem(L->slot_in)[p0 + i];
+            const bool bad = (unsigned)n >= (unsigned)M || (unsigned)s >= (unsigned)K;
+            err |= bad ? kErrBadList : 0;
+            s_n[i] = bad ? -1 : n;
+            s_s[i] = s;
+        }
+        __syncthreads();
+        const int total = np * cb;  // CAP * 3 * 2048 chunks at most: fits 32 bits
+        for (int k0 = threadIdx.x; k0 < total; k0 += NT * kFlatU) {
+            u4 v[kFlatU];
+#pragma unroll
+            for (int u = 0; u < kFlatU; ++u) {
+                const int k = k0 + u * NT, b = k / cb, n = k < total ? s_n[b] : -1;
+                if (n >= 0) v[u] = store[(size_t)n * cb + (k - b * cb)];
+            }
+#pragma unroll
+            for (int u = 0; u < kFlatU; ++u) {
+                const int k = k0 + u * NT, b = k / cb, n = k < total ? s_n[b] : -1;
+                if (n >= 0) buf[slot_chunk(s_s[b], k - b * cb, row16, stride16, plane16)] = v[u];
+            }
+        }
+    }
+    if (err) raise_err(L->counts, err);
+}
+
 // Launchers (return hipError_t from the launch).
 hipError_t launch_delta_assign(const DeltaLaunch& a, hipStream_t s);
 hipError_t launch_set_params(const ParamsUpdate& p, DecodeParams* dst, hipStream_t s);
@@ -213,6 +260,7 @@ hipError_t launch_scatter(int32_t* counts, const int32_t* d_in, const int32_t* s
                           int32_t bundle_elems, int32_t row16, int32_t stride16, int64_t plane16, int grid,
                           hipStream_t s);
 hipError_t launch_scatter_all(const ScatterLaunch& a, int wgs_per_layer, hipStream_t s);
+hipError_t launch_scatter_flat(const LayerDev* L, int wgs, hipStream_t s);
 hipError_t launch_move_all(const ScatterLaunch& a, int wgs_per_layer, hipStream_t s);
 hipError_t launch_scatter_staged(int32_t* counts, const int32_t* slot_in, const void* stage, uint16_t* buf,
                                  int32_t cnt, int32_t K, int32_t bundle_elems, int32_t row16, int32_t stride16,

@@ -518,7 +518,8 @@ def main():
         **({"compact_moves": moves} if moves else {}),
         "cold_start_ms": dec["cold_start_ms"],
         "host_enqueue_ms_per_step": dec["host_enqueue_ms_per_step"],
-        "decode_launches": "captured graph replay" if args.graphs else "one by one",
+        "decode_launches": ("captured graph replay" if args.graphs else "direct launches") +
+                           ": per token one assign launch and one token launch (every layer's delta scatter and FFN)",
         "roofline": {"bound": "hbm", "achieved": ffn["achieved_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": ffn["achieved_gbps"] / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": "k_sparse_ffn", "bytes_per_launch": ffn["bytes_per_launch"],

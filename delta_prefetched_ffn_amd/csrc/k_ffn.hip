@@ -157,9 +157,10 @@ __device__ inline float pair_val(uint64_t p) { return __uint_as_float((uint32_t)
 // NT threads; JX 16-byte x chunks per lane; SB slots per phase-1 batch per row lane;
 // U2 down rows per lane per phase-2 batch; RT read-through of the slots filled this step (a
 // separate instantiation, so that a profile tells the two kinds of launch apart); PF prefetch
-// workgroups ahead of the FFN's (separate too: without them the kernel is unchanged).
-template <int NT, int JX, bool GATED, int SB, int U2, bool RT, bool PF>
-__global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
+// workgroups ahead of the FFN's (separate too: without them the kernel is unchanged); TOK the
+// token launch (a.tok: every layer's scatter and FFN of a decode token in one grid).
+template <int NT, int JX, bool GATED, int SB, int U2, bool RT, bool PF, bool TOK>
+__global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
     constexpr int kWaves = NT / 64;
     constexpr int R = GATED ? 3 : 2;
     constexpr int NR1 = GATED ? 2 : 1;  // rows dotted with x per slot
@@ -171,12 +172,54 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a) {
     __shared__ float s_red2[NT * 8];
 
     if constexpr (PF) {
-        if ((int)blockIdx.x < a.pf_wgs) {
-            scatter_flat<NT, kWinMax>(a.pf, blockIdx.x, a.pf_wgs, s_act, s_src);
+        if ((int)blockIdx.x < a0.pf_wgs) {
+            scatter_flat<NT, kWinMax>(a0.pf, blockIdx.x, a0.pf_wgs, s_act, s_src);
             return;
         }
     }
-    const int w = PF ? blockIdx.x - a.pf_wgs : blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int w_tok = 0, l_tok = 0;
+    const TokenArgs* __restrict__ ta = a0.tok;
+    if constexpr (TOK) {
+        const int n_pf = ta->n_pf, nl = ta->n_layers;
+        if ((int)blockIdx.x < n_pf) {
+            // Prefetch workgroup: each layer's share of the delta, then its completion. Every
+            // wave first waits for its own stores (they are then in this XCD's L2); after the
+            // barrier one release at agent scope writes the L2 back, so the FFN workgroups on
+            // the other XCDs read the new rows from memory, and then raises the count. (Those
+            // workgroups have read none of these lines since the launch began, so their caches
+            // hold no stale copy.)
+            for (int l = 0; l < nl; ++l) {
+                const LayerDev* L = ta->src[l];
+                scatter_flat<NT, kWinMax>(L, blockIdx.x, n_pf, s_act, s_src);
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                if (threadIdx.x == 0)
+                    __hip_atomic_fetch_add(&L->counts[kPfDoneSlot], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            return;
+        }
+        // FFN workgroup b of the token: layer l, workgroup b - wg0[l] of its FFN, once all n_pf
+        // prefetch workgroups (lower IDs, started first) have finished layer l.
+        const int b = blockIdx.x - n_pf;
+        int l = 0;
+        while (l + 1 < nl && b >= ta->wg0[l + 1]) ++l;
+        if (threadIdx.x == 0) {
+            const int32_t* done = &ta->src[l]->counts[kPfDoneSlot];
+            for (uint32_t it = 0; __hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n_pf; ++it) {
+                if (it >= kSpinLimit) {
+                    raise_err(ta->ffn[l].counts, kErrSpin);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(16);
+            }
+        }
+        __syncthreads();
+        w_tok = b - ta->wg0[l];
+        l_tok = l;
+    }
+    // This launch's arguments: the kernel argument, or the layer's entry of a token launch.
+    const FfnArgs& a = TOK ? ta->ffn[l_tok] : a0;
+    const int w = TOK ? w_tok : (PF ? blockIdx.x - a.pf_wgs : blockIdx.x), tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int d = a.d, cpr = d >> 3;
     // In a replayed decode step the per-token values come from the parameter block.
     const uint32_t seq = a.prm ? a.prm->seq[a.layer] : a.seq;
@@ -574,15 +617,17 @@ hipError_t launch_t(const FfnArgs& a, const FfnShape& sh, hipStream_t s) {
     constexpr int SB = 4;
     constexpr int U2 = NT >= 1024 ? 4 : (NT >= 512 ? 6 : 12);
     const dim3 grid(sh.nwg + a.pf_wgs), block(NT);
-    if (a.pf_wgs > 0) {
+    if (a.tok) {  // sh.nwg: the token's whole grid
+        hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, false, false, true>), dim3(sh.nwg), block, 0, s, a);
+    } else if (a.pf_wgs > 0) {
         if (a.read_through)
-            hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, true, true>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, true, true, false>), grid, block, 0, s, a);
         else
-            hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, false, true>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, false, true, false>), grid, block, 0, s, a);
     } else if (a.read_through) {
-        hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, true, false>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, true, false, false>), grid, block, 0, s, a);
     } else {
-        hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, false, false>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, false, false, false>), grid, block, 0, s, a);
     }
     return hipGetLastError();
 }
@@ -608,6 +653,14 @@ hipError_t launch_sparse_ffn(const FfnArgs& a, const FfnShape& sh, bool gated, h
     if (sh.nt == 512) return gated ? launch_jx<512, true>(a, sh, s) : launch_jx<512, false>(a, sh, s);
     if (sh.nt == 1024) return gated ? launch_jx<1024, true>(a, sh, s) : launch_jx<1024, false>(a, sh, s);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_token(const TokenArgs* ta, int grid, const FfnShape& sh, bool gated, hipStream_t s) {
+    FfnArgs a{};
+    a.tok = ta;
+    FfnShape g = sh;
+    g.nwg = grid;
+    return launch_sparse_ffn(a, g, gated, s);
 }
 
 int ffn_win_max() { return kWinMax; }

@@ -51,7 +51,8 @@ struct LayerDev {
     int32_t* d_out;          // [K]
     int32_t* act;            // [K] ascending occupied slots
     int32_t* act_src;        // [K] per act position: the neuron if its slot was filled this step, else -1
-    int32_t* counts;         // [8] n_in, n_out, n_active, error bits, tokens assigned, moves
+    int32_t* counts;         // [8] n_in, n_out, n_active, error bits, tokens assigned, moves,
+                             // prefetch workgroups done (token launch)
     unsigned long long* acc; // [2] running sums of n_active and n_in
     uint64_t* ring;          // [window - 1][W] active sets of the last tokens (window > 1)
     int32_t W, Kw, M, K;
@@ -125,6 +126,8 @@ struct FfnShape {
     int win_max;   // LDS window capacity (positions)
 };
 
+struct TokenArgs;
+
 struct FfnArgs {
     uint16_t* buf;          // [K][R][d]
     const int32_t* act;     // [K]
@@ -154,6 +157,23 @@ struct FfnArgs {
     // another layer (pf) from its row store into its slots; the FFN workgroups follow them.
     const LayerDev* pf;
     int32_t pf_wgs;
+    // Token launch (only this field is read from the kernel argument): the whole decode token
+    // of a group of layers, described by *tok in device memory.
+    const TokenArgs* tok;
+};
+
+// One launch for a decode token over up to kTokenLayers layers whose row stores are pinned host
+// memory. Workgroups [0, n_pf) copy every layer's new bundles (scatter_flat), layer after layer,
+// and after each layer add 1 to that layer's counts[kPfDoneSlot] (zeroed by the assign launch);
+// workgroups [n_pf + wg0[l], n_pf + wg0[l + 1]) are layer l's FFN, which starts once that count
+// reaches n_pf. ffn is last so that a copy can stop after the layers in use.
+constexpr int kTokenLayers = 64;
+constexpr int kPfDoneSlot = 6;
+struct TokenArgs {
+    int32_t n_layers, n_pf;
+    int32_t wg0[kTokenLayers + 1];
+    const LayerDev* src[kTokenLayers];
+    FfnArgs ffn[kTokenLayers];
 };
 
 // Device code: view a pointer read from memory as a global-memory pointer. Without it the
@@ -266,6 +286,7 @@ hipError_t launch_scatter_staged(int32_t* counts, const int32_t* slot_in, const 
                                  int32_t cnt, int32_t K, int32_t bundle_elems, int32_t row16, int32_t stride16,
                                  int64_t plane16, hipStream_t s);
 hipError_t launch_sparse_ffn(const FfnArgs& a, const FfnShape& sh, bool gated, hipStream_t s);
+hipError_t launch_token(const TokenArgs* ta, int grid, const FfnShape& sh, bool gated, hipStream_t s);
 hipError_t launch_probe_read(const void* src, int64_t bytes, float* sink, hipStream_t s);
 hipError_t launch_probe_copy(void* dst, const void* src, int64_t bytes, hipStream_t s);
 

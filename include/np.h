@@ -198,11 +198,16 @@ np_status np_layer_set_ffn_reduce(np_layer* layer, int32_t mode);
  * compute_stream: one launch assigns the deltas of all layers, then one
  * launch per layer runs that layer's FFN. A layer whose row store is device
  * memory has its FFN read the new bundles through from the store (as
- * np_sparse_ffn right after np_delta_assign). For pinned host row stores the
- * prefetch of section 3.5 overlaps the host link with the FFNs: layer 0's
- * bundles are scattered by a launch of their own, and the FFN launch of
- * layer l also scatters layer l + 1's new bundles from its host store, on a
- * few compute units of their own, while the FFN runs on the rest.
+ * np_sparse_ffn right after np_delta_assign). When every row store is
+ * pinned host memory (and the layers share their FFN workgroup size), the
+ * rest of the token is one launch per group of up to 64 layers, which
+ * overlaps the host link with the FFNs (the prefetch of section 3.5): 24
+ * workgroups copy every layer's new bundles, layer after layer, without a
+ * break at layer boundaries, and each layer's FFN runs on the other compute
+ * units as soon as its bundles are in place. Other pinned host stores:
+ * layer 0's bundles are scattered by a launch of their own, and the FFN
+ * launch of layer l also scatters layer l + 1's new bundles, on a few
+ * compute units of their own, while the FFN runs on the rest.
  * copy_stream is used only for staged delta I/O (np_decode_set_staging):
  * then the staged layers' copies and scatters run there and layer l's FFN
  * waits only for layer l's, and copy_stream is joined back into

@@ -182,6 +182,63 @@ def test_decode_paths_agree_and_repeat_bitwise(torch):
         assert np.array_equal(b, bufs[0])
 
 
+@pytest.mark.parametrize("reduce", ["ordered", "atomic"])
+def test_token_launch_groups_graphs_and_fallback(torch, reduce):
+    """Pinned-host row stores: a decode step runs as one launch per group of up to 64 layers
+    (prefetch workgroups stream every layer's delta, each layer's FFN starts once its delta is
+    in place). 70 layers take two launches per step. Against the oracle for every (step, layer):
+    direct launches, graph replay, and (ordered reduction) bit-identical y and slot buffers in
+    the two, and in per-layer calls. A layer with another FFN workgroup size makes the step
+    fall back to per-layer launches, with the same results."""
+    from delta_prefetched_ffn_amd import binding as B
+    cfg = small_config(980, L=70, d=64, M=256, K=96, C=5, mode="union", m=60, swap=12, T=5)
+    wl = Workload(cfg)
+    x_all = wl.x_all()
+    x = torch.from_numpy(x_all).cuda()
+    orc = OracleRun(wl)
+    stores = [wl.store(l) for l in range(cfg.L)]
+    ref = {}
+    for t in range(cfg.T):
+        for l in range(cfg.L):
+            S, _ = orc.step(t, l, stores[l])
+            ref[t, l] = O.sparse_ffn(stores[l], cfg.R, cfg.d, S, x_all[t, l], cfg.act)
+    final_bufs = [orc.layers[l].buf.copy() for l in range(cfg.L)]
+    outs = {}
+    for path in ["token-direct", "token-graph", "calls", "fallback-direct", "fallback-calls"]:
+        B.decode_use_graphs(path == "token-graph")
+        layers = [make_layer(wl, l, "host", stores[l])[0] for l in range(cfg.L)]
+        for layer in layers:
+            layer.set_ffn_reduce(reduce)
+        if path.startswith("fallback"):
+            layers[33].set_ffn_shape(threads=512)  # the others use 256-thread workgroups at d = 64
+        y = torch.zeros_like(x)
+        s = torch.cuda.Stream()
+        for t in range(cfg.T):
+            if path.endswith("calls"):
+                for l, layer in enumerate(layers):
+                    g, u = (int(v) for v in wl.cids()[t, l])
+                    layer.delta_assign(g, u, s.cuda_stream)
+                    layer.scatter_rows(s.cuda_stream)
+                    layer.sparse_ffn(x[t, l].data_ptr(), y[t, l].data_ptr(), s.cuda_stream)
+            else:
+                B.decode_step(layers, wl.cids()[t], x[t].data_ptr(), y[t].data_ptr(), s.cuda_stream, s.cuda_stream)
+        torch.cuda.synchronize()
+        assert all(L.read_state()["err"] == 0 for L in layers), path
+        yh = y.cpu().numpy()
+        for t in range(cfg.T):
+            for l in range(cfg.L):
+                check_y(yh[t, l], ref[t, l], f"{path} t={t} l={l}")
+        for l in (0, 33, 63, 64, 69):
+            assert np.array_equal(layers[l].read_rows(), final_bufs[l]), f"{path}: layer {l} buffer"
+        outs[path] = yh
+        for layer in layers:
+            layer.close()
+    B.decode_use_graphs(False)
+    if reduce == "ordered":
+        for a, b in (("token-graph", "token-direct"), ("calls", "token-direct"), ("fallback-calls", "fallback-direct")):
+            assert np.array_equal(outs[a].view(np.uint32), outs[b].view(np.uint32)), (a, b)
+
+
 def test_edge_cases_empty_full_turnover_and_exact_capacity(torch):
     from delta_prefetched_ffn_amd import binding as B
     M, K, d, R = 256, 64, 128, 3

@@ -556,7 +556,8 @@ __global__ __launch_bounds__(kNT) void k_delta_assign(DeltaLaunch a) {
         counts[1] = n_out;
         counts[2] = n_act;
         counts[4] = tok + 1;
-        counts[kPfDoneSlot] = 0;  // a token launch counts its prefetch workgroups from here
+        counts[kPfDoneSlot] = 0;  // a token launch counts its finished workgroups from here
+        counts[kFfnDoneSlot] = 0;
         if (s_err) raise_err(L.counts, s_err);
         auto* acc = gmem(L.acc);
         acc[0] += (unsigned long long)n_act;

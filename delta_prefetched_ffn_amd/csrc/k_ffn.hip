@@ -198,14 +198,21 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
             }
             return;
         }
-        // FFN workgroup b of the token: layer l, workgroup b - wg0[l] of its FFN, once all n_pf
-        // prefetch workgroups (lower IDs, started first) have finished layer l.
+        // FFN workgroup b of the token: layer l, workgroup b - wg0[l] of its FFN. It starts once
+        // all n_pf prefetch workgroups have finished layer l and, so that the layers run in
+        // order as a model's do, all workgroups of layer l - 1's FFN have finished (both have
+        // lower IDs and started first).
         const int b = blockIdx.x - n_pf;
         int l = 0;
         while (l + 1 < nl && b >= ta->wg0[l + 1]) ++l;
         if (threadIdx.x == 0) {
             const int32_t* done = &ta->src[l]->counts[kPfDoneSlot];
-            for (uint32_t it = 0; __hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n_pf; ++it) {
+            const int32_t* prev = l > 0 ? &ta->src[l - 1]->counts[kFfnDoneSlot] : nullptr;
+            const int n_prev = l > 0 ? ta->wg0[l] - ta->wg0[l - 1] : 0;
+            for (uint32_t it = 0;; ++it) {
+                if (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n_pf &&
+                    (!prev || __hip_atomic_load(prev, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n_prev))
+                    break;
                 if (it >= kSpinLimit) {
                     raise_err(ta->ffn[l].counts, kErrSpin);
                     break;
@@ -608,6 +615,14 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
     if (host_n && tid == 0 && __hip_atomic_load(&a.counts[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != n)
         err |= kErrCount;
     if (err) raise_err(a.counts, err);
+    if constexpr (TOK) {
+        // This workgroup of the layer's FFN is done (its stores have completed): the next
+        // layer's FFN counts them. The next layer reads nothing this one wrote, so the count
+        // orders the layers without a release (which would write the whole L2 back).
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) __hip_atomic_fetch_add(&a.counts[kFfnDoneSlot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 template <int NT, int JX, bool G>

@@ -52,7 +52,7 @@ struct LayerDev {
     int32_t* act;            // [K] ascending occupied slots
     int32_t* act_src;        // [K] per act position: the neuron if its slot was filled this step, else -1
     int32_t* counts;         // [8] n_in, n_out, n_active, error bits, tokens assigned, moves,
-                             // prefetch workgroups done (token launch)
+                             // prefetch and FFN workgroups done (token launch)
     unsigned long long* acc; // [2] running sums of n_active and n_in
     uint64_t* ring;          // [window - 1][W] active sets of the last tokens (window > 1)
     int32_t W, Kw, M, K;
@@ -164,11 +164,14 @@ struct FfnArgs {
 
 // One launch for a decode token over up to kTokenLayers layers whose row stores are pinned host
 // memory. Workgroups [0, n_pf) copy every layer's new bundles (scatter_flat), layer after layer,
-// and after each layer add 1 to that layer's counts[kPfDoneSlot] (zeroed by the assign launch);
-// workgroups [n_pf + wg0[l], n_pf + wg0[l + 1]) are layer l's FFN, which starts once that count
-// reaches n_pf. ffn is last so that a copy can stop after the layers in use.
+// and after each layer add 1 to that layer's counts[kPfDoneSlot]; workgroups
+// [n_pf + wg0[l], n_pf + wg0[l + 1]) are layer l's FFN, which starts once that count reaches
+// n_pf and layer l - 1's counts[kFfnDoneSlot] (one per finished FFN workgroup) reaches its
+// workgroup count. The assign launch zeroes both counts. ffn is last so that a copy can stop
+// after the layers in use.
 constexpr int kTokenLayers = 64;
 constexpr int kPfDoneSlot = 6;
+constexpr int kFfnDoneSlot = 7;
 struct TokenArgs {
     int32_t n_layers, n_pf;
     int32_t wg0[kTokenLayers + 1];

@@ -1,6 +1,6 @@
 """GPU parity of the options at full workload shapes (page-native SwiGLU shapes, residency
-window, frequency levels, compacted and planar buffers, staged delta I/O), in the launch
-configuration the benchmark times (np_decode_step on a compute and a copy stream). The
+window, frequency levels, compacted and planar buffers, staged delta I/O), through
+np_decode_step as the benchmark calls it (a compute and a copy stream). The
 benchmark's own workloads have the complete check in test_gpu_full_complete.py.
 
 Every (step, layer): delta lists, slot map, owner table and active-slot list

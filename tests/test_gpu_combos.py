@@ -4,7 +4,7 @@ across the 256/512/1024-thread launch shapes), d_ff, K_max, mask mode and row co
 SiLU, crossed with one retention rule (exact S, a residency window, frequency levels or the
 compacted layout), slot or planar buffers, atomic or ordered reduce, a random FFN launch shape
 and one of four launch paths (np_decode_step with direct launches or graph replay, per-layer
-np_delta_assign + read-through np_sparse_ffn, pinned-host store on two streams). Each option
+np_delta_assign + read-through np_sparse_ffn, pinned-host store: the token launch). Each option
 has its own tests elsewhere; this file looks for interactions between them.
 
 Checked per (step, layer): delta lists, slot map, owner table and the FFN's slot list

@@ -1,8 +1,8 @@
 """Different layers driven from different host threads at the same time (the C ABI allows it:
 a layer is not thread-safe, but separate layers are): two threads each run their own workload's
-decode steps on their own streams, one with its row stores in HBM (one queue), one with pinned
-host stores on a compute and a copy stream; afterwards each workload's state, whole buffer and
-y match the oracle exactly as in a single-threaded run. ctypes releases the GIL around every
+decode steps on their own streams, one with its row stores in HBM (one queue), two with pinned
+host stores (token launches, so two of them can run on the GPU at once); afterwards each
+workload's state, whole buffer and y match the oracle exactly as in a single-threaded run. ctypes releases the GIL around every
 library call, so the two threads' host work and enqueues really interleave."""
 import threading
 
@@ -23,14 +23,15 @@ def torch():
     return t
 
 
-def test_two_threads_two_workloads(torch):
+def test_three_threads_three_workloads(torch):
     from delta_prefetched_ffn_amd import binding as B
     B.decode_use_graphs(False)
     runs = []
     for k, (where, cfg) in enumerate([
             ("device", small_config(1500, L=3, d=512, M=900, K=300, C=5, mode="union", m=120, swap=20, T=24)),
             ("host", small_config(1501, L=2, d=1000, M=700, K=260, C=4, mode="intersect", m=200, swap=30, T=24,
-                                  act="silu"))]):
+                                  act="silu")),
+            ("host", small_config(1502, L=4, d=256, M=600, K=200, C=5, mode="union", m=80, swap=15, T=24))]):
         wl = Workload(cfg)
         layers, stores = zip(*[make_layer(wl, l, where) for l in range(cfg.L)])
         x = torch.from_numpy(wl.x_all()).cuda()

@@ -1,18 +1,20 @@
 """Benchmark: sparse-FFN decode at batch 1 on the Llama-2-7B-shaped workload.
 
 One step = one decode token through all 31 sparse layers (np_decode_step), with
-the row stores in pinned host memory as the workload specifies: one launch
+the row stores in pinned host memory as the workload specifies. One launch
 decodes the active sets, diffs them against the resident rows and assigns
-slots for all layers; then, per layer, a scatter kernel on a copy stream pulls
-the token's new [gate|up|down^T] bundles over the host link into their slots,
-and the layer's fused sparse FFN runs on the compute stream as soon as its
-scatter is done, so later layers' transfers overlap earlier layers' FFNs.
+slots for all layers. Then one token launch does the rest: a few workgroups
+pull every layer's new [gate|up|down^T] bundles over the host link into their
+slots, layer after layer. Each layer's fused sparse FFN runs on the other
+compute units as soon as its bundles are in place and the previous layer's FFN
+has finished.
 Centroid IDs and x are resident in HBM before the timed region; the deltas
 cross the host link inside it. `value` is that decode rate.
 
 Beside it: the FFN kernel's own time per launch (the roofline: HBM bytes per
 launch over launch time, against the 8 TB/s peak and a plain read of the same
-bytes), the scatter kernel's rate against the host link's measured ceilings,
+bytes), the decode's and the scatter kernel's rates against the host link's
+measured ceilings,
 the same decode with the row stores moved into HBM ("hbm_store": the FFN then
 reads the new bundles through and no scatter runs), and the CPU oracle.
 
@@ -340,9 +342,9 @@ def main():
         return out
 
     # ---------------- the workload as specified: row stores in pinned host memory ----------------
-    # Per token: one assignment launch for all layers, then per layer a scatter on the copy
-    # stream that pulls the new bundles over the host link, and the layer's FFN on the compute
-    # stream once its scatter is done, so later layers' transfers overlap earlier FFNs.
+    # Per token: one assignment launch for all layers, then one token launch: a few workgroups
+    # pull every layer's new bundles over the host link, and each layer's FFN runs on the other
+    # compute units once its bundles are in place (and the previous layer's FFN has finished).
     hl = make_layers("host")
     log(f"pinned-host layers ready in {time.time() - t0:.1f}s")
     dec = decode_leg(hl, args.steps, args.warmup)

@@ -691,11 +691,9 @@ np_status enqueue_staged(np_layer* L, const std::vector<int32_t>& d_in, hipStrea
     return NP_OK;
 }
 
-// A token's launches go to one queue (assign, the FFNs in layer order, which read their new
-// bundles through from device-memory row stores; one scatter launch first for host-memory
-// stores) unless some row store is in host memory and a separate copy stream is given: then
-// layer l's scatter runs on the copy stream and layer l's FFN waits only for it, so the
-// host-link transfers of later layers overlap earlier FFNs.
+// Staged delta I/O: the staged layers' copies and scatters go to the copy stream, and layer l's
+// FFN waits only for layer l's, unless the two streams are the same (or no row store is in
+// host memory): then everything goes to one queue.
 bool one_queue(np_layer* const* layers, int n, hipStream_t cs, hipStream_t ps) {
     if (cs == ps) return true;
     for (int l = 0; l < n; ++l)

@@ -223,9 +223,9 @@ np_status np_decode_step(np_layer* const* layers, int32_t n_layers, const int32_
  * stream, copy stream) captures the step's launches into a HIP graph; every
  * call then writes that token's centroid IDs, x and y pointers into a small
  * device parameter block with one kernel launch and replays the graph on
- * compute_stream, so a token costs two host calls instead of one per layer
- * (for callers whose host thread is the bottleneck; on the GPU the extra
- * parameter launch makes a step slightly longer). The graph is rebuilt when a
+ * compute_stream, so a token costs two host calls (for callers whose host
+ * thread is the bottleneck; on the GPU the extra parameter launch can make a
+ * step slightly longer). The graph is rebuilt when a
  * layer is reset, reshaped or destroyed. Streams must be non-NULL for the
  * graph path (otherwise, and if capture fails, the launches are issued one by
  * one). Results are the same either way. */

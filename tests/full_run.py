@@ -2,9 +2,9 @@
 
 One run covers a group of layers of a workload from a cold start over all its steps, with the
 same layers built once per row-store placement ("device": the row store in HBM, the FFN reads
-the new bundles through; "host": the row store in pinned host memory, the scatter pulls them
-over the host link on a copy stream). Every placement runs np_decode_step on a compute and a
-copy stream, the launch configuration bench.py times, and is compared with one oracle run:
+the new bundles through; "host": the row store in pinned host memory, the token launch pulls
+them over the host link). Every placement runs np_decode_step as bench.py calls it (a compute
+and a copy stream), and is compared with one oracle run:
 
   * at every (step, layer): the delta lists, slot map, owner table and active-slot list,
     bit-exact (NeuroPrefetcher section 3.4);

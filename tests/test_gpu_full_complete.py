@@ -1,5 +1,5 @@
-"""Complete parity at the benchmark's full workload shapes (configs 2-5), in the launch
-configuration bench.py times (np_decode_step on a compute and a copy stream), with the row
+"""Complete parity at the benchmark's full workload shapes (configs 2-5), through
+np_decode_step as bench.py calls it (a compute and a copy stream), with the row
 store both in HBM and in pinned host memory (the placement the workloads specify: the delta
 bundles cross the host link every token). See tests/full_run.py for what is compared:
 state at every (step, layer), every layer's whole buffer at steps 0, 1, T/2 and T-1, y at

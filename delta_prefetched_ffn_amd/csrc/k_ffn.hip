@@ -154,6 +154,120 @@ __device__ inline void st_pair(uint64_t* p, uint32_t seq, float v) {
 __device__ inline uint32_t pair_seq(uint64_t p) { return (uint32_t)p; }
 __device__ inline float pair_val(uint64_t p) { return __uint_as_float((uint32_t)(p >> 32)); }
 
+// Prefetch workgroup g of n_pf in a token launch: its share of every layer's delta, layer after
+// layer (the same shares and chunk runs as scatter_flat). Each layer's parameters and share are
+// read once, in parallel (one lane per layer), into LDS. When the (neuron, slot) lists of all its
+// shares fit in LDS they are staged there too, and at each layer boundary the next layer's first
+// loads are issued before the wait that completes the stores of the layers before it, so the
+// workgroup keeps the host link busy while it publishes them: after that wait and a barrier, one
+// agent-scope release (which writes this XCD's L2 back) raises each such layer's
+// counts[kPfDoneSlot]. (The FFN workgroups that read those rows have read none of these lines
+// since the launch began, so their caches hold no stale copy.) Otherwise each layer is copied,
+// completed and published in turn.
+struct PfLayer {
+    const uint4* store;
+    uint4* buf;
+    const int32_t* d_in;
+    const int32_t* slot_in;
+    int32_t* counts;
+    int64_t plane16;
+    int32_t cb, row16, stride16, b0, M, K;
+};
+// Loads per lane in flight.
+constexpr int kTokU = 8;
+template <int NT>
+__device__ __forceinline__ void prefetch_token(const TokenArgs* __restrict__ ta, int g, int n_pf, int* s_n, int* s_s) {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    __shared__ PfLayer s_ly[kTokenLayers];
+    __shared__ int s_off[kTokenLayers + 1];
+    const int nl = ta->n_layers;
+    auto publish = [&](int l0, int l1) {  // layers [l0, l1): every wave has waited for its stores
+        __syncthreads();
+        if (threadIdx.x == 0)
+            for (int l = l0; l < l1; ++l)
+                __hip_atomic_fetch_add(&s_ly[l].counts[kPfDoneSlot], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    if ((int)threadIdx.x < nl) {
+        const LayerDev* L = ta->src[threadIdx.x];
+        PfLayer y;
+        y.store = reinterpret_cast<const uint4*>(L->store);
+        y.buf = reinterpret_cast<uint4*>(L->buf);
+        y.d_in = L->d_in;
+        y.slot_in = L->slot_in;
+        y.counts = L->counts;
+        y.plane16 = L->plane16;
+        y.cb = L->bundle16;
+        y.row16 = L->row16;
+        y.stride16 = L->stride16;
+        y.M = L->M;
+        y.K = L->K;
+        const int n_in = max(0, min(gmem(L->counts)[0], y.K));  // the lists hold at most K entries
+        y.b0 = (int)((int64_t)n_in * g / n_pf);
+        s_off[threadIdx.x + 1] = (int)((int64_t)n_in * (g + 1) / n_pf) - y.b0;  // this share's length
+        s_ly[threadIdx.x] = y;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        s_off[0] = 0;
+        for (int l = 0; l < nl; ++l) s_off[l + 1] += s_off[l];
+    }
+    __syncthreads();
+    const int total_entries = s_off[nl];
+    if (total_entries > kWinMax) {  // lists too long for LDS (a cold start of large layers)
+        for (int l = 0; l < nl; ++l) {
+            scatter_flat<NT, kWinMax>(ta->src[l], g, n_pf, s_n, s_s);
+            __builtin_amdgcn_s_waitcnt(0);
+            publish(l, l + 1);
+        }
+        return;
+    }
+    uint64_t bad_layers = 0;  // layers with a list entry out of range (raised at the end)
+    for (int e = threadIdx.x; e < total_entries; e += NT) {
+        int l = 0;
+        while (s_off[l + 1] <= e) ++l;
+        const PfLayer& y = s_ly[l];
+        const int i = y.b0 + e - s_off[l];
+        const int n = gmem(y.d_in)[i], sl = gmem(y.slot_in)[i];
+        const bool bad = (unsigned)n >= (unsigned)y.M || (unsigned)sl >= (unsigned)y.K;
+        bad_layers |= bad ? 1ull << l : 0ull;
+        s_n[e] = bad ? -1 : n;
+        s_s[e] = sl;
+    }
+    __syncthreads();
+    int pend = 0;  // layers [pend, l) are copied by this workgroup but not yet published
+    for (int l = 0; l < nl; ++l) {
+        const int cb = s_ly[l].cb, row16 = s_ly[l].row16, stride16 = s_ly[l].stride16;
+        const int64_t plane16 = s_ly[l].plane16;
+        const auto* store = gmem(reinterpret_cast<const u4*>(s_ly[l].store));
+        auto* buf = gmem(reinterpret_cast<u4*>(s_ly[l].buf));
+        const int off = s_off[l], total = (s_off[l + 1] - off) * cb;
+        const int passes = (total + NT * kTokU - 1) / (NT * kTokU);
+        for (int p = 0; p < passes; ++p) {
+            const int k0 = p * NT * kTokU + (int)threadIdx.x;
+            u4 v[kTokU];
+#pragma unroll
+            for (int u = 0; u < kTokU; ++u) {
+                const int k = k0 + u * NT, b = k / cb, n = k < total ? s_n[off + b] : -1;
+                if (n >= 0) v[u] = store[(size_t)n * cb + (k - b * cb)];
+            }
+            if (p == 0 && pend < l) {
+                // this layer's first loads are in flight: complete and publish the layers before it
+                __builtin_amdgcn_s_waitcnt(0);
+                publish(pend, l);
+                pend = l;
+            }
+#pragma unroll
+            for (int u = 0; u < kTokU; ++u) {
+                const int k = k0 + u * NT, b = k / cb, n = k < total ? s_n[off + b] : -1;
+                if (n >= 0) buf[slot_chunk(s_s[off + b], k - b * cb, row16, stride16, plane16)] = v[u];
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    publish(pend, nl);
+    for (; bad_layers; bad_layers &= bad_layers - 1) raise_err(s_ly[__builtin_ctzll(bad_layers)].counts, kErrBadList);
+}
+
 // NT threads; JX 16-byte x chunks per lane; SB slots per phase-1 batch per row lane;
 // U2 down rows per lane per phase-2 batch; RT read-through of the slots filled this step (a
 // separate instantiation, so that a profile tells the two kinds of launch apart); PF prefetch
@@ -182,20 +296,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
     if constexpr (TOK) {
         const int n_pf = ta->n_pf, nl = ta->n_layers;
         if ((int)blockIdx.x < n_pf) {
-            // Prefetch workgroup: each layer's share of the delta, then its completion. Every
-            // wave first waits for its own stores (they are then in this XCD's L2); after the
-            // barrier one release at agent scope writes the L2 back, so the FFN workgroups on
-            // the other XCDs read the new rows from memory, and then raises the count. (Those
-            // workgroups have read none of these lines since the launch began, so their caches
-            // hold no stale copy.)
-            for (int l = 0; l < nl; ++l) {
-                const LayerDev* L = ta->src[l];
-                scatter_flat<NT, kWinMax>(L, blockIdx.x, n_pf, s_act, s_src);
-                __builtin_amdgcn_s_waitcnt(0);
-                __syncthreads();
-                if (threadIdx.x == 0)
-                    __hip_atomic_fetch_add(&L->counts[kPfDoneSlot], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            prefetch_token<NT>(ta, blockIdx.x, n_pf, s_act, s_src);
             return;
         }
         // FFN workgroup b of the token: layer l, workgroup b - wg0[l] of its FFN. It starts once

@@ -281,6 +281,59 @@ def test_edge_cases_empty_full_turnover_and_exact_capacity(torch):
     layer.close()
 
 
+def test_token_launch_edge_cases(torch):
+    """The edge sequence above through np_decode_step on pinned host stores (the token launch),
+    two layers whose sets differ, with every state, buffer and y checked: empty sets (no FFN
+    work, no delta), |S| = K_max, full turnover, empty deltas for one layer while the other
+    layer's delta is whole."""
+    from delta_prefetched_ffn_amd import binding as B
+    M, K, d, R = 256, 64, 128, 3
+    W = M // 64
+
+    def mask(ids):
+        m = np.zeros(M, dtype=bool)
+        m[list(ids)] = True
+        return np.packbits(m.astype(np.uint8), bitorder="little").view("<u8").astype(np.uint64)
+
+    seqs = [
+        [[], list(range(0, 64)), list(range(0, 64)), list(range(64, 128)), list(range(100, 140)), [],
+         list(range(192, 256))],
+        [list(range(10, 20)), [], list(range(0, 64)), list(range(0, 64)), [], list(range(128, 192)),
+         list(range(128, 192))],
+    ]
+    rng = np.random.default_rng(5)
+    stores, layers, ols = [], [], []
+    for l, sets in enumerate(seqs):
+        gate = np.stack([mask(s_) for s_ in sets])
+        up = np.stack([mask([]) for _ in sets])
+        store = ((rng.standard_normal((M, R, d)).astype(np.float32) * 0.02).view(np.uint32) >> 16).astype(np.uint16)
+        pinned = upload_store(store, "host")
+        layers.append(B.Layer(d_model=d, d_ff=M, k_max=K, n_rows=R, masks=np.stack([gate, up]),
+                              mask_mode=B.MASK_UNION, row_store=pinned.data_ptr(), keepalive=pinned))
+        stores.append(store)
+        ols.append(O.OracleLayer(M, K, R, d))
+    s = torch.cuda.Stream()
+    x_np = rng.standard_normal((2, d)).astype(np.float32)
+    x = torch.from_numpy(x_np).cuda()
+    for i in range(len(seqs[0])):
+        y = torch.full((2, d), float("nan"), device="cuda")
+        cids = np.array([[i, i], [i, i]], dtype=np.int32)
+        B.decode_step(layers, cids, x.data_ptr(), y.data_ptr(), s.cuda_stream, s.cuda_stream)
+        s.synchronize()
+        yh = y.cpu().numpy()
+        for l in range(2):
+            S = np.array(seqs[l][i], dtype=np.int32)
+            res = ols[l].step(S)
+            ols[l].copy_bundles(stores[l], res)
+            compare_state(layers[l].read_state(), ols[l], res, S, f"step {i} layer {l}")
+            assert np.array_equal(layers[l].read_rows(), ols[l].buf), f"step {i} layer {l}: buffer"
+            if S.size == 0:
+                assert (yh[l] == 0).all(), f"step {i} layer {l}"
+            check_y(yh[l], O.sparse_ffn(stores[l], R, d, S, x_np[l]), f"step {i} layer {l}")
+    for layer in layers:
+        layer.close()
+
+
 LIMITS = [
     # the largest d_model (16384: 512-thread FFN workgroups, four x chunks per lane, 64 tiles)
     small_config(970, L=1, d=16384, M=320, K=200, C=4, mode="union", m=90, swap=10, T=5),

@@ -334,6 +334,52 @@ def test_token_launch_edge_cases(torch):
         layer.close()
 
 
+def test_token_launch_layers_of_different_shapes(torch):
+    """One decode step over layers that share d_model but differ in d_ff, K_max, mask mode and
+    activation (pinned host stores: one token launch with per-layer shapes, deltas and FFN
+    arguments), against the oracle at every (step, layer), and bit-identical to per-layer calls."""
+    from delta_prefetched_ffn_amd import binding as B
+    cfgs = [small_config(990, L=1, d=512, M=900, K=300, C=5, mode="union", m=120, swap=20, T=6),
+            small_config(991, L=1, d=512, M=500, K=120, C=4, mode="intersect", m=100, swap=15, T=6, act="silu"),
+            small_config(992, L=1, d=512, M=1300, K=500, C=6, mode="union", m=200, swap=40, T=6)]
+    wls = [Workload(c) for c in cfgs]
+    T = cfgs[0].T
+    x_np = np.stack([np.concatenate([w.x_all()[t] for w in wls]) for t in range(T)])  # [T][3][d]
+    x = torch.from_numpy(x_np).cuda()
+    outs = {}
+    for path in ["token", "calls"]:
+        layers, stores = [], []
+        for w in wls:
+            layer, store = make_layer(w, 0, "host")
+            layer.set_ffn_reduce("ordered")
+            layers.append(layer)
+            stores.append(store)
+        orcs = [OracleRun(w) for w in wls]
+        y = torch.zeros_like(x)
+        s = torch.cuda.Stream()
+        for t in range(T):
+            cids = np.concatenate([w.cids()[t] for w in wls])
+            if path == "token":
+                B.decode_step(layers, cids, x[t].data_ptr(), y[t].data_ptr(), s.cuda_stream, s.cuda_stream)
+            else:
+                for l, layer in enumerate(layers):
+                    layer.delta_assign(int(cids[l, 0]), int(cids[l, 1]), s.cuda_stream)
+                    layer.scatter_rows(s.cuda_stream)
+                    layer.sparse_ffn(x[t, l].data_ptr(), y[t, l].data_ptr(), s.cuda_stream)
+            s.synchronize()
+            for l, (w, orc) in enumerate(zip(wls, orcs)):
+                S, res = orc.step(t, 0, stores[l])
+                compare_state(layers[l].read_state(), orc.layers[0], res, S, f"{path} t={t} l={l}")
+                check_y(y[t, l].cpu().numpy(), O.sparse_ffn(stores[l], w.cfg.R, w.cfg.d, S, x_np[t, l], w.cfg.act),
+                        f"{path} t={t} l={l}")
+        for l, orc in enumerate(orcs):
+            assert np.array_equal(layers[l].read_rows(), orc.layers[0].buf), f"{path} layer {l}: buffer"
+        outs[path] = y.cpu().numpy()
+        for layer in layers:
+            layer.close()
+    assert np.array_equal(outs["token"].view(np.uint32), outs["calls"].view(np.uint32))
+
+
 LIMITS = [
     # the largest d_model (16384: 512-thread FFN workgroups, four x chunks per lane, 64 tiles)
     small_config(970, L=1, d=16384, M=320, K=200, C=4, mode="union", m=90, swap=10, T=5),

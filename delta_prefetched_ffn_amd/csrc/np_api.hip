@@ -464,21 +464,30 @@ np_status token_args(np_layer* const* layers, int n, const float* x, float* y, c
 
 size_t token_bytes(int n) { return offsetof(TokenArgs, ffn) + (size_t)n * sizeof(FfnArgs); }
 
+// The argument staging of direct token launches led by `lead`, allocated on first use.
+np_status token_stage(np_layer* lead) {
+    if (lead->tstage) return NP_OK;
+    auto ts = std::make_unique<TokenStage>();
+    if (hipMalloc(&ts->dev, sizeof(TokenArgs)) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(NP_ENOMEM, "cannot allocate the token launch arguments");
+    }
+    for (int i = 0; i < TokenStage::kRing; ++i) {
+        if (hipHostMalloc((void**)&ts->host[i], sizeof(TokenArgs), 0) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(NP_ENOMEM, "cannot allocate pinned token launch arguments");
+        }
+        NP_HIP(hipEventCreateWithFlags(&ts->copied[i], hipEventDisableTiming));
+    }
+    lead->tstage = std::move(ts);
+    return NP_OK;
+}
+
 np_status enqueue_token_launch(np_layer* const* layers, int n, const float* x, float* y, hipStream_t s,
                                int layer0, bool y_holds_base) {
     np_layer* lead = layers[0];
-    if (!lead->tstage) {
-        auto ts = std::make_unique<TokenStage>();
-        if (hipMalloc(&ts->dev, sizeof(TokenArgs)) != hipSuccess) {
-            (void)hipGetLastError();
-            return fail(NP_ENOMEM, "cannot allocate the token launch arguments");
-        }
-        for (int i = 0; i < TokenStage::kRing; ++i) {
-            NP_HIP(hipHostMalloc((void**)&ts->host[i], sizeof(TokenArgs), 0));
-            NP_HIP(hipEventCreateWithFlags(&ts->copied[i], hipEventDisableTiming));
-        }
-        lead->tstage = std::move(ts);
-    }
+    const np_status as = token_stage(lead);
+    if (as != NP_OK) return as;
     TokenStage& ts = *lead->tstage;
     const int k = ts.next;
     ts.next = (k + 1) % TokenStage::kRing;
@@ -1401,6 +1410,17 @@ np_status np_decode_step(np_layer* const* layers, int32_t n_layers, const int32_
     }
     // the direct launches size their grids from the new host counts; a launch failure leaves the
     // layers assigned-but-unscattered, so they need np_layer_reset before further use
+    if (!any_staged) {
+        // token launches (groups of pinned-host-store layers): their argument staging is allocated
+        // before anything is enqueued, so that a failed allocation leaves every layer unchanged
+        for (int g0 = 0; g0 < n_layers; g0 += kTokenLayers) {
+            bool host = true;
+            for (int l = g0; l < std::min(n_layers, g0 + kTokenLayers); ++l) host = host && layers[l]->store_is_host;
+            if (!host) continue;
+            const np_status r = token_stage(layers[g0]);
+            if (r != NP_OK) return r;
+        }
+    }
     Stager* stg = nullptr;
     if (any_staged) {
         for (int l = 0; l < n_layers; ++l)

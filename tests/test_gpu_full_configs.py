@@ -123,9 +123,9 @@ def test_full_config_compact_layout(num, where):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("num", [2, 8])
-def test_full_config_planar_buffers(num):
-    run_full(num, "device", planar=True)
+@pytest.mark.parametrize("num,where", [(2, "device"), (8, "device"), (2, "host")])
+def test_full_config_planar_buffers(num, where):
+    run_full(num, where, planar=True)
 
 
 @pytest.mark.timeout(600)

@@ -145,10 +145,10 @@ __device__ inline void gstore(char* p, const uint4 v) {
 }
 
 __device__ inline uint64_t ld_pair(const uint64_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(gmem(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ inline void st_pair(uint64_t* p, uint32_t seq, float v) {
-    __hip_atomic_store(p, ((uint64_t)__float_as_uint(v) << 32) | seq, __ATOMIC_RELAXED,
+    __hip_atomic_store(gmem(p), ((uint64_t)__float_as_uint(v) << 32) | seq, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ inline uint32_t pair_seq(uint64_t p) { return (uint32_t)p; }
@@ -176,7 +176,8 @@ struct PfLayer {
 // Loads per lane in flight.
 constexpr int kTokU = 8;
 template <int NT>
-__device__ __forceinline__ void prefetch_token(const TokenArgs* __restrict__ ta, int g, int n_pf, int* s_n, int* s_s) {
+__device__ __forceinline__ void prefetch_token(const NP_GLOBAL TokenArgs* __restrict__ ta, int g, int n_pf, int* s_n,
+                                               int* s_s) {
     typedef uint32_t u4 __attribute__((ext_vector_type(4)));
     __shared__ PfLayer s_ly[kTokenLayers];
     __shared__ int s_off[kTokenLayers + 1];
@@ -185,10 +186,10 @@ __device__ __forceinline__ void prefetch_token(const TokenArgs* __restrict__ ta,
         __syncthreads();
         if (threadIdx.x == 0)
             for (int l = l0; l < l1; ++l)
-                __hip_atomic_fetch_add(&s_ly[l].counts[kPfDoneSlot], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(gmem(s_ly[l].counts) + kPfDoneSlot, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     };
     if ((int)threadIdx.x < nl) {
-        const LayerDev* L = ta->src[threadIdx.x];
+        const auto* L = gmem(ta->src[threadIdx.x]);
         PfLayer y;
         y.store = reinterpret_cast<const uint4*>(L->store);
         y.buf = reinterpret_cast<uint4*>(L->buf);
@@ -284,6 +285,9 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
     __shared__ float s_h[kWinMax];  // h of the window positions
     __shared__ float s_red1[kWaves * SB * NR1];  // wave sums of the gate/up dot products
     __shared__ float s_red2[NT * 8];
+    // Token launch: this workgroup's layer's arguments. Read from LDS, they never wait behind
+    // the row loads (a field read from global memory mid-stream would, returns being in order).
+    __shared__ FfnArgs s_fa;
 
     if constexpr (PF) {
         if ((int)blockIdx.x < a0.pf_wgs) {
@@ -291,8 +295,8 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
             return;
         }
     }
-    int w_tok = 0, l_tok = 0;
-    const TokenArgs* __restrict__ ta = a0.tok;
+    int w_tok = 0;
+    const NP_GLOBAL TokenArgs* __restrict__ ta = gmem(a0.tok);
     if constexpr (TOK) {
         const int n_pf = ta->n_pf, nl = ta->n_layers;
         if ((int)blockIdx.x < n_pf) {
@@ -306,9 +310,13 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
         const int b = blockIdx.x - n_pf;
         int l = 0;
         while (l + 1 < nl && b >= ta->wg0[l + 1]) ++l;
+        static_assert(sizeof(FfnArgs) % 4 == 0 && sizeof(FfnArgs) / 4 <= NT, "FfnArgs copy");
+        if (threadIdx.x < sizeof(FfnArgs) / 4)
+            reinterpret_cast<int32_t*>(&s_fa)[threadIdx.x] =
+                reinterpret_cast<const NP_GLOBAL int32_t*>(&ta->ffn[l])[threadIdx.x];
         if (threadIdx.x == 0) {
-            const int32_t* done = &ta->src[l]->counts[kPfDoneSlot];
-            const int32_t* prev = l > 0 ? &ta->src[l - 1]->counts[kFfnDoneSlot] : nullptr;
+            const NP_GLOBAL int32_t* done = gmem(gmem(ta->src[l])->counts) + kPfDoneSlot;
+            const NP_GLOBAL int32_t* prev = l > 0 ? gmem(gmem(ta->src[l - 1])->counts) + kFfnDoneSlot : nullptr;
             const int n_prev = l > 0 ? ta->wg0[l] - ta->wg0[l - 1] : 0;
             for (uint32_t it = 0;; ++it) {
                 if (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n_pf &&
@@ -323,10 +331,9 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
         }
         __syncthreads();
         w_tok = b - ta->wg0[l];
-        l_tok = l;
     }
     // This launch's arguments: the kernel argument, or the layer's entry of a token launch.
-    const FfnArgs& a = TOK ? ta->ffn[l_tok] : a0;
+    const FfnArgs& a = TOK ? s_fa : a0;
     const int w = TOK ? w_tok : (PF ? blockIdx.x - a.pf_wgs : blockIdx.x), tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int d = a.d, cpr = d >> 3;
     // In a replayed decode step the per-token values come from the parameter block.
@@ -367,8 +374,8 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
 #pragma unroll
     for (int k = 0; k < kStage; ++k) {
         const int i = min(plo + tid + k * NT, a.K - 1);
-        sv[k] = a.act[i];
-        su[k] = a.act_src[i];
+        sv[k] = gmem(a.act)[i];
+        su[k] = gmem(a.act_src)[i];
     }
 #pragma unroll
     for (int k = 0; k < kStage; ++k) {
@@ -708,12 +715,12 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
         if (colok) {
             float yv = 0.f;
             for (int gg = 0; gg < G; ++gg) yv += s_red2[gg * a.tw + tid];
-            auto* yg = gmem(a.prm ? a.prm->y + (size_t)a.layer * a.d : a.y);
+            auto* yg = gmem(a.prm ? gmem(a.prm)->y + (size_t)a.layer * a.d : a.y);
             const float y0 = a.accumulate ? yg[col0 + mycol] : 0.f;
             yg[col0 + mycol] = a.accumulate ? y0 + (yv + own) : yv + own;
         }
     }
-    if (host_n && tid == 0 && __hip_atomic_load(&a.counts[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != n)
+    if (host_n && tid == 0 && __hip_atomic_load(gmem(a.counts) + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != n)
         err |= kErrCount;
     if (err) raise_err(a.counts, err);
     if constexpr (TOK) {
@@ -722,7 +729,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
         // orders the layers without a release (which would write the whole L2 back).
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (tid == 0) __hip_atomic_fetch_add(&a.counts[kFfnDoneSlot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) __hip_atomic_fetch_add(gmem(a.counts) + kFfnDoneSlot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

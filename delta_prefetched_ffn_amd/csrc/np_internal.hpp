@@ -26,6 +26,15 @@ constexpr int kErrWindow = 4;          // FFN: window larger than the LDS stagin
 constexpr int kErrSpin = 8;            // FFN: a wait hit its iteration limit
 constexpr int kErrCount = 16;          // FFN: host and device active counts differ
 
+// Device code: view a pointer read from memory as a global-memory pointer. Without it the
+// compiler must use flat accesses, which share a wait counter with LDS, so every LDS wait
+// would also wait for outstanding global loads and stores.
+#define NP_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ inline NP_GLOBAL T* gmem(T* p) {
+    return (NP_GLOBAL T*)p;
+}
+
 // A layer's counts block: int32 [8] (counts[3] = error bits), 2 x uint64 running sums, then
 // (int32 index 12, 8-byte aligned, not cleared by resets) the device address of the layer's
 // pinned host error word. A kernel that raises error bits ORs them into counts[3] and stores
@@ -34,9 +43,10 @@ constexpr int kErrCount = 16;          // FFN: host and device active counts dif
 // counts[3] has them all).
 constexpr int kErrMirrorSlot = 12;
 __device__ inline void raise_err(int32_t* counts, int bits) {
-    atomicOr(&counts[3], bits);
-    uint32_t* const m = *reinterpret_cast<uint32_t* const*>(counts + kErrMirrorSlot);
-    if (m) __hip_atomic_store(m, (uint32_t)bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    NP_GLOBAL int32_t* const c = gmem(counts);
+    __hip_atomic_fetch_or(c + 3, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    auto* const m = reinterpret_cast<uint32_t*>(*reinterpret_cast<NP_GLOBAL const uintptr_t*>(c + kErrMirrorSlot));
+    if (m) __hip_atomic_store(gmem(m), (uint32_t)bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 // Everything a kernel needs about one layer; lives in device memory.
@@ -179,15 +189,6 @@ struct TokenArgs {
     FfnArgs ffn[kTokenLayers];
 };
 
-// Device code: view a pointer read from memory as a global-memory pointer. Without it the
-// compiler must use flat accesses, which share a wait counter with LDS, so every LDS wait
-// would also wait for outstanding global loads and stores.
-#define NP_GLOBAL __attribute__((address_space(1)))
-template <typename T>
-__device__ inline NP_GLOBAL T* gmem(T* p) {
-    return (NP_GLOBAL T*)p;
-}
-
 // 16-byte chunk c of a bundle (rows of row16 chunks, one after the other) in slot s of the
 // slot buffer: row r = c / row16 lives at s * stride16 + r * plane16 (interleaved or planar).
 __device__ inline size_t slot_chunk(int s, int c, int row16, int stride16, int64_t plane16) {
@@ -200,7 +201,8 @@ __device__ inline size_t slot_chunk(int s, int c, int row16, int stride16, int64
 // g, g + ng, ...; each lane moves U 16-byte chunks per pass, all U loads issued before the
 // stores.
 template <int NT, int U>
-__device__ inline void scatter_bundles(const LayerDev* L, int g, int ng) {
+__device__ inline void scatter_bundles(const LayerDev* layer, int g, int ng) {
+    const NP_GLOBAL LayerDev* const L = gmem(layer);
     typedef uint32_t u4 __attribute__((ext_vector_type(4)));
     const int M = L->M, K = L->K, cb = L->bundle16;
     const int n_in = min(gmem(L->counts)[0], K);  // the lists hold at most K entries
@@ -235,7 +237,8 @@ __device__ inline void scatter_bundles(const LayerDev* L, int g, int ng) {
 // LDS (s_n, s_s: CAP entries each) in pieces.
 constexpr int kFlatU = 8;
 template <int NT, int CAP>
-__device__ inline void scatter_flat(const LayerDev* L, int g, int ng, int* s_n, int* s_s) {
+__device__ inline void scatter_flat(const LayerDev* layer, int g, int ng, int* s_n, int* s_s) {
+    const NP_GLOBAL LayerDev* const L = gmem(layer);
     typedef uint32_t u4 __attribute__((ext_vector_type(4)));
     const int M = L->M, K = L->K, cb = L->bundle16;
     const int row16 = L->row16, stride16 = L->stride16;

@@ -66,18 +66,45 @@ __device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 typedef float fv4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 
-// Dot product of 8 bf16 weights with 8 fp32 x values (lo: x[0..3], hi: x[4..7]).
-__device__ inline float dot8(const uint4 v, const fv4 lo, const fv4 hi) {
+// x is held as two bf16 halves per value (x = hi + lo to 16 significant bits, relative error
+// at most 2^-17), so that a gate or up row, whose weights are bf16, is dotted with x by
+// v_dot2c_f32_bf16: two products and the fp32 accumulation in one instruction, with no
+// unpacking of the weights. 16 bytes of weights (8 columns) take 8 such instructions.
+struct XSplit {
+    uint32_t hi[4], lo[4];
+};
+__device__ inline XSplit split_x(const fv4 a, const fv4 b, bool valid) {
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    XSplit s;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float2 f = valid ? make_float2(v[2 * k], v[2 * k + 1]) : make_float2(0.f, 0.f);
+        const bf2 h = __builtin_convertvector((float __attribute__((ext_vector_type(2)))){f.x, f.y}, bf2);
+        const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+        const float r0 = f.x - __uint_as_float(hb << 16), r1 = f.y - __uint_as_float(hb & 0xffff0000u);
+        const bf2 l = __builtin_convertvector((float __attribute__((ext_vector_type(2)))){r0, r1}, bf2);
+        s.hi[k] = hb;
+        s.lo[k] = __builtin_bit_cast(uint32_t, l);
+    }
+    return s;
+}
+__device__ inline float dot2(uint32_t w, uint32_t x, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, w), __builtin_bit_cast(bf2, x), c, false);
+}
+// Dot product of 8 bf16 weights with the 8 x values of s: the hi half first, then the lo half.
+__device__ inline float dot8(const uint4 v, const XSplit& s) {
     float a = 0.f;
-    a = fmaf(bf_lo(v.x), lo.x, a);
-    a = fmaf(bf_hi(v.x), lo.y, a);
-    a = fmaf(bf_lo(v.y), lo.z, a);
-    a = fmaf(bf_hi(v.y), lo.w, a);
-    a = fmaf(bf_lo(v.z), hi.x, a);
-    a = fmaf(bf_hi(v.z), hi.y, a);
-    a = fmaf(bf_lo(v.w), hi.z, a);
-    a = fmaf(bf_hi(v.w), hi.w, a);
+    a = dot2(v.x, s.hi[0], a);
+    a = dot2(v.y, s.hi[1], a);
+    a = dot2(v.z, s.hi[2], a);
+    a = dot2(v.w, s.hi[3], a);
+    a = dot2(v.x, s.lo[0], a);
+    a = dot2(v.y, s.lo[1], a);
+    a = dot2(v.z, s.lo[2], a);
+    a = dot2(v.w, s.lo[3], a);
     return a;
 }
 
@@ -127,21 +154,33 @@ __device__ inline float lane_fold(float x, float y, int lane) {
     }
 }
 
-// Weight rows are read with unconditional 16-byte loads: a lane with nothing to load
-// reads a fixed valid address (the start of the slot buffer) and its value is not used.
-// Every load is then an unconditional instruction, so the compiler can wait for exactly
-// the loads a computation needs.
-__device__ inline uint4 gload(const char* p) {
-    typedef uint32_t uv4 __attribute__((ext_vector_type(4)));
-    const uv4 t = __builtin_nontemporal_load((const NP_GLOBAL uv4*)p);
+// Weight rows are read with 16-byte buffer loads at 32-bit offsets from a buffer descriptor of
+// the slot buffer (or of the row store). A lane with nothing to load uses an offset past the
+// end of every buffer: the hardware's range check returns zeros for it without a memory access.
+// Every load is then an unconditional instruction, so the compiler waits for exactly the loads
+// a computation needs, and the zeros add nothing to the sums they enter.
+constexpr uint32_t kOOB = 0xFFFFF000u;  // >= every buffer's size (at most 4 GiB - 4096)
+constexpr int kBufWord3 = 0x00020000;   // descriptor word 3: 32-bit data format, no swizzle
+__device__ inline __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+    // (readfirstlane returns a signed int: each half goes through uint32_t before widening, so
+    // the low half cannot sign-extend over the high one)
+    const uint64_t b = (uint64_t)base;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    const uint64_t u = ((uint64_t)hi << 32) | (uint64_t)lo;
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), (short)0,
+                                            (int)__builtin_amdgcn_readfirstlane(bytes), kBufWord3);
+}
+// Non-temporal: every weight byte is read once per launch.
+__device__ inline uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
     return make_uint4(t.x, t.y, t.z, t.w);
 }
-// Read-through stores of new rows are streaming (non-temporal): nothing in this launch reads
-// them again, and they should not sit dirty in the L2 when the launch ends.
-__device__ inline void gstore(char* p, const uint4 v) {
-    typedef uint32_t uv4 __attribute__((ext_vector_type(4)));
-    uv4 t = {v.x, v.y, v.z, v.w};
-    __builtin_nontemporal_store(t, (NP_GLOBAL uv4*)p);
+// Read-through stores of new rows (streaming: nothing in this launch reads them again); an
+// offset past the end drops the store.
+__device__ inline void bstore(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint4 v) {
+    const u32x4 t = {v.x, v.y, v.z, v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(t, r, (int)off, 0, 2);
 }
 
 __device__ inline uint64_t ld_pair(const uint64_t* p) {
@@ -273,25 +312,27 @@ __device__ __forceinline__ void prefetch_token(const NP_GLOBAL TokenArgs* __rest
 // U2 down rows per lane per phase-2 batch; RT read-through of the slots filled this step (a
 // separate instantiation, so that a profile tells the two kinds of launch apart); PF prefetch
 // workgroups ahead of the FFN's (separate too: without them the kernel is unchanged); TOK the
-// token launch (a.tok: every layer's scatter and FFN of a decode token in one grid).
-template <int NT, int JX, bool GATED, int SB, int U2, bool RT, bool PF, bool TOK>
+// token launch (a.tok: every layer's scatter and FFN of a decode token in one grid); FCL, when
+// not 0, the lanes per row (CL) fixed at compile time, together with 256-column tiles: the
+// lane geometry then costs no runtime divisions or branches.
+template <int NT, int JX, bool GATED, int SB, int U2, bool RT, bool PF, bool TOK, int FCL>
 __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
     constexpr int kWaves = NT / 64;
     constexpr int R = GATED ? 3 : 2;
     constexpr int NR1 = GATED ? 2 : 1;  // rows dotted with x per slot
 
-    __shared__ int s_act[kWinMax];
-    __shared__ int s_src[kWinMax];  // read-through: neuron whose bundle is in the row store, else -1
     __shared__ float s_h[kWinMax];  // h of the window positions
     __shared__ float s_red1[kWaves * SB * NR1];  // wave sums of the gate/up dot products
-    __shared__ float s_red2[NT * 8];
+    // partial-sum rows: one per wave of 256 columns with the compiled geometry, else up to 8 NT
+    __shared__ float s_red2[FCL ? kWaves * 256 : NT * 8];
     // Token launch: this workgroup's layer's arguments. Read from LDS, they never wait behind
     // the row loads (a field read from global memory mid-stream would, returns being in order).
     __shared__ FfnArgs s_fa;
 
     if constexpr (PF) {
         if ((int)blockIdx.x < a0.pf_wgs) {
-            scatter_flat<NT, kWinMax>(a0.pf, blockIdx.x, a0.pf_wgs, s_act, s_src);
+            __shared__ int s_pn[kWinMax], s_ps[kWinMax];
+            scatter_flat<NT, kWinMax>(a0.pf, blockIdx.x, a0.pf_wgs, s_pn, s_ps);
             return;
         }
     }
@@ -300,7 +341,8 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
     if constexpr (TOK) {
         const int n_pf = ta->n_pf, nl = ta->n_layers;
         if ((int)blockIdx.x < n_pf) {
-            prefetch_token<NT>(ta, blockIdx.x, n_pf, s_act, s_src);
+            __shared__ int s_pn[kWinMax], s_ps[kWinMax];
+            prefetch_token<NT>(ta, blockIdx.x, n_pf, s_pn, s_ps);
             return;
         }
         // FFN workgroup b of the token: layer l, workgroup b - wg0[l] of its FFN. It starts once
@@ -335,23 +377,28 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
     // This launch's arguments: the kernel argument, or the layer's entry of a token launch.
     const FfnArgs& a = TOK ? s_fa : a0;
     const int w = TOK ? w_tok : (PF ? blockIdx.x - a.pf_wgs : blockIdx.x), tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int d = a.d, cpr = d >> 3;
+    const int d = a.d, cpr = d >> 3, K = a.K;
     // In a replayed decode step the per-token values come from the parameter block.
     const uint32_t seq = a.prm ? a.prm->seq[a.layer] : a.seq;
     const auto* xg = gmem(a.prm ? a.prm->x + (size_t)a.layer * a.d : a.x);
+    const auto* act = gmem(a.act);
+    const auto* act_src = gmem(a.act_src);
 
     // Phase-1 lane geometry: CL lanes share a row (power of two), RL row lanes.
-    int CL = NT;
-    while (CL > cpr && CL > 1) CL >>= 1;
+    int CL_rt = NT;
+    while (CL_rt > cpr && CL_rt > 1) CL_rt >>= 1;
+    const int CL = FCL ? FCL : CL_rt;
     const int RL = NT / CL;
     const int rl = tid / CL, cl = tid % CL;
 
     // |S| comes from the host (it validated the capacity with it); the device count is only
-    // checked against it, at the very end, so that no address waits for that load. A replayed
-    // graph has no host count and reads the device one.
+    // checked against it, with a load that goes out beside the h polls below, whose wait covers
+    // it (a wave's loads return in order: issued before the row loads it would hold them back,
+    // and a check right after its load would wait for all of them). A replayed graph has no
+    // host count and reads the device one.
     const bool host_n = a.n >= 0 && !a.prm;
     int n = host_n ? a.n : gmem(a.counts)[2];
-    n = n < 0 ? 0 : (n > a.K ? a.K : n);
+    n = n < 0 ? 0 : (n > K ? K : n);
     // c * n <= 4096 * 65536 < 2^31: 32-bit arithmetic
     auto cbeg = [&](int c) { return (int)(((unsigned)c * (unsigned)n) / (unsigned)a.p1); };
 
@@ -365,33 +412,41 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
         phi = plo + kWinMax;
     }
     const int wn = phi - plo;
+    const bool has1 = w < a.p1;
+    const int c0 = has1 ? max(cbeg(w), plo) : 0, c1 = has1 ? min(cbeg(w + 1), phi) : 0;
 
-    // The slot list of the window and its sources: unconditional loads (clamped indexes,
-    // values selected afterwards), so that staging waits for exactly these loads.
-    constexpr int kStage = (kWinMax + NT - 1) / NT;
-    constexpr bool rt = RT;
-    int sv[kStage], su[kStage];
-#pragma unroll
-    for (int k = 0; k < kStage; ++k) {
-        const int i = min(plo + tid + k * NT, a.K - 1);
-        sv[k] = gmem(a.act)[i];
-        su[k] = gmem(a.act_src)[i];
-    }
-#pragma unroll
-    for (int k = 0; k < kStage; ++k) {
-        const int i = tid + k * NT;
-        const int u = rt ? su[k] : -1;
-        const bool bad = (unsigned)sv[k] >= (unsigned)a.K;
-        const bool badsrc = u >= a.M;
-        if (i < wn) {
-            err |= (bad || badsrc) ? kErrBadList : 0;
-            s_act[i] = bad ? 0 : sv[k];
-            s_src[i] = (bad || badsrc || u < 0) ? -1 : u;
-        }
-    }
-    __syncthreads();
+    // Phase-2 lane geometry: down tile t, CT lanes per row segment, RL2 row lanes.
+    const int t = w % a.q;
+    const int col0 = t * a.tw;
+    const int tcols = min(a.tw, d - col0);
+    const int CT = FCL ? 32 : a.tw >> 3;
+    const int RL2 = NT / CT;
+    const int c2 = tid % CT, r2 = tid / CT;
+    const bool cok = (c2 << 3) < tcols;
 
-    // x for this lane's fixed column chunks (needed only once the rows arrive)
+    // Row offsets. Slot buffer: row r of slot s at s * slot_stride + r * row_plane. Row store
+    // (read-through): row r of neuron u at u * bundle + r * row bytes.
+    const uint32_t rowb = (uint32_t)cpr * 16u, bundle = (uint32_t)R * rowb;
+    const __amdgpu_buffer_rsrc_t rs_buf = buf_rsrc(a.buf, a.buf_bytes);
+    const __amdgpu_buffer_rsrc_t rs_sto = buf_rsrc(RT ? a.store : a.buf, RT ? a.store_bytes : 0u);
+    // A position's slot and (read-through) source neuron, from the lists; bad entries raise an
+    // error bit and read nothing.
+    auto slot_of = [&](int pos, bool valid, int& src) -> int {
+        const int i = min(max(pos, 0), K - 1);
+        const int s = act[i];
+        const int u = RT ? act_src[i] : -1;
+        err |= valid && ((unsigned)s >= (unsigned)K || u >= a.M) ? kErrBadList : 0;
+        src = (u >= 0 && u < a.M) ? u : -1;
+        return s;
+    };
+
+    // ---------------- list loads (issued before any row load) ----------------
+    int sl1[SB], sr1[SB];
+#pragma unroll
+    for (int i = 0; i < SB; ++i) sl1[i] = slot_of(c0 + rl + RL * i, c0 + rl + RL * i < c1, sr1[i]);
+    int sl2[U2], sr2[U2];
+#pragma unroll
+    for (int u = 0; u < U2; ++u) sl2[u] = slot_of(plo + r2 + u * RL2, r2 + u * RL2 < wn, sr2[u]);
     fv4 xr[JX][2];
 #pragma unroll
     for (int j = 0; j < JX; ++j) {
@@ -401,58 +456,54 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
     }
 
     // ---------------- phase 1 loads: gate/up rows of chunk w (issued first) ----------------
-    const size_t slot_bytes = (size_t)R * cpr * 16u;  // a bundle in the row store
-    const char* const buf_c = reinterpret_cast<const char*>(a.buf);
-    char* const buf_w = reinterpret_cast<char*>(a.buf);
-    const char* const store_c = reinterpret_cast<const char*>(a.store);
-    // Row r of the slot at window position p in the slot buffer (interleaved or planar).
-    auto slot_row = [&](int p, int r) -> size_t {
-        return (size_t)s_act[p] * a.slot_stride + (size_t)r * a.row_plane;
+    // Offsets of row r of the position with slot s / source u, at this lane's column chunk c.
+    auto off_buf = [&](bool ok, int s, int r, uint32_t colb) -> uint32_t {
+        return ok && (unsigned)s < (unsigned)K ? (uint32_t)s * a.slot_stride + (uint32_t)r * a.row_plane + colb : kOOB;
     };
-    // Start of row r of the bundle at window position p: in its slot, or in the row store for a
-    // slot filled this step (read-through).
-    auto row_at = [&](int p, int r) -> const char* {
-        const int src = s_src[p];
-        return src >= 0 ? store_c + (size_t)src * slot_bytes + (size_t)r * cpr * 16u : buf_c + slot_row(p, r);
+    auto off_sto = [&](bool ok, int u, int r, uint32_t colb) -> uint32_t {
+        return ok && u >= 0 ? (uint32_t)u * bundle + (uint32_t)r * rowb + colb : kOOB;
     };
-    const bool has1 = w < a.p1;
-    const int c0 = has1 ? max(cbeg(w), plo) : 0, c1 = has1 ? min(cbeg(w + 1), phi) : 0;
+    // Row r at position pos (slot s, source u): from the row store when read-through applies,
+    // else from the slot buffer. One of the two loads is out of range and returns zeros.
+    auto row_load = [&](bool ok, int s, int u, int r, uint32_t cb_buf, uint32_t cb_sto) -> uint4 {
+        if constexpr (RT) {
+            const uint4 p = bload(rs_buf, off_buf(ok && u < 0, s, r, cb_buf));
+            const uint4 q = bload(rs_sto, off_sto(ok, u, r, cb_sto));
+            return make_uint4(p.x | q.x, p.y | q.y, p.z | q.z, p.w | q.w);
+        } else {
+            return bload(rs_buf, off_buf(ok, s, r, cb_buf));
+        }
+    };
     uint4 wv[SB][NR1][JX];
-    auto load_batch = [&](int b0) {
+    auto load_batch = [&](int b0, const int* sl, const int* sr) {
 #pragma unroll
         for (int i = 0; i < SB; ++i) {
-            const int pos = b0 + rl + RL * i;
-            const bool ok = pos < c1;
+            const bool ok = b0 + rl + RL * i < c1;
 #pragma unroll
-            for (int r = 0; r < NR1; ++r) {
-                const char* rp = ok ? row_at(pos - plo, r) : buf_c;
+            for (int r = 0; r < NR1; ++r)
 #pragma unroll
                 for (int j = 0; j < JX; ++j) {
                     const int c = cl + CL * j;
-                    wv[i][r][j] = gload(ok && c < cpr ? rp + (size_t)c * 16u : buf_c);
+                    wv[i][r][j] = row_load(ok && c < cpr, sl[i], sr[i], r, (uint32_t)c * 16u, (uint32_t)c * 16u);
                 }
-            }
         }
     };
     // h for the batch starting at b0: dot products, reduction over the row lane, store.
-    auto compute_batch = [&](int b0) {
+    XSplit xs[JX];
+    auto compute_batch = [&](int b0, const int* sl, const int* sr) {
         constexpr int V = SB * NR1;  // partial dot products per lane (a power of two <= 64)
-        if (rt) {
+        if constexpr (RT) {
             // read-through: the gate/up pieces of slots filled this step go into their slots
 #pragma unroll
             for (int i = 0; i < SB; ++i) {
-                const int pos = b0 + rl + RL * i;
-                if (pos < c1 && s_src[pos - plo] >= 0) {
+                const bool ok = b0 + rl + RL * i < c1 && sr[i] >= 0;
 #pragma unroll
-                    for (int r = 0; r < NR1; ++r) {
-                        char* dst = buf_w + slot_row(pos - plo, r);
+                for (int r = 0; r < NR1; ++r)
 #pragma unroll
-                        for (int j = 0; j < JX; ++j) {
-                            const int c = cl + CL * j;
-                            if (c < cpr) gstore(dst + (size_t)c * 16u, wv[i][r][j]);
-                        }
+                    for (int j = 0; j < JX; ++j) {
+                        const int c = cl + CL * j;
+                        bstore(rs_buf, off_buf(ok && c < cpr, sl[i], r, (uint32_t)c * 16u), wv[i][r][j]);
                     }
-                }
             }
         }
         float v[V];
@@ -461,9 +512,12 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
 #pragma unroll
             for (int r = 0; r < NR1; ++r) {
                 float acc = 0.f;
+                // nothing to compute for an unused position (uniform over the wave when a row
+                // spans whole waves); its loads returned zeros either way
+                if (b0 + rl + RL * i < c1) {
 #pragma unroll
-                for (int j = 0; j < JX; ++j)
-                    if (cl + CL * j < cpr) acc += dot8(wv[i][r][j], xr[j][0], xr[j][1]);
+                    for (int j = 0; j < JX; ++j) acc += dot8(wv[i][r][j], xs[j]);
+                }
                 v[i * NR1 + r] = acc;
             }
         if (CL >= 64) {
@@ -534,35 +588,35 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
             }
         }
     };
-    if (has1) load_batch(c0);
+    // Unconditional: a workgroup without gate/up work issues out-of-range loads, so that the
+    // wait counts below are the same on every path.
+    load_batch(c0, sl1, sr1);
     // Every wave issues its gate/up loads before any wave issues down loads: each SIMD issues
     // its oldest wave's loads back to back, so without this barrier the down rows of the first
     // waves queue ahead of the gate/up rows of the last ones and h waits for the whole stream.
     __syncthreads();
 
     // ---------------- phase 2 loads: first batch of the down tile (overlaps phase 1) -------------
-    const int t = w % a.q;
-    const int col0 = t * a.tw;
-    const int tcols = min(a.tw, d - col0);
-    const int CT = a.tw >> 3;                 // lanes per row segment
-    const int RL2 = NT / CT;                  // row lanes
-    const int c2 = tid % CT, r2 = tid / CT;
-    const bool cok = (c2 << 3) < tcols;
-    const size_t dcol = ((size_t)(col0 >> 3) + c2) * 16u;  // this lane's columns within a down row
+    const uint32_t dcol = ((uint32_t)(col0 >> 3) + c2) * 16u;  // this lane's columns within a down row
     uint4 dv[U2];
 #pragma unroll
-    for (int u = 0; u < U2; ++u) {
-        const int i = r2 + u * RL2;
-        dv[u] = gload(cok && i < wn ? row_at(i, R - 1) + dcol : buf_c);
-    }
+    for (int u = 0; u < U2; ++u) dv[u] = row_load(cok && r2 + u * RL2 < wn, sl2[u], sr2[u], R - 1, dcol, dcol);
+
+
+    // x as bf16 halves (a lane past the row's end holds zeros)
+#pragma unroll
+    for (int j = 0; j < JX; ++j) xs[j] = split_x(xr[j][0], xr[j][1], cl + CL * j < cpr);
 
     // ---------------- phase 1 compute: h for chunk w ----------------
     if (has1) {
-        compute_batch(c0);
+        compute_batch(c0, sl1, sr1);
         for (int b0 = c0 + SB * RL; b0 < c1; b0 += SB * RL) {
             if (CL >= 64) __syncthreads();  // s_red1 is reused by this batch
-            load_batch(b0);
-            compute_batch(b0);
+            int sl[SB], sr[SB];
+#pragma unroll
+            for (int i = 0; i < SB; ++i) sl[i] = slot_of(b0 + rl + RL * i, b0 + rl + RL * i < c1, sr[i]);
+            load_batch(b0, sl, sr);
+            compute_batch(b0, sl, sr);
         }
     }
 
@@ -570,11 +624,15 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
     // The window's other chunks belong to lower workgroup IDs: their h words are polled, one
     // word per thread, until they carry this launch's sequence number, and go into LDS next
     // to this workgroup's own h (if any), so the down rows then take h from LDS.
+    constexpr int kStage = (kWinMax + NT - 1) / NT;
+    int n_dev = n;
     {
         const int n_other = (has1 ? c0 : phi) - plo;  // positions plo .. plo + n_other - 1
         uint64_t hp[kStage];
 #pragma unroll
-        for (int k = 0; k < kStage; ++k) hp[k] = ld_pair(&a.hpair[min(plo + tid + k * NT, a.K - 1)]);
+        for (int k = 0; k < kStage; ++k) hp[k] = ld_pair(&a.hpair[min(plo + tid + k * NT, K - 1)]);
+        if (host_n && tid == 0)
+            n_dev = __hip_atomic_load(gmem(a.counts) + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         for (uint32_t it = 0;; ++it) {
             bool ready = true;
 #pragma unroll
@@ -601,19 +659,18 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
 #pragma unroll
         for (int u = 0; u < U2; ++u) {
             const int i = i0 + u * RL2;
-            if (cok && i < wn) {
-                axpy8(acc, s_h[i], dv[u]);
-                // read-through: this tile's piece of the down row goes into its slot
-                if (rt && s_src[i] >= 0) gstore(buf_w + slot_row(i, R - 1) + dcol, dv[u]);
-            }
+            // a position past the window has zero rows (out-of-range loads) and zero h
+            const float h = i < wn ? s_h[min(i, kWinMax - 1)] : 0.f;
+            axpy8(acc, h, dv[u]);
+            // read-through: this tile's piece of the down row goes into its slot
+            if constexpr (RT) bstore(rs_buf, off_buf(cok && i < wn && sr2[u] >= 0, sl2[u], R - 1, dcol), dv[u]);
         }
         i0 += U2 * RL2;
         if (i0 >= wn) break;
 #pragma unroll
-        for (int u = 0; u < U2; ++u) {
-            const int i = i0 + u * RL2;
-            dv[u] = gload(cok && i < wn ? row_at(i, R - 1) + dcol : buf_c);
-        }
+        for (int u = 0; u < U2; ++u) sl2[u] = slot_of(plo + i0 + u * RL2, i0 + u * RL2 < wn, sr2[u]);
+#pragma unroll
+        for (int u = 0; u < U2; ++u) dv[u] = row_load(cok && i0 + u * RL2 < wn, sl2[u], sr2[u], R - 1, dcol, dcol);
     }
 
     // Reduce the RL2 row lanes: column c of wave k's partial sums sits at s_red2[k * TW + swz(c)],
@@ -720,8 +777,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
             yg[col0 + mycol] = a.accumulate ? y0 + (yv + own) : yv + own;
         }
     }
-    if (host_n && tid == 0 && __hip_atomic_load(gmem(a.counts) + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != n)
-        err |= kErrCount;
+    if (n_dev != n) err |= kErrCount;
     if (err) raise_err(a.counts, err);
     if constexpr (TOK) {
         // This workgroup of the layer's FFN is done (its stores have completed): the next
@@ -733,26 +789,36 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
     }
 }
 
-template <int NT, int JX, bool G>
-hipError_t launch_t(const FfnArgs& a, const FfnShape& sh, hipStream_t s) {
+template <int NT, int JX, bool G, int FCL>
+hipError_t launch_k(const FfnArgs& a, const FfnShape& sh, hipStream_t s) {
     // Slots per row lane per phase-1 batch and down rows per lane per phase-2 batch,
     // sized so that about five slots per workgroup take one batch each.
     constexpr int SB = 4;
     constexpr int U2 = NT >= 1024 ? 4 : (NT >= 512 ? 6 : 12);
     const dim3 grid(sh.nwg + a.pf_wgs), block(NT);
     if (a.tok) {  // sh.nwg: the token's whole grid
-        hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, false, false, true>), dim3(sh.nwg), block, 0, s, a);
+        hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, false, false, true, FCL>), dim3(sh.nwg), block, 0, s, a);
     } else if (a.pf_wgs > 0) {
         if (a.read_through)
-            hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, true, true, false>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, true, true, false, FCL>), grid, block, 0, s, a);
         else
-            hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, false, true, false>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, false, true, false, FCL>), grid, block, 0, s, a);
     } else if (a.read_through) {
-        hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, true, false, false>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, true, false, false, FCL>), grid, block, 0, s, a);
     } else {
-        hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, false, false, false>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_sparse_ffn<NT, JX, G, SB, U2, false, false, false, FCL>), grid, block, 0, s, a);
     }
     return hipGetLastError();
+}
+
+// The compiled lane geometry (rows of 512 lanes, 256-column tiles) for the shapes that have
+// it: d_model 4096 with 1024 threads, and d_model above 4096 (up to 8192) with 512.
+template <int NT, int JX, bool G>
+hipError_t launch_t(const FfnArgs& a, const FfnShape& sh, hipStream_t s) {
+    if constexpr ((NT == 1024 && JX == 1) || (NT == 512 && JX == 2)) {
+        if (sh.fixed) return launch_k<NT, JX, G, 512>(a, sh, s);
+    }
+    return launch_k<NT, JX, G, 0>(a, sh, s);
 }
 
 template <int NT, bool G>

@@ -229,6 +229,7 @@ bool ffn_shape(const np_layer* L, int n, FfnShape* sh, bool fixed = false) {
     sh->p1 = p1;
     sh->nwg = p1 + sh->q - 1;
     sh->win_max = win;
+    sh->fixed = cl == 512 && sh->tw == 256 && sh->nt >= 512 ? 1 : 0;
     // 1024-thread workgroups keep x for one 16-byte chunk per lane in registers
     return sh->jx <= (sh->nt == 1024 ? 1 : 4) && sh->tw <= sh->nt;
 }
@@ -358,6 +359,7 @@ np_status ffn_args(np_layer* L, const float* x, float* y, const DecodeParams* pr
     a.act_src = L->act_src();
     a.store = L->store_dev;
     a.read_through = read_through ? 1 : 0;
+    a.store_bytes = read_through ? (uint32_t)((size_t)L->desc.d_ff * L->bundle_elems() * 2) : 0u;
     a.counts = L->counts;
     a.x = x;
     a.y = y;
@@ -447,7 +449,7 @@ np_status token_args(np_layer* const* layers, int n, const float* x, float* y, c
     const int d = layers[0]->desc.d_model;
     T->n_layers = n;
     T->n_pf = kTokenPfWgs;
-    int tot = 0;
+    int tot = 0, fixed = 1;
     for (int l = 0; l < n; ++l) {
         const int gl = layer0 + l;
         const np_status st = ffn_args(layers[l], prm ? nullptr : x + (size_t)gl * d, prm ? nullptr : y + (size_t)gl * d,
@@ -455,8 +457,10 @@ np_status token_args(np_layer* const* layers, int n, const float* x, float* y, c
         if (st != NP_OK) return st;
         T->wg0[l] = tot;
         tot += sh->nwg;
+        fixed &= sh->fixed;  // the compiled lane geometry only when every layer of the launch has it
         T->src[l] = layers[l]->ldev;
     }
+    sh->fixed = fixed;
     T->wg0[n] = tot;
     *grid = kTokenPfWgs + tot;
     return NP_OK;
@@ -513,6 +517,24 @@ np_status enqueue_scatter(np_layer* L, hipStream_t s, bool fixed_grid = false) {
                           L->desc.k_max, (int32_t)L->bundle_elems(), L->ldh.row16, L->ldh.stride16, L->ldh.plane16,
                           grid, s));
     return NP_OK;
+}
+
+// The FFN reads a device row store through a buffer descriptor with 32-bit offsets, so it reads
+// new bundles straight from the store (read-through) only when the store is below 4 GiB; a larger
+// one is scattered into the slots first.
+bool read_through_ok(const np_layer* L) {
+    return !L->store_is_host && (uint64_t)L->desc.d_ff * L->bundle_elems() * 2 <= kMaxBufBytes;
+}
+
+// The FFN of a layer in a decode step: device row stores go through read-through, or, above
+// 4 GiB, an explicit scatter first.
+np_status enqueue_step_ffn(np_layer* L, const float* x, float* y, hipStream_t s, const DecodeParams* prm, int layer,
+                           bool y_holds_base, const np_layer* pf = nullptr, bool pf_fixed = false) {
+    if (!L->store_is_host && !read_through_ok(L)) {
+        const np_status r = enqueue_scatter(L, s, prm != nullptr);
+        if (r != NP_OK) return r;
+    }
+    return enqueue_ffn(L, x, y, s, prm, layer, read_through_ok(L), y_holds_base, nullptr, pf, pf_fixed);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -779,8 +801,9 @@ np_status enqueue_token(np_layer* const* layers, int n, const int32_t* cid, cons
         }
         for (int l = 0; l < n; ++l) {
             const np_layer* pf = l + 1 < n && layers[l + 1]->store_is_host ? layers[l + 1] : nullptr;
-            np_status r = enqueue_ffn(layers[l], prm ? nullptr : x + (size_t)l * d, prm ? nullptr : y + (size_t)l * d,
-                                      cs, prm, l, !layers[l]->store_is_host, any_atomic, nullptr, pf, prm != nullptr);
+            np_status r = enqueue_step_ffn(layers[l], prm ? nullptr : x + (size_t)l * d,
+                                           prm ? nullptr : y + (size_t)l * d, cs, prm, l, any_atomic, pf,
+                                           prm != nullptr);
             if (r != NP_OK) return r;
         }
         return NP_OK;
@@ -806,8 +829,8 @@ np_status enqueue_token(np_layer* const* layers, int n, const int32_t* cid, cons
         }
         if (sa.n_layers > 0) NP_HIP(launch_scatter_all(sa, kScatterWgsPerLayer, cs));
         for (int l = 0; l < n; ++l) {
-            np_status r = enqueue_ffn(layers[l], prm ? nullptr : x + (size_t)l * d, prm ? nullptr : y + (size_t)l * d,
-                                      cs, prm, l, !layers[l]->store_is_host, any_atomic);
+            np_status r = enqueue_step_ffn(layers[l], prm ? nullptr : x + (size_t)l * d,
+                                           prm ? nullptr : y + (size_t)l * d, cs, prm, l, any_atomic);
             if (r != NP_OK) return r;
         }
         return NP_OK;
@@ -1245,7 +1268,7 @@ np_status sparse_ffn_call(np_layer* L, const float* x, float* y, void* stream, b
         const np_status pe = check_io_ptr(io.first, L->desc.device, io.second);
         if (pe != NP_OK) return pe;
     }
-    const bool read_through = L->state == kAssigned;
+    bool read_through = L->state == kAssigned;
     if (read_through && L->store_is_host)
         return fail(NP_ESTATE, "the row store is host memory: call np_scatter_rows before np_sparse_ffn");
     const np_status de = check_device_err(L);
@@ -1275,6 +1298,11 @@ np_status sparse_ffn_call(np_layer* L, const float* x, float* y, void* stream, b
         }
         if (!base) return fail(NP_EHIP, "the static scratch of device %d has no device address", L->desc.device);
         xs = Exchange{base, base + kScratchHWords, seq};
+    }
+    if (read_through && !read_through_ok(L)) {  // a device row store above 4 GiB: scatter first
+        const np_status r = enqueue_scatter(L, (hipStream_t)stream);
+        if (r != NP_OK) return r;
+        read_through = false;
     }
     np_status st = enqueue_ffn(L, x, y, (hipStream_t)stream, nullptr, 0, read_through, acc, xch ? &xs : nullptr);
     if (st != NP_OK) return st;

@@ -134,6 +134,7 @@ struct FfnShape {
     int nwg;       // p1 + q - 1 workgroups
     int jx;        // 16-byte x chunks per thread (gate/up phase)
     int win_max;   // LDS window capacity (positions)
+    int fixed;     // 1: rows of 512 lanes and 256-column tiles, a lane geometry fixed at compile time
 };
 
 struct TokenArgs;
@@ -145,6 +146,7 @@ struct FfnArgs {
     // row store (act_src gives the neuron) and written into their slots by this launch.
     const int32_t* act_src; // [K] (always a valid array)
     const uint16_t* store;  // [M][R][d]
+    uint32_t store_bytes;   // size of store when read_through (below 4 GiB), else 0
     int32_t read_through;
     int32_t* counts;        // [4]
     const float* x;         // [d]

@@ -442,8 +442,9 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
 
     // ---------------- list loads (issued before any row load) ----------------
     int sl1[SB], sr1[SB];
+    const int rl_u = CL >= 64 ? __builtin_amdgcn_readfirstlane(rl) : rl;  // uniform when a row spans waves
 #pragma unroll
-    for (int i = 0; i < SB; ++i) sl1[i] = slot_of(c0 + rl + RL * i, c0 + rl + RL * i < c1, sr1[i]);
+    for (int i = 0; i < SB; ++i) sl1[i] = slot_of(c0 + rl_u + RL * i, c0 + rl_u + RL * i < c1, sr1[i]);
     int sl2[U2], sr2[U2];
 #pragma unroll
     for (int u = 0; u < U2; ++u) sl2[u] = slot_of(plo + r2 + u * RL2, r2 + u * RL2 < wn, sr2[u]);
@@ -545,9 +546,12 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
             stage(std::integral_constant<int, 1>{});
             if ((lane & (64 / V - 1)) == 0) s_red1[wave * V + (lane / (64 / V))] = v[0];
             __syncthreads();
-            // across the waves of each row lane: lane cl = i of the row lane finishes slot i
-            if (cl < SB) {
-                const int pos = b0 + rl + RL * cl;
+            // across the waves of each row lane: thread i of the first wave finishes position i of
+            // the batch (row lane i % RL, its slot i / RL). One wave does them all: split over the
+            // row lanes' first waves, the h of a chunk came out later (measured).
+            if (tid < SB * RL) {
+                const int rlp = tid % RL, ip = tid / RL;
+                const int pos = b0 + rlp + RL * ip;
                 if (pos < c1) {
                     // the CL / 64 wave sums of each row: all reads issued, then added in order
                     float part[NR1][kWaves];
@@ -555,7 +559,7 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
                     for (int r = 0; r < NR1; ++r)
 #pragma unroll
                         for (int k = 0; k < kWaves; ++k)
-                            part[r][k] = k < CL / 64 ? s_red1[(rl * (CL / 64) + k) * V + cl * NR1 + r] : 0.f;
+                            part[r][k] = k < CL / 64 ? s_red1[(rlp * (CL / 64) + k) * V + ip * NR1 + r] : 0.f;
                     float g[NR1];
 #pragma unroll
                     for (int r = 0; r < NR1; ++r) {
@@ -655,13 +659,15 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    const int r2_first = __builtin_amdgcn_readfirstlane(r2);  // the wave's first row lane
     for (int i0 = r2;;) {
 #pragma unroll
         for (int u = 0; u < U2; ++u) {
             const int i = i0 + u * RL2;
-            // a position past the window has zero rows (out-of-range loads) and zero h
+            // a position past the window has zero rows (out-of-range loads) and zero h; a wave
+            // whose positions are all past it skips the work (a branch uniform over the wave)
             const float h = i < wn ? s_h[min(i, kWinMax - 1)] : 0.f;
-            axpy8(acc, h, dv[u]);
+            if (i0 - r2 + r2_first + u * RL2 < wn) axpy8(acc, h, dv[u]);
             // read-through: this tile's piece of the down row goes into its slot
             if constexpr (RT) bstore(rs_buf, off_buf(cok && i < wn && sr2[u] >= 0, sl2[u], R - 1, dcol), dv[u]);
         }

@@ -632,9 +632,11 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
     int n_dev = n;
     {
         const int n_other = (has1 ? c0 : phi) - plo;  // positions plo .. plo + n_other - 1
+        // only the lanes that cover a position poll (the others would add memory-side reads
+        // while the down rows stream)
         uint64_t hp[kStage];
 #pragma unroll
-        for (int k = 0; k < kStage; ++k) hp[k] = ld_pair(&a.hpair[min(plo + tid + k * NT, K - 1)]);
+        for (int k = 0; k < kStage; ++k) hp[k] = tid + k * NT < n_other ? ld_pair(&a.hpair[plo + tid + k * NT]) : 0;
         if (host_n && tid == 0)
             n_dev = __hip_atomic_load(gmem(a.counts) + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         for (uint32_t it = 0;; ++it) {

@@ -475,6 +475,15 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
             return bload(rs_buf, off_buf(ok, s, r, cb_buf));
         }
     };
+    // A gate/up position is the same for every lane of a wave when a row spans whole waves: its
+    // read-through source then picks one buffer for the wave, and the row takes one load.
+    auto row_load_u = [&](bool ok, int s, int u, int r, uint32_t cb) -> uint4 {
+        const int uu = __builtin_amdgcn_readfirstlane(u);
+        const bool from_store = uu >= 0;
+        const __amdgpu_buffer_rsrc_t rsel = buf_rsrc(from_store ? (const void*)a.store : (const void*)a.buf,
+                                                     from_store ? a.store_bytes : a.buf_bytes);
+        return bload(rsel, from_store ? off_sto(ok, uu, r, cb) : off_buf(ok, s, r, cb));
+    };
     uint4 wv[SB][NR1][JX];
     auto load_batch = [&](int b0, const int* sl, const int* sr) {
 #pragma unroll
@@ -485,7 +494,10 @@ __global__ __launch_bounds__(NT) void k_sparse_ffn(FfnArgs a0) {
 #pragma unroll
                 for (int j = 0; j < JX; ++j) {
                     const int c = cl + CL * j;
-                    wv[i][r][j] = row_load(ok && c < cpr, sl[i], sr[i], r, (uint32_t)c * 16u, (uint32_t)c * 16u);
+                    if (RT && CL >= 64)
+                        wv[i][r][j] = row_load_u(ok && c < cpr, sl[i], sr[i], r, (uint32_t)c * 16u);
+                    else
+                        wv[i][r][j] = row_load(ok && c < cpr, sl[i], sr[i], r, (uint32_t)c * 16u, (uint32_t)c * 16u);
                 }
         }
     };

@@ -172,7 +172,7 @@ def cpu_baseline(wl, stores, seconds: float, window: int = 1, n_levels: int = 0,
     eff = (act + din) * c.bundle_bytes
     return {"value": tok / dt, "unit": "tokens/s", "cores": threads, "host_cpu_count": os.cpu_count(),
             "threads_note": "threads = min(16, os.cpu_count()): the oracle's thread pool, capped at the "
-                            "GPU box's CPU share", "kind": "oracle",
+                            "16 host CPUs that one GPU's host share provides", "kind": "oracle",
             "sample": f"{tok} tokens of the same workload (tokens 1..{c.T - 1} in order, repeating; all "
                       f"{c.L} layers; after an untimed cold start), fp64 oracle, "
                       + ("layers in parallel threads" if threads > 1 else "layers one after another on one thread"),

@@ -30,7 +30,7 @@ from oracle import oracle as O
 from tests.harness import check_y, compare_state, torch_mod
 from workload.gen import CONFIGS, Workload
 
-POOL = 16  # host threads for the oracle (the GPU machine's CPU share)
+POOL = 16  # host threads for the oracle (one GPU's share of the host CPUs)
 
 
 def log(msg: str) -> None:

@@ -153,6 +153,10 @@ np_status np_scatter_rows(np_layer* layer, void* stream);
  * device memory, it does step 4 itself: the bundles of the slots filled by
  * that assignment are read from the row store and written into their slots
  * by the same launch (read-through), with the same y and buffer contents.
+ * The FFN addresses the row store with 32-bit offsets, so a device row store
+ * above 4 GiB - 4096 bytes (d_ff * n_rows * d_model * 2) is instead scattered
+ * into its slots by a launch of its own before the FFN; y and the buffer are
+ * the same either way.
  * Errors: NP_ESTATE before the first np_delta_assign, or after an
  * unscattered assignment when the row store is host memory. */
 np_status np_sparse_ffn(np_layer* layer, const float* x, float* y, void* stream);
@@ -198,7 +202,8 @@ np_status np_layer_set_ffn_reduce(np_layer* layer, int32_t mode);
  * compute_stream: one launch assigns the deltas of all layers, then one
  * launch per layer runs that layer's FFN. A layer whose row store is device
  * memory has its FFN read the new bundles through from the store (as
- * np_sparse_ffn right after np_delta_assign). When every row store is
+ * np_sparse_ffn right after np_delta_assign; a device store above
+ * 4 GiB - 4096 bytes is scattered by a launch of its own first). When every row store is
  * pinned host memory (and the layers share their FFN workgroup size), the
  * rest of the token is one launch per group of up to 64 layers, which
  * overlaps the host link with the FFNs (the prefetch of section 3.5): 24

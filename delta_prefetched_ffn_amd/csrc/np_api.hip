@@ -1300,6 +1300,9 @@ np_status sparse_ffn_call(np_layer* L, const float* x, float* y, void* stream, b
         xs = Exchange{base, base + kScratchHWords, seq};
     }
     if (read_through && !read_through_ok(L)) {  // a device row store above 4 GiB: scatter first
+        FfnShape sh{};
+        if (!ffn_shape(L, L->n_active, &sh))  // refused before anything is enqueued
+            return fail(NP_EINVAL, "no FFN launch shape for d_model=%d n=%d", L->desc.d_model, L->n_active);
         const np_status r = enqueue_scatter(L, (hipStream_t)stream);
         if (r != NP_OK) return r;
         read_through = false;
